@@ -1,0 +1,280 @@
+"""Python binding of libcpattn.so, the MI355X-native hot path of causal
+context-parallel (zigzag ring) attention.
+
+Every function here only marshals arguments (tensor pointers, strides, the
+current HIP stream) into the C ABI declared in ``include/cpattn.h`` and turns
+error codes into exceptions; all work runs in the library's host index builder
+and HIP kernels.  There is no fallback: if the library is not built the calls
+raise.  PyTorch provides device memory and streams only.
+
+Names match the C entry points.  Error codes map to exceptions the way the
+Accelerate plugin reports bad configuration: invalid arguments and shapes raise
+``ValueError``; HIP runtime failures raise ``RuntimeError``.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from ctypes import c_float, c_int32, c_int64, c_size_t, c_void_p, POINTER
+
+import numpy as np
+import torch
+
+__all__ = [
+    "CP_OK", "CP_EINVAL", "CP_ESHAPE", "CP_EDTYPE", "CP_EWORKSPACE", "CP_EHIP",
+    "CP_F32", "CP_BF16", "CP_STREAM", "CP_PER_DOC", "CpShape", "CpError", "LIB_PATH",
+    "lib", "cp_version", "cp_last_error", "cp_shard_zigzag", "cp_unshard_zigzag",
+    "cp_varlen_index", "cp_ring_source", "cp_pairs", "cp_attn_fwd_workspace",
+    "cp_attn_partial_fwd", "cp_attn_merge", "cp_attn_ring_fwd", "RingFwdPlan",
+]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libcpattn.so")
+
+CP_OK, CP_EINVAL, CP_ESHAPE, CP_EDTYPE, CP_EWORKSPACE, CP_EHIP = range(6)
+CP_F32, CP_BF16 = 0, 1
+CP_STREAM, CP_PER_DOC = 0, 1
+
+_DT = {torch.float32: CP_F32, torch.bfloat16: CP_BF16}
+_I32P = POINTER(c_int32)
+
+
+class CpShape(ctypes.Structure):
+    _fields_ = [
+        ("b", c_int32), ("hq", c_int32), ("hkv", c_int32), ("d", c_int32),
+        ("sq", c_int64), ("sk", c_int64), ("scale", c_float),
+        ("in_dtype", c_int32), ("out_dtype", c_int32),
+        ("q_str", c_int64 * 3), ("k_str", c_int64 * 3), ("v_str", c_int64 * 3), ("o_str", c_int64 * 3),
+    ]
+
+
+class CpError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"cpattn error {code}: {msg}")
+        self.code = code
+
+
+_lib_handle = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library; raises if it has not been built."""
+    global _lib_handle
+    if _lib_handle is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run __graft_entry__.build() first")
+        L = ctypes.CDLL(LIB_PATH)
+        L.cp_last_error.restype = ctypes.c_char_p
+        L.cp_version.restype = c_int32
+        L.cp_shard_zigzag.argtypes = [c_int64, c_int32, c_int32, _I32P]
+        L.cp_unshard_zigzag.argtypes = [c_int64, c_int32, _I32P]
+        L.cp_varlen_index.argtypes = [_I32P, c_int32, c_int32, c_int32, c_int32, _I32P, _I32P]
+        L.cp_ring_source.argtypes = [c_int32, c_int32, c_int32]
+        L.cp_pairs.argtypes = [_I32P, _I32P, c_int64, _I32P, c_int64]
+        L.cp_pairs.restype = c_int64
+        L.cp_attn_fwd_workspace.argtypes = [POINTER(CpShape), c_int32]
+        L.cp_attn_fwd_workspace.restype = c_size_t
+        L.cp_attn_partial_fwd.argtypes = [POINTER(CpShape)] + [c_void_p] * 6 + [c_void_p, c_void_p, c_void_p,
+                                                                                c_size_t, c_void_p]
+        L.cp_attn_merge.argtypes = [c_int64, c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]
+        L.cp_attn_ring_fwd.argtypes = [POINTER(CpShape), c_int32, c_int32] + [c_void_p] * 6 + \
+            [c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]
+        for name in ("cp_shard_zigzag", "cp_unshard_zigzag", "cp_varlen_index", "cp_ring_source",
+                     "cp_attn_partial_fwd", "cp_attn_merge", "cp_attn_ring_fwd"):
+            getattr(L, name).restype = c_int32
+        _lib_handle = L
+    return _lib_handle
+
+
+def cp_version() -> int:
+    return int(lib().cp_version())
+
+
+def cp_last_error() -> str:
+    return lib().cp_last_error().decode()
+
+
+def _check(rc: int):
+    if rc == CP_OK:
+        return
+    msg = cp_last_error()
+    if rc == CP_EHIP:
+        raise CpError(rc, msg)
+    raise ValueError(f"cpattn error {rc}: {msg}")
+
+
+def _i32(a) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(a, dtype=np.int32))
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(_I32P)
+
+
+# ------------------------------------------------------------------ host index builder
+def cp_shard_zigzag(S: int, cp: int, rank: int) -> np.ndarray:
+    """Global positions of ``rank``'s rows: chunk rank, then chunk 2cp-1-rank."""
+    n = S // cp if cp >= 1 and S >= 0 else 0
+    out = np.empty(max(n, 1), dtype=np.int32)
+    _check(lib().cp_shard_zigzag(S, cp, rank, _ptr(out)))
+    return out[:n]
+
+
+def cp_unshard_zigzag(S: int, cp: int) -> np.ndarray:
+    """Rank-major concatenation of every rank's positions (a permutation of [0, S))."""
+    out = np.empty(max(S, 1), dtype=np.int32)
+    _check(lib().cp_unshard_zigzag(S, cp, _ptr(out)))
+    return out[:S]
+
+
+def cp_varlen_index(cu_seqlens, cp: int, rank: int, mode: int = CP_STREAM):
+    """(pos, lo) of ``rank``'s rows for packed documents with boundaries ``cu_seqlens``."""
+    cu = _i32(cu_seqlens)
+    n_docs = len(cu) - 1
+    S = int(cu[-1]) if len(cu) else 0
+    n = S // cp if cp >= 1 and S >= 0 else 0
+    pos = np.empty(max(n, 1), dtype=np.int32)
+    lo = np.empty(max(n, 1), dtype=np.int32)
+    _check(lib().cp_varlen_index(_ptr(cu), n_docs, cp, rank, mode, _ptr(pos), _ptr(lo)))
+    return pos[:n], lo[:n]
+
+
+def cp_ring_source(cp: int, rank: int, step: int) -> int:
+    """Rank whose shard ``rank`` attends at ring step ``step``."""
+    r = int(lib().cp_ring_source(cp, rank, step))
+    if r < 0:
+        raise ValueError(cp_last_error())
+    return r
+
+
+def cp_pairs(q_pos, q_lo, k_pos) -> int:
+    """Exact count of allowed (query, key) pairs; ``q_lo`` may be None."""
+    qp, kp = _i32(q_pos), _i32(k_pos)
+    ql = None if q_lo is None else _i32(q_lo)
+    n = lib().cp_pairs(_ptr(qp), None if ql is None else _ptr(ql), len(qp), _ptr(kp), len(kp))
+    if n < 0:
+        raise ValueError(cp_last_error())
+    return int(n)
+
+
+# ------------------------------------------------------------------ device calls
+def _stream(dev) -> int:
+    return torch.cuda.current_stream(dev).cuda_stream
+
+
+def _strides(t: torch.Tensor):
+    if t.dim() != 4 or t.stride(-1) != 1:
+        raise ValueError("tensors must be [B, H, rows, D] with a contiguous last dimension")
+    return (ctypes.c_int64 * 3)(t.stride(0), t.stride(1), t.stride(2))
+
+
+def _shape(q, k, v, o_strides, scale, out_dtype) -> CpShape:
+    if q.dtype not in _DT or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError(f"q, k, v must share a dtype among float32/bfloat16 (got {q.dtype}, {k.dtype}, {v.dtype})")
+    B, Hq, Sq, D = q.shape
+    if k.shape[0] != B or v.shape != k.shape or k.shape[3] != D:
+        raise ValueError(f"inconsistent shapes q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
+    s = CpShape()
+    s.b, s.hq, s.hkv, s.d = B, Hq, k.shape[1], D
+    s.sq, s.sk = Sq, k.shape[2]
+    s.scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    s.in_dtype = _DT[q.dtype]
+    s.out_dtype = _DT[out_dtype]
+    s.q_str, s.k_str, s.v_str = _strides(q), _strides(k), _strides(v)
+    s.o_str = o_strides
+    return s
+
+
+def _dev_i32(a, device) -> torch.Tensor:
+    if isinstance(a, torch.Tensor):
+        if a.dtype != torch.int32 or a.device != device or not a.is_contiguous():
+            a = a.to(device=device, dtype=torch.int32).contiguous()
+        return a
+    return torch.from_numpy(_i32(a)).to(device)
+
+
+def cp_attn_fwd_workspace(q, k, v, cp: int = 1) -> int:
+    s = _shape(q, k, v, (ctypes.c_int64 * 3)(0, 0, 0), None, torch.float32)
+    n = int(lib().cp_attn_fwd_workspace(ctypes.byref(s), cp))
+    if n == 0:
+        raise ValueError(cp_last_error() or "invalid shape")
+    return n
+
+
+def _workspace(nbytes, device, ws):
+    if ws is None:
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    if ws.numel() < nbytes or ws.data_ptr() % 256:
+        raise ValueError("workspace too small or not 256-byte aligned")
+    return ws
+
+
+def cp_attn_partial_fwd(q, k, v, q_pos, q_lo, k_pos, scale=None, out=None, lse=None, workspace=None):
+    """One ring step: partial (O fp32, LSE fp32) of q against the allowed keys of k/v."""
+    dev = q.device
+    B, Hq, Sq, D = q.shape
+    out = torch.empty(B, Hq, Sq, D, dtype=torch.float32, device=dev) if out is None else out
+    lse = torch.empty(B, Hq, Sq, dtype=torch.float32, device=dev) if lse is None else lse
+    if lse.dtype != torch.float32 or not lse.is_contiguous() or tuple(lse.shape) != (B, Hq, Sq):
+        raise ValueError("lse must be contiguous float32 [B, Hq, Sq]")
+    s = _shape(q, k, v, _strides(out), scale, torch.float32)
+    qp, kp = _dev_i32(q_pos, dev), _dev_i32(k_pos, dev)
+    ql = None if q_lo is None else _dev_i32(q_lo, dev)
+    ws = _workspace(int(lib().cp_attn_fwd_workspace(ctypes.byref(s), 1)) or 256, dev, workspace)
+    _check(lib().cp_attn_partial_fwd(ctypes.byref(s), q.data_ptr(), k.data_ptr(), v.data_ptr(), qp.data_ptr(),
+                                     None if ql is None else ql.data_ptr(), kp.data_ptr(), out.data_ptr(),
+                                     lse.data_ptr(), ws.data_ptr(), ws.numel(), _stream(dev)))
+    return out, lse
+
+
+def cp_attn_merge(o_acc, lse_acc, o_p, lse_p):
+    """In place: (o_acc, lse_acc) <- (o_acc, lse_acc) (+) (o_p, lse_p)."""
+    for t in (o_acc, lse_acc, o_p, lse_p):
+        if t.dtype != torch.float32 or not t.is_contiguous():
+            raise ValueError("merge operands must be contiguous float32")
+    d = o_acc.shape[-1]
+    rows = o_acc.numel() // d
+    if o_p.numel() != o_acc.numel() or lse_acc.numel() != rows or lse_p.numel() != rows:
+        raise ValueError("merge operands disagree in size")
+    _check(lib().cp_attn_merge(rows, d, o_acc.data_ptr(), lse_acc.data_ptr(), o_p.data_ptr(), lse_p.data_ptr(),
+                               _stream(o_acc.device)))
+    return o_acc, lse_acc
+
+
+class RingFwdPlan:
+    """A validated cp_attn_ring_fwd call with its workspace, replayable with no
+    Python-side allocation (used by the bench to time the call alone)."""
+
+    def __init__(self, q_loc, k_all, v_all, cp, rank, q_pos, q_lo, k_pos_all, scale=None, out_dtype=None,
+                 out=None, lse=None, workspace=None):
+        dev = q_loc.device
+        B, Hq, Sq, D = q_loc.shape
+        out_dtype = torch.float32 if out_dtype is None else out_dtype
+        self.out = torch.empty(B, Hq, Sq, D, dtype=out_dtype, device=dev) if out is None else out
+        self.lse = torch.empty(B, Hq, Sq, dtype=torch.float32, device=dev) if lse is None else lse
+        if self.out.dtype != out_dtype:
+            raise ValueError("out dtype disagrees with out_dtype")
+        self.shape = _shape(q_loc, k_all, v_all, _strides(self.out), scale, out_dtype)
+        self.qp = _dev_i32(q_pos, dev)
+        self.ql = None if q_lo is None else _dev_i32(q_lo, dev)
+        self.kp = _dev_i32(k_pos_all, dev)
+        nws = int(lib().cp_attn_fwd_workspace(ctypes.byref(self.shape), cp))
+        self.ws = _workspace(nws or 256, dev, workspace)
+        self.keep = (q_loc, k_all, v_all)
+        self.args = (ctypes.byref(self.shape), cp, rank, q_loc.data_ptr(), k_all.data_ptr(), v_all.data_ptr(),
+                     self.qp.data_ptr(), None if self.ql is None else self.ql.data_ptr(), self.kp.data_ptr(),
+                     self.out.data_ptr(), self.lse.data_ptr(), self.ws.data_ptr(), self.ws.numel())
+        self.device = dev
+
+    def run(self, stream=None):
+        st = _stream(self.device) if stream is None else stream
+        _check(lib().cp_attn_ring_fwd(*self.args, st))
+        return self.out, self.lse
+
+
+def cp_attn_ring_fwd(q_loc, k_all, v_all, cp, rank, q_pos, q_lo, k_pos_all, scale=None, out_dtype=None,
+                     out=None, lse=None, workspace=None):
+    """A virtual rank's whole ring with every K/V shard resident: final (O, LSE)."""
+    return RingFwdPlan(q_loc, k_all, v_all, cp, rank, q_pos, q_lo, k_pos_all, scale, out_dtype, out, lse,
+                       workspace).run()

@@ -1,0 +1,203 @@
+// C ABI of libcpattn.so: argument validation, workspace layout and dispatch to
+// the HIP kernels.  Every check happens before anything is enqueued, so a call
+// that returns an error has launched nothing.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "internal.h"
+
+namespace cpattn {
+
+namespace {
+thread_local std::string g_last_error;
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int esize(int32_t dtype) { return dtype == CP_BF16 ? 2 : 4; }
+
+int check_dtype(int32_t dt, const char* what) {
+  if (dt != CP_F32 && dt != CP_BF16) return fail(CP_EDTYPE, "%s: unknown dtype code %d", what, dt);
+  return CP_OK;
+}
+
+int check_strides(const int64_t* st, int32_t dtype, const char* what) {
+  for (int i = 0; i < 3; ++i) {
+    if (st[i] < 0) return fail(CP_EINVAL, "%s stride %d is negative", what, i);
+    if ((st[i] * esize(dtype)) % 16 != 0)
+      return fail(CP_EINVAL, "%s stride %d (%lld elements) is not a multiple of 16 bytes", what, i,
+                  (long long)st[i]);
+  }
+  return CP_OK;
+}
+
+// Checks common to every attention call.
+int check_shape(const cp_shape* s) {
+  if (!s) return fail(CP_EINVAL, "shape descriptor is null");
+  if (s->b < 1 || s->hq < 1 || s->hkv < 1)
+    return fail(CP_EINVAL, "b, hq and hkv must be >= 1 (got %d, %d, %d)", s->b, s->hq, s->hkv);
+  if (s->hq % s->hkv != 0) return fail(CP_EINVAL, "hq (%d) is not a multiple of hkv (%d)", s->hq, s->hkv);
+  if (s->d != 64 && s->d != 128) return fail(CP_EINVAL, "head dimension %d is not 64 or 128", s->d);
+  if (s->sq < 0 || s->sk < 0 || s->sq > (INT32_MAX / 2) || s->sk > (INT32_MAX / 2))
+    return fail(CP_EINVAL, "row counts sq=%lld sk=%lld outside [0, 2^30)", (long long)s->sq,
+                (long long)s->sk);
+  if (!std::isfinite(s->scale) || !(s->scale > 0.0f))
+    return fail(CP_EINVAL, "scale must be finite and > 0 (got %g)", (double)s->scale);
+  if (int rc = check_dtype(s->in_dtype, "in_dtype")) return rc;
+  if (int rc = check_dtype(s->out_dtype, "out_dtype")) return rc;
+  if (int rc = check_strides(s->q_str, s->in_dtype, "q")) return rc;
+  if (int rc = check_strides(s->k_str, s->in_dtype, "k")) return rc;
+  if (int rc = check_strides(s->v_str, s->in_dtype, "v")) return rc;
+  return CP_OK;
+}
+
+int check_ptrs16(std::initializer_list<std::pair<const void*, const char*>> ps) {
+  for (auto& p : ps) {
+    if (!p.first) return fail(CP_EINVAL, "%s is null", p.second);
+    if (!aligned16(p.first)) return fail(CP_EINVAL, "%s is not 16-byte aligned", p.second);
+  }
+  return CP_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return CP_OK;
+  return fail(CP_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+FwdArgs base_args(const cp_shape* s) {
+  FwdArgs a{};
+  for (int i = 0; i < 3; ++i) {
+    a.q_str[i] = s->q_str[i];
+    a.k_str[i] = s->k_str[i];
+    a.v_str[i] = s->v_str[i];
+    a.o_str[i] = s->o_str[i];
+  }
+  a.b = s->b;
+  a.hq = s->hq;
+  a.hkv = s->hkv;
+  a.d = s->d;
+  a.sq = (int32_t)s->sq;
+  a.sk = (int32_t)s->sk;
+  a.scale_log2 = (float)((double)s->scale * 1.4426950408889634);
+  a.in_dtype = s->in_dtype;
+  return a;
+}
+
+}  // namespace
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+void clear_error() { g_last_error.clear(); }
+
+FwdWorkspace fwd_workspace_layout(int32_t b, int32_t hkv, int32_t d, int64_t sk, int32_t cp,
+                                  int32_t in_dtype) {
+  FwdWorkspace w{};
+  const int tk = tile_keys(in_dtype);
+  const int64_t per = cp > 0 ? sk / cp : 0;
+  const int64_t tpr = (per + tk - 1) / tk;
+  const int64_t ntiles = tpr * cp;
+  w.bounds_off = 0;
+  size_t off = align_up((size_t)ntiles * 16, 256);
+  w.vt_off = off;
+  w.vt_row = ntiles * tk;
+  if (in_dtype == CP_BF16) off += align_up((size_t)b * hkv * d * (size_t)w.vt_row * 2, 256);
+  w.total = off < 256 ? 256 : off;
+  return w;
+}
+
+}  // namespace cpattn
+
+using namespace cpattn;
+
+extern "C" const char* cp_last_error(void) { return g_last_error.c_str(); }
+
+extern "C" int cp_version(void) { return 100; }
+
+extern "C" size_t cp_attn_fwd_workspace(const cp_shape* s, int32_t cp) {
+  if (check_shape(s) != CP_OK || cp < 1) return 0;
+  return fwd_workspace_layout(s->b, s->hkv, s->d, s->sk, cp, s->in_dtype).total;
+}
+
+namespace {
+
+int run_fwd(const cp_shape* s, int32_t cp, int32_t rank, const void* q, const void* k, const void* v,
+            const int32_t* q_pos, const int32_t* q_lo, const int32_t* k_pos, void* o, int32_t o_dtype,
+            float* lse, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (s->sq == 0) return CP_OK;  // no query rows: nothing to read or write
+  if (int rc = check_ptrs16({{q, "q"}, {o, "o"}, {lse, "lse"}})) return rc;
+  if (!q_pos) return fail(CP_EINVAL, "q_pos is null");
+  if (s->sk > 0) {
+    if (int rc = check_ptrs16({{k, "k"}, {v, "v"}})) return rc;
+    if (!k_pos) return fail(CP_EINVAL, "k_pos is null");
+  }
+  if (int rc = check_strides(s->o_str, o_dtype, "o")) return rc;
+  if (s->o_str[2] < s->d) return fail(CP_EINVAL, "o row stride %lld is smaller than d", (long long)s->o_str[2]);
+  const FwdWorkspace w = fwd_workspace_layout(s->b, s->hkv, s->d, s->sk, cp, s->in_dtype);
+  if (!ws) return fail(CP_EWORKSPACE, "workspace is null (%zu bytes needed)", w.total);
+  if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0) return fail(CP_EWORKSPACE, "workspace is not 256-byte aligned");
+  if (ws_bytes < w.total) return fail(CP_EWORKSPACE, "workspace too small: %zu < %zu bytes", ws_bytes, w.total);
+  FwdArgs a = base_args(s);
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.q_pos = q_pos;
+  a.q_lo = q_lo;
+  a.k_pos = k_pos;
+  a.o = o;
+  a.lse = lse;
+  a.cp = cp;
+  a.rank = rank;
+  a.rows_per_rank = (int32_t)(s->sk / cp);
+  const int tk = tile_keys(s->in_dtype);
+  a.tiles_per_rank = (a.rows_per_rank + tk - 1) / tk;
+  a.out_dtype = o_dtype;
+  a.ws = ws;
+  return hip_status(launch_fwd(a, stream), "forward launch");
+}
+
+}  // namespace
+
+extern "C" int cp_attn_partial_fwd(const cp_shape* s, const void* q, const void* k, const void* v,
+                                   const int32_t* q_pos, const int32_t* q_lo, const int32_t* k_pos, float* o,
+                                   float* lse, void* ws, size_t ws_bytes, hipStream_t stream) {
+  clear_error();
+  if (int rc = check_shape(s)) return rc;
+  return run_fwd(s, 1, 0, q, k, v, q_pos, q_lo, k_pos, o, CP_F32, lse, ws, ws_bytes, stream);
+}
+
+extern "C" int cp_attn_ring_fwd(const cp_shape* s, int32_t cp, int32_t rank, const void* q_loc,
+                                const void* k_all, const void* v_all, const int32_t* q_pos,
+                                const int32_t* q_lo, const int32_t* k_pos_all, void* o, float* lse,
+                                void* ws, size_t ws_bytes, hipStream_t stream) {
+  clear_error();
+  if (int rc = check_shape(s)) return rc;
+  if (cp < 1) return fail(CP_EINVAL, "cp must be >= 1 (got %d)", cp);
+  if (rank < 0 || rank >= cp) return fail(CP_EINVAL, "rank %d outside [0, %d)", rank, cp);
+  if (s->sk % (2 * (int64_t)cp) != 0)
+    return fail(CP_ESHAPE, "key rows %lld are not a multiple of 2*cp = %lld", (long long)s->sk,
+                2 * (long long)cp);
+  return run_fwd(s, cp, rank, q_loc, k_all, v_all, q_pos, q_lo, k_pos_all, o, s->out_dtype, lse, ws,
+                 ws_bytes, stream);
+}
+
+extern "C" int cp_attn_merge(int64_t rows, int32_t d, float* o_acc, float* lse_acc, const float* o_p,
+                             const float* lse_p, hipStream_t stream) {
+  clear_error();
+  if (rows < 0) return fail(CP_EINVAL, "rows must be >= 0 (got %lld)", (long long)rows);
+  if (d != 64 && d != 128) return fail(CP_EINVAL, "head dimension %d is not 64 or 128", d);
+  if (int rc = check_ptrs16({{o_acc, "o_acc"}, {o_p, "o_p"}})) return rc;
+  if (!lse_acc || !lse_p) return fail(CP_EINVAL, "lse pointer is null");
+  if (rows == 0) return CP_OK;
+  return hip_status(launch_merge(rows, d, o_acc, lse_acc, o_p, lse_p, stream), "merge launch");
+}

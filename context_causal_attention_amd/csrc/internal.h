@@ -1,0 +1,63 @@
+// Internal declarations shared by the host layer (api.cpp, index.cpp) and the
+// kernel translation units.  Not part of the public ABI.
+#pragma once
+
+#include <cstdint>
+#include <cstddef>
+
+#include <hip/hip_runtime_api.h>
+
+#include "cpattn.h"
+
+namespace cpattn {
+
+// Records a message for cp_last_error() and returns `code`.
+int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+void clear_error();
+
+// Key-tile geometry of the forward kernels: keys are processed in tiles of
+// kTileKeys rows that never straddle two ranks' shards.
+constexpr int kTileKeysBf16 = 64;
+constexpr int kTileKeysF32 = 32;
+
+inline int tile_keys(int32_t dtype) { return dtype == CP_BF16 ? kTileKeysBf16 : kTileKeysF32; }
+
+// Everything the forward launch needs, resolved and validated on the host.
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const int32_t* q_pos;
+  const int32_t* q_lo;  // may be null
+  const int32_t* k_pos;
+  void* o;
+  float* lse;
+  int64_t q_str[3], k_str[3], v_str[3], o_str[3];
+  int32_t b, hq, hkv, d;
+  int32_t sq;
+  int32_t sk;
+  int32_t cp, rank;
+  int32_t rows_per_rank;   // sk / cp
+  int32_t tiles_per_rank;  // ceil(rows_per_rank / tile_keys)
+  float scale_log2;        // scale * log2(e)
+  int32_t in_dtype;
+  int32_t out_dtype;       // dtype of o (CP_F32 for partial outputs)
+  void* ws;                // workspace (layout: see fwd_workspace_layout)
+};
+
+struct FwdWorkspace {
+  size_t bounds_off;   // int4 per key tile: {min pos, max pos, valid rows, 0}
+  size_t vt_off;       // bf16 V^T [b][hkv][d][cp * tiles_per_rank * tile_keys] (bf16 inputs only)
+  size_t total;
+  int64_t vt_row;      // elements per V^T row
+};
+
+FwdWorkspace fwd_workspace_layout(int32_t b, int32_t hkv, int32_t d, int64_t sk, int32_t cp,
+                                  int32_t in_dtype);
+
+// Kernel launchers (attn_fwd.hip, merge.hip).  Return hipError_t codes.
+hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
+hipError_t launch_merge(int64_t rows, int32_t d, float* o_acc, float* lse_acc, const float* o_p,
+                        const float* lse_p, hipStream_t stream);
+
+}  // namespace cpattn

@@ -1,0 +1,179 @@
+/*
+ * cpattn.h -- C ABI of libcpattn.so: the per-rank hot path of causal
+ * context-parallel ("zigzag ring") attention on AMD Instinct MI355X (gfx950).
+ *
+ * What the calls compute
+ *   Context parallelism shards Q, K and V along the sequence dimension; a rank
+ *   keeps its Q shard, attends it to every K/V shard in turn and combines the
+ *   partial results (Accelerate concept guide "Context Parallel in accelerate",
+ *   sections "Technical details" and "So how does it work?").  The sequence is
+ *   cut into 2*cp chunks, so its length must be a multiple of 2*cp (NeMo
+ *   Megatron-Bridge "Hierarchical Context Parallel Skill", "Required
+ *   constraints"); rank r holds chunk r followed by chunk 2*cp-1-r, which gives
+ *   every rank the same number of causal (query, key) pairs.  Each step yields a
+ *   partial output O and its log-sum-exp (LSE, natural log); partials over
+ *   disjoint key sets are combined by LSE weighting.
+ *
+ * Conventions shared by every call
+ *   - Return value: CP_OK (0) or a CP_E* code; cp_last_error() then holds a
+ *     message (thread-local, valid until the next call on that thread).
+ *   - All argument checks run before any launch: a failed call has no side
+ *     effects and launches nothing.
+ *   - Ownership: the caller owns every buffer.  The library never allocates
+ *     device memory; scratch space is a caller-provided workspace whose size a
+ *     *_workspace query returns.  Pointers marked (device) must be device
+ *     memory on the current HIP device; (host) ones are ordinary host memory.
+ *   - Streams: device work is enqueued asynchronously on the caller's stream,
+ *     with no implicit synchronisation; a device fault surfaces at the caller's
+ *     next synchronisation.  Calls are re-entrant and keep no state.
+ *   - Layout: tensors are [B, H, rows, D] with the D dimension contiguous
+ *     ("[batch, num_heads, seq_len // context_parallel_size, head_dim]" in the
+ *     guide's pseudocode); element strides for B, H and rows are passed, so row
+ *     range views are legal.  Base pointers and every stride in bytes must be
+ *     multiples of 16.
+ *   - Positions: q_pos / k_pos give the global sequence position of every query
+ *     / key row and q_lo the first position of the query row's document (NULL
+ *     means 0 for every row: plain causal attention).  Key j is allowed for
+ *     query i iff q_lo[i] <= k_pos[j] <= q_pos[i].  Position values are only
+ *     compared, never used as addresses, so any int32 values are memory-safe.
+ *   - Query head h reads key/value head h / (hq / hkv) (grouped-query heads).
+ *   - cp == 1 is valid and means one rank holding the whole sequence: plain
+ *     causal attention (the Accelerate plugin treats a CP size of 1 as off).
+ */
+#ifndef CPATTN_H
+#define CPATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* hipStream_t;
+
+enum cp_status {
+  CP_OK = 0,
+  CP_EINVAL = 1,     /* null pointer, cp < 1, rank out of range, hq % hkv != 0, d not 64/128, bad stride, bad enum */
+  CP_ESHAPE = 2,     /* sequence length not a multiple of 2*cp; cu_seqlens not monotone or not ending at S */
+  CP_EDTYPE = 3,     /* unsupported dtype code */
+  CP_EWORKSPACE = 4, /* workspace missing, too small or misaligned */
+  CP_EHIP = 5        /* HIP launch / runtime error */
+};
+
+enum cp_dtype { CP_F32 = 0, CP_BF16 = 1 };
+
+enum cp_shard_mode {
+  CP_STREAM = 0,  /* zigzag of the packed stream: rank r holds stream chunks r and 2cp-1-r */
+  CP_PER_DOC = 1  /* every document cut into 2cp chunks; rank r holds chunks r and 2cp-1-r of each */
+};
+
+/* Shape and layout descriptor of an attention call. */
+typedef struct cp_shape {
+  int32_t b;          /* batch */
+  int32_t hq;         /* query heads */
+  int32_t hkv;        /* key/value heads; hq % hkv == 0 */
+  int32_t d;          /* head dimension: 64 or 128 */
+  int64_t sq;         /* query rows per (batch, head) */
+  int64_t sk;         /* key/value rows per (batch, kv head) */
+  float scale;        /* softmax scale, finite and > 0 (usually 1/sqrt(d)) */
+  int32_t in_dtype;   /* dtype of q, k, v (and dO): CP_BF16 or CP_F32 */
+  int32_t out_dtype;  /* dtype of the final O of ring calls; partial outputs are always fp32 */
+  int64_t q_str[3];   /* element strides of q for batch, head, row */
+  int64_t k_str[3];   /* same for k */
+  int64_t v_str[3];   /* same for v */
+  int64_t o_str[3];   /* same for o (in elements of o's dtype) */
+} cp_shape;
+
+/* ---------------------------------------------------------------- host index builder */
+
+/* Global positions of rank `rank`'s rows: chunk rank, then chunk 2cp-1-rank,
+ * of a sequence of S tokens cut into 2cp chunks.  pos_out (host) receives S/cp
+ * int32 values.  CP_ESHAPE if S % (2cp) != 0 ("Required constraints" of the
+ * hierarchical-CP skill page); CP_EINVAL for cp < 1, rank outside [0, cp),
+ * S < 0 or S > INT32_MAX. */
+int cp_shard_zigzag(int64_t S, int32_t cp, int32_t rank, int32_t* pos_out);
+
+/* The rank-major concatenation of every rank's positions (what gathering all
+ * shards yields; the guide's "all-gather" section).  perm_out (host) receives S
+ * int32 values forming a permutation of [0, S); its inverse un-shards. */
+int cp_unshard_zigzag(int64_t S, int32_t cp, int32_t* perm_out);
+
+/* Index map of packed documents.  cu_seqlens (host) holds n_docs+1 document
+ * boundaries, starting at 0, non-decreasing, ending at S.  Writes S/cp
+ * positions to pos_out and the start of each row's document to lo_out (host).
+ * mode CP_STREAM deals the whole packed stream zigzag (needs S % 2cp == 0);
+ * CP_PER_DOC deals every document zigzag on its own (needs every document
+ * length % 2cp == 0), keeping documents in order, so a rank's local document
+ * boundaries are cu_seqlens / cp.  The whole-document and per-document
+ * sharding of packed sequences is named in the FlashCP abstract. */
+int cp_varlen_index(const int32_t* cu_seqlens, int32_t n_docs, int32_t cp, int32_t rank,
+                    int32_t mode, int32_t* pos_out, int32_t* lo_out);
+
+/* Rank whose K/V shard rank `rank` attends at ring step `step`: (rank - step)
+ * mod cp; step 0 is the local shard (guide, "all-to-all vs all-gather": every
+ * shard is visited once over cp steps).  Returns that rank, or -1 (with
+ * cp_last_error set) for cp < 1 or rank/step outside [0, cp). */
+int cp_ring_source(int32_t cp, int32_t rank, int32_t step);
+
+/* Exact number of allowed (query, key) pairs, q_lo[i] <= k_pos[j] <= q_pos[i],
+ * over host arrays (q_lo may be NULL).  Used for FLOP accounting and the
+ * zigzag balance check.  Returns the count, or -1 on a null array with n > 0
+ * or a negative length. */
+int64_t cp_pairs(const int32_t* q_pos, const int32_t* q_lo, int64_t nq,
+                 const int32_t* k_pos, int64_t nk);
+
+/* ---------------------------------------------------------------- device calls */
+
+/* Workspace bytes needed by cp_attn_partial_fwd (cp = 1) and cp_attn_ring_fwd
+ * (cp = ring size).  Returns 0 for an invalid descriptor. */
+size_t cp_attn_fwd_workspace(const cp_shape* s, int32_t cp);
+
+/* One ring step, the guide's attn(Q_i, K_j, V_j): every query row attends to
+ * the allowed keys among the sk key rows.  q (device, in_dtype) [b,hq,sq,d];
+ * k, v (device, in_dtype) [b,hkv,sk,d]; q_pos, q_lo (device int32 [sq], q_lo
+ * may be NULL); k_pos (device int32 [sk]).  Writes the partial O (device fp32,
+ * strides o_str) normalised over this step's allowed keys and LSE (device fp32,
+ * contiguous [b,hq,sq]).  A row with no allowed key gets O = 0, LSE = -inf (the
+ * identity of cp_attn_merge).  ws (device) of at least
+ * cp_attn_fwd_workspace(s, 1) bytes, 256-byte aligned. */
+int cp_attn_partial_fwd(const cp_shape* s, const void* q, const void* k, const void* v,
+                        const int32_t* q_pos, const int32_t* q_lo, const int32_t* k_pos,
+                        float* o, float* lse, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* combine(): in place (o_acc, lse_acc) <- (o_acc, lse_acc) (+) (o_p, lse_p) with
+ * L = max(l1,l2) + ln(e^(l1-max) + e^(l2-max)) and O = e^(l1-L) o1 + e^(l2-L) o2.
+ * (0, -inf) is the identity; two empty rows stay (0, -inf).  The operation is
+ * symmetric in its operands bit for bit.  Contiguous device fp32 arrays:
+ * o_* [rows, d], lse_* [rows]; d is 64 or 128.  The pages name combine() but
+ * print no formula; this is the exact recombination of softmax over disjoint
+ * key sets. */
+int cp_attn_merge(int64_t rows, int32_t d, float* o_acc, float* lse_acc,
+                  const float* o_p, const float* lse_p, hipStream_t stream);
+
+/* A whole virtual rank's ring with every K/V shard resident: for step t =
+ * 0..cp-1 the local queries attend the shard of rank (rank - t) mod cp, and the
+ * partials are merged on the fly in registers.  q_loc (device, in_dtype)
+ * [b,hq,sq,d]; k_all, v_all (device, in_dtype) [b,hkv,sk,d] hold every rank's
+ * shard in rank-major order (rows [r*sk/cp, (r+1)*sk/cp) are rank r's), as an
+ * all-gather of the shards lays them out; k_pos_all (device int32 [sk]) their
+ * global positions.  Writes the final O (device, out_dtype, strides o_str) and
+ * LSE (device fp32, contiguous [b,hq,sq]).  CP_ESHAPE unless sk % (2cp) == 0.
+ * ws (device) of at least cp_attn_fwd_workspace(s, cp) bytes, 256-byte
+ * aligned. */
+int cp_attn_ring_fwd(const cp_shape* s, int32_t cp, int32_t rank, const void* q_loc,
+                     const void* k_all, const void* v_all, const int32_t* q_pos,
+                     const int32_t* q_lo, const int32_t* k_pos_all, void* o, float* lse,
+                     void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Message of the last failed call on this thread ("" if none). */
+const char* cp_last_error(void);
+
+/* Library version: major*10000 + minor*100 + patch. */
+int cp_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CPATTN_H */

@@ -1,0 +1,70 @@
+"""Shared set-up for the GPU parity tests: seeded inputs, the shard
+materialisation of one virtual rank, and the oracle's rows for it."""
+import math
+
+import numpy as np
+import torch
+
+import oracle as orc
+import seeded_inputs as si
+import context_causal_attention_amd as cpa
+
+# Acceptance bars: bf16 inputs O <= 2e-2 and LSE <= 1e-3 max-abs against the
+# fp64 oracle; fp32 inputs 1e-5 for both.
+TOL = {"bf16": (2e-2, 1e-3), "f32": (1e-5, 1e-5)}
+
+
+def announce(msg):
+    print(f"[case] {msg}", flush=True)
+
+
+class Rank:
+    """Inputs of one virtual rank, on the GPU, plus fp64 copies for the oracle."""
+
+    def __init__(self, B, Hq, Hkv, S, d, cp, rank, dtype, seed=0, cu=None, mode=cpa.CP_STREAM,
+                 with_dout=False, full=None):
+        self.B, self.Hq, self.Hkv, self.S, self.d, self.cp, self.rank = B, Hq, Hkv, S, d, cp, rank
+        self.dtype, self.cu = dtype, cu
+        if full is None:
+            full = si.make_qkv(B, Hq, Hkv, S, d, dtype, seed=seed, with_dout=with_dout)
+        self.full = full
+        q, k, v = full[:3]
+        if cu is None:
+            self.pos = cpa.cp_shard_zigzag(S, cp, rank)
+            self.lo = None
+            self.allp = cpa.cp_unshard_zigzag(S, cp)
+        else:
+            self.pos, self.lo = cpa.cp_varlen_index(cu, cp, rank, mode)
+            self.allp = np.concatenate([cpa.cp_varlen_index(cu, cp, r, mode)[0] for r in range(cp)])
+        pi = torch.from_numpy(self.pos.astype(np.int64))
+        ai = torch.from_numpy(self.allp.astype(np.int64))
+        self.q_loc = q.index_select(2, pi).cuda()
+        self.k_all = k.index_select(2, ai).cuda()
+        self.v_all = v.index_select(2, ai).cuda()
+        self.scale = 1.0 / math.sqrt(d)
+
+    def ring_fwd(self, out_dtype=None):
+        return cpa.cp_attn_ring_fwd(self.q_loc, self.k_all, self.v_all, self.cp, self.rank, self.pos, self.lo,
+                                    self.allp, scale=self.scale, out_dtype=out_dtype)
+
+    def oracle(self, rows_idx=None):
+        """Oracle O, LSE for this rank's rows (or the subset rows_idx of them)."""
+        q, k, v = (t.double().numpy() for t in self.full[:3])
+        rows = self.pos if rows_idx is None else self.pos[rows_idx]
+        return orc.attention_fwd(q, k, v, self.scale, cu_seqlens=self.cu, rows=rows)
+
+
+def max_err(gpu, ref):
+    g = gpu.detach().double().cpu().numpy()
+    both_inf = np.isneginf(g) & np.isneginf(ref)
+    g = np.where(both_inf, 0.0, g)
+    r = np.where(both_inf, 0.0, ref)
+    return float(np.abs(g - r).max()) if g.size else 0.0
+
+
+def assert_close(o, lse, O_ref, L_ref, dtype, what=""):
+    to, tl = TOL[dtype]
+    eo, el = max_err(o, O_ref), max_err(lse, L_ref)
+    assert np.isfinite(eo) and eo <= to, f"{what}: O max-abs error {eo:.3e} > {to}"
+    assert np.isfinite(el) and el <= tl, f"{what}: LSE max-abs error {el:.3e} > {tl}"
+    return eo, el

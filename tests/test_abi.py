@@ -1,0 +1,222 @@
+"""CPU tests of the C ABI: the library loads and exports every declared symbol,
+the host index builder is bit-exact against the oracle's deal, and invalid
+arguments return error codes before anything is launched (so they need no GPU)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as orc
+import seeded_inputs as si
+import context_causal_attention_amd as cpa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    text = open(os.path.join(ROOT, "include", "cpattn.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(cp_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = cpa.lib()
+    names = _declared_functions()
+    assert "cp_attn_ring_fwd" in names and "cp_shard_zigzag" in names
+    for n in names:
+        assert hasattr(L, n), f"{n} declared in cpattn.h but not exported"
+    assert cpa.cp_version() >= 100
+
+
+@pytest.mark.parametrize("S,cp", [(1024, 2), (32768, 8), (64, 1), (48, 3), (16, 8), (131072, 8)])
+def test_shard_zigzag_bit_exact(S, cp):
+    for r in range(cp):
+        assert np.array_equal(cpa.cp_shard_zigzag(S, cp, r), orc.zigzag_positions(S, cp, r))
+    perm = cpa.cp_unshard_zigzag(S, cp)
+    assert np.array_equal(perm, orc.all_rank_positions(S, cp))
+    assert np.array_equal(np.sort(perm), np.arange(S))
+
+
+def test_seq_multiple_rule_and_argument_errors():
+    with pytest.raises(ValueError, match="multiple of 2"):
+        cpa.cp_shard_zigzag(1000, 8, 0)
+    with pytest.raises(ValueError, match="rank"):
+        cpa.cp_shard_zigzag(1024, 2, 2)
+    with pytest.raises(ValueError, match="cp must be"):
+        cpa.cp_shard_zigzag(1024, 0, 0)
+    with pytest.raises(ValueError):
+        cpa.cp_unshard_zigzag(30, 4)
+    assert cpa.lib().cp_shard_zigzag(1024, 2, 0, None) == cpa.CP_EINVAL
+
+
+def test_cp_one_is_identity():
+    assert np.array_equal(cpa.cp_shard_zigzag(64, 1, 0), np.arange(64))
+
+
+def test_ring_source():
+    for cp in (1, 2, 3, 8):
+        for r in range(cp):
+            srcs = [cpa.cp_ring_source(cp, r, t) for t in range(cp)]
+            assert srcs[0] == r and sorted(srcs) == list(range(cp))
+            assert all(s == (r - t) % cp for t, s in enumerate(srcs))
+    with pytest.raises(ValueError):
+        cpa.cp_ring_source(4, 0, 4)
+    with pytest.raises(ValueError):
+        cpa.cp_ring_source(0, 0, 0)
+
+
+@pytest.mark.parametrize("cp", [1, 2, 3, 5, 8, 16])
+def test_pairs_balance(cp):
+    c = 7
+    S = 2 * cp * c
+    allp = cpa.cp_unshard_zigzag(S, cp)
+    for r in range(cp):
+        pos = cpa.cp_shard_zigzag(S, cp, r)
+        assert cpa.cp_pairs(pos, None, allp) == S * (S + 1) // (2 * cp)
+
+
+def test_pairs_matches_oracle_random():
+    rng = np.random.default_rng(3)
+    for _ in range(10):
+        qp = rng.integers(0, 500, 100)
+        ql = np.minimum(qp, rng.integers(0, 500, 100))
+        kp = rng.integers(0, 500, 80)
+        assert cpa.cp_pairs(qp, ql, kp) == orc.pair_count(qp, ql, kp)
+
+
+def test_varlen_stream_index_matches_oracle():
+    L = si.doc_lengths()
+    cu = si.cu_seqlens_from_lengths(L)
+    S = int(cu[-1])
+    allp = cpa.cp_unshard_zigzag(S, 4)
+    for r in range(4):
+        pos, lo = cpa.cp_varlen_index(cu, 4, r, cpa.CP_STREAM)
+        assert np.array_equal(pos, orc.zigzag_positions(S, 4, r))
+        assert np.array_equal(lo, orc.doc_start_of(pos, cu))
+        assert cpa.cp_pairs(pos, lo, allp) == orc.pair_count(pos, lo, allp)
+
+
+def test_varlen_per_doc_index():
+    cp = 2
+    lengths = np.array([8, 4, 12, 0, 8])
+    cu = si.cu_seqlens_from_lengths(lengths)
+    S = int(cu[-1])
+    got = [cpa.cp_varlen_index(cu, cp, r, cpa.CP_PER_DOC) for r in range(cp)]
+    allpos = np.concatenate([g[0] for g in got])
+    assert np.array_equal(np.sort(allpos), np.arange(S))
+    for r, (pos, lo) in enumerate(got):
+        assert np.array_equal(lo, orc.doc_start_of(pos, cu))
+        # per document: chunk r then chunk 2cp-1-r of that document
+        off = 0
+        for d in range(len(lengths)):
+            n = lengths[d]
+            if n == 0:
+                continue
+            sub = orc.zigzag_positions(n, cp, r) + cu[d]
+            assert np.array_equal(pos[off:off + n // cp], sub)
+            off += n // cp
+    # every rank gets the same number of causal pairs inside documents
+    kp = np.arange(S)
+    counts = [cpa.cp_pairs(p, l, kp) for p, l in got]
+    assert len(set(counts)) == 1
+    with pytest.raises(ValueError, match="multiple of 2"):
+        cpa.cp_varlen_index([0, 6, 16], 2, 0, cpa.CP_PER_DOC)
+
+
+def test_varlen_errors():
+    with pytest.raises(ValueError, match="must be 0"):
+        cpa.cp_varlen_index([1, 8], 2, 0)
+    with pytest.raises(ValueError, match="decreases"):
+        cpa.cp_varlen_index([0, 8, 4, 16], 2, 0)
+    with pytest.raises(ValueError, match="multiple of 2"):
+        cpa.cp_varlen_index([0, 5, 10], 2, 0)
+    with pytest.raises(ValueError, match="shard mode"):
+        cpa.cp_varlen_index([0, 8], 2, 0, mode=7)
+
+
+# ------------------------------------------------------------------ device-call validation (no launch)
+def _shape(**kw):
+    s = cpa.CpShape()
+    s.b, s.hq, s.hkv, s.d = kw.get("b", 1), kw.get("hq", 4), kw.get("hkv", 2), kw.get("d", 128)
+    s.sq, s.sk = kw.get("sq", 256), kw.get("sk", 512)
+    s.scale = kw.get("scale", 0.088)
+    s.in_dtype, s.out_dtype = kw.get("in_dtype", cpa.CP_BF16), kw.get("out_dtype", cpa.CP_F32)
+    d = s.d
+    s.q_str = (ctypes.c_int64 * 3)(s.hq * s.sq * d, s.sq * d, kw.get("q_row", d))
+    s.k_str = (ctypes.c_int64 * 3)(s.hkv * s.sk * d, s.sk * d, d)
+    s.v_str = (ctypes.c_int64 * 3)(s.hkv * s.sk * d, s.sk * d, d)
+    s.o_str = (ctypes.c_int64 * 3)(s.hq * s.sq * d, s.sq * d, d)
+    return s
+
+
+FAKE = 0x10000  # 16-byte aligned non-null address; never dereferenced (validation fails first)
+
+
+def _ring(s, cp=2, rank=0, ws=FAKE, ws_bytes=1 << 40, q=FAKE, qpos=FAKE):
+    L = cpa.lib()
+    return L.cp_attn_ring_fwd(ctypes.byref(s) if s is not None else None, cp, rank, q, FAKE, FAKE, qpos, None,
+                              FAKE, FAKE, FAKE, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(hq=3, hkv=2), cpa.CP_EINVAL),
+    (dict(d=96), cpa.CP_EINVAL),
+    (dict(d=256), cpa.CP_EINVAL),
+    (dict(b=0), cpa.CP_EINVAL),
+    (dict(scale=0.0), cpa.CP_EINVAL),
+    (dict(scale=float("nan")), cpa.CP_EINVAL),
+    (dict(in_dtype=7), cpa.CP_EDTYPE),
+    (dict(out_dtype=3), cpa.CP_EDTYPE),
+    (dict(q_row=129), cpa.CP_EINVAL),
+    (dict(sk=502), cpa.CP_ESHAPE),
+])
+def test_ring_fwd_rejects_bad_shapes(kw, code):
+    assert _ring(_shape(**kw)) == code
+    assert cpa.cp_last_error() != ""
+
+
+def test_ring_fwd_rejects_bad_args():
+    s = _shape()
+    assert _ring(None) == cpa.CP_EINVAL
+    assert _ring(s, cp=0) == cpa.CP_EINVAL
+    assert _ring(s, rank=2) == cpa.CP_EINVAL
+    assert _ring(s, rank=-1) == cpa.CP_EINVAL
+    assert _ring(s, q=0) == cpa.CP_EINVAL
+    assert _ring(s, q=FAKE + 8) == cpa.CP_EINVAL
+    assert _ring(s, qpos=0) == cpa.CP_EINVAL
+    assert _ring(s, ws=0) == cpa.CP_EWORKSPACE
+    assert _ring(s, ws=FAKE + 16) == cpa.CP_EWORKSPACE
+    need = cpa.lib().cp_attn_fwd_workspace(ctypes.byref(s), 2)
+    assert need > 0
+    assert _ring(s, ws_bytes=need - 1) == cpa.CP_EWORKSPACE
+
+
+def test_workspace_query():
+    s = _shape(sk=131072, sq=16384, hq=32, hkv=8)
+    n = cpa.lib().cp_attn_fwd_workspace(ctypes.byref(s), 8)
+    # bf16 V^T copy (8 heads x 128 x 131072 x 2 B) plus the tile bounds table
+    assert n >= 8 * 128 * 131072 * 2
+    assert n < 8 * 128 * 131072 * 2 + (1 << 20)
+    assert cpa.lib().cp_attn_fwd_workspace(ctypes.byref(_shape(d=96)), 8) == 0
+
+
+def test_merge_and_partial_validation():
+    L = cpa.lib()
+    assert L.cp_attn_merge(-1, 128, FAKE, FAKE, FAKE, FAKE, None) == cpa.CP_EINVAL
+    assert L.cp_attn_merge(16, 96, FAKE, FAKE, FAKE, FAKE, None) == cpa.CP_EINVAL
+    assert L.cp_attn_merge(16, 128, 0, FAKE, FAKE, FAKE, None) == cpa.CP_EINVAL
+    assert L.cp_attn_merge(0, 128, FAKE, FAKE, FAKE, FAKE, None) == cpa.CP_OK
+    s = _shape(hq=5, hkv=2)
+    assert L.cp_attn_partial_fwd(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE,
+                                 1 << 30, None) == cpa.CP_EINVAL
+
+
+def test_python_wrappers_raise_value_error():
+    q = torch.zeros(1, 2, 8, 96)
+    with pytest.raises(ValueError):
+        cpa.cp_attn_fwd_workspace(q, q, q, 1)
+    with pytest.raises(ValueError):
+        cpa.cp_attn_merge(torch.zeros(4, 64), torch.zeros(3), torch.zeros(4, 64), torch.zeros(4))
