@@ -26,6 +26,7 @@ typedef float f32x4 __attribute__((__vector_size__(4 * sizeof(float))));
 __global__ __launch_bounds__(256) void merge_kernel(long long n4, int d4, f32x4* __restrict__ o_acc,
                                                     float* lse_acc, const f32x4* __restrict__ o_p,
                                                     const float* __restrict__ lse_p) {
+#pragma clang fp contract(off)
   const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
   if (i >= n4) return;
   const long long row = i / d4;
@@ -38,13 +39,17 @@ __global__ __launch_bounds__(256) void merge_kernel(long long n4, int d4, f32x4*
     out = f32x4{0.f, 0.f, 0.f, 0.f};
     L = -INFINITY;
   } else {
-    L = __fadd_rn(M, logf(__fadd_rn(expf(l1 - M), expf(l2 - M))));
+    L = M + logf(expf(l1 - M) + expf(l2 - M));
     const float w1 = expf(l1 - L);
     const float w2 = expf(l2 - L);
     const f32x4 a = o_acc[i];
     const f32x4 c = o_p[i];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) out[e] = __fadd_rn(__fmul_rn(w1, a[e]), __fmul_rn(w2, c[e]));
+    for (int e = 0; e < 4; ++e) {
+      const float x = w1 * a[e];
+      const float y = w2 * c[e];
+      out[e] = x + y;
+    }
   }
   o_acc[i] = out;
   if (i % d4 == 0) lse_acc[row] = L;
