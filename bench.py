@@ -38,11 +38,30 @@ def parse():
     ap.add_argument("--ranks", default="all", help="'all' or a comma list of virtual ranks")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time for the cpu_baseline sample")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 1 GiB device copy (the reference for HBM byte counters) and exit")
     return ap.parse_args()
+
+
+def calibrate_copy():
+    """A plain device-to-device copy of 1 GiB, three times: its FETCH_SIZE and
+    WRITE_SIZE counter readings against the known 1 GiB give the scale for the
+    attention kernel's HBM traffic counters."""
+    import torch
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibrate_copy_bytes": n, "repeats": 3}), flush=True)
 
 
 def main():
     args = parse()
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the path is one GPU's share; "
               "see DESIGN.md for how it would shard.", file=sys.stderr)

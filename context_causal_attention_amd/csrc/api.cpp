@@ -109,6 +109,8 @@ FwdWorkspace fwd_workspace_layout(int32_t b, int32_t hkv, int32_t d, int64_t sk,
   const int64_t ntiles = tpr * cp;
   w.bounds_off = 0;
   size_t off = align_up((size_t)ntiles * 16, 256);
+  w.kpos_off = off;
+  if (in_dtype == CP_BF16) off += align_up((size_t)ntiles * tk * 4, 256);
   w.vt_off = off;
   w.vt_row = ntiles * tk;
   if (in_dtype == CP_BF16) off += align_up((size_t)b * hkv * d * (size_t)w.vt_row * 2, 256);
@@ -143,6 +145,13 @@ int run_fwd(const cp_shape* s, int32_t cp, int32_t rank, const void* q, const vo
   }
   if (int rc = check_strides(s->o_str, o_dtype, "o")) return rc;
   if (s->o_str[2] < s->d) return fail(CP_EINVAL, "o row stride %lld is smaller than d", (long long)s->o_str[2]);
+  if (s->sk > 0 && (s->k_str[2] < s->d || s->v_str[2] < s->d))
+    return fail(CP_EINVAL, "k/v row strides must be at least d");
+  // The bf16 kernel addresses one (batch, kv head) of K with 32-bit buffer offsets.
+  if (s->in_dtype == CP_BF16 && (double)s->sk * (double)s->k_str[2] * 2.0 >= 4294967040.0)
+    return fail(CP_EINVAL, "key rows x row stride exceed the 4 GiB reach of one buffer descriptor");
+  if (s->sk / cp / tile_keys(s->in_dtype) * (int64_t)cp >= (1 << 24))
+    return fail(CP_EINVAL, "too many key tiles (sk too large)");
   const FwdWorkspace w = fwd_workspace_layout(s->b, s->hkv, s->d, s->sk, cp, s->in_dtype);
   if (!ws) return fail(CP_EWORKSPACE, "workspace is null (%zu bytes needed)", w.total);
   if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0) return fail(CP_EWORKSPACE, "workspace is not 256-byte aligned");

@@ -11,15 +11,15 @@
 // Work decomposition
 //   A workgroup of 4 wave64s owns 128 query rows of one query head (32 rows a
 //   wave) and walks the ring's key tiles in step order.  Key tiles never cross
-//   a rank's shard; a tile is skipped, computed without masks ("full") or with
-//   the per-element mask q_lo <= k_pos <= q_pos ("partial") from the tile's
-//   position bounds, at workgroup granularity for loading and at wave
-//   granularity for compute.
+//   a rank's shard.  Before the walk the workgroup lists the tiles it needs,
+//   each tagged, per wave, as skipped, "full" (no mask needed) or "partial"
+//   (per-element mask q_lo <= k_pos <= q_pos), from the position bounds of the
+//   tile and of the wave's rows.
 //
 // Matrix-core mapping (bf16: v_mfma_f32_32x32x16_bf16; fp32: 32x32x2 f32)
 //   Scores are computed transposed, S^T = K Q^T, so the accumulator column -- a
-//   lane modulo 32 -- is a query row: each lane holds 16 (or 32) scores of its
-//   own row and the row max / row sum need only one cross-lane exchange
+//   lane modulo 32 -- is a query row: each lane holds 16 scores of its own row
+//   per 32-key sub-tile and the row max / row sum need one cross-lane exchange
 //   (lane ^ 32).  The K operand rows are loaded in a permuted key order (bits 2
 //   and 3 of the row index swapped) so that each lane's 8 consecutive
 //   accumulator registers hold 8 consecutive keys; those registers, converted to
@@ -27,6 +27,15 @@
 //   LDS.  V is staged transposed ([d][keys]) so the V^T operand is one 16-byte
 //   LDS read.  The output accumulator O^T likewise keeps one query row per
 //   lane, so the online-softmax rescale is one multiply per register.
+//
+// bf16 data movement
+//   K, V^T and the key positions of the next tile are copied HBM -> LDS by
+//   buffer loads with the LDS-direct bit (no staging registers, no VALU), into
+//   one of two statically addressed buffers while the current tile is computed.
+//   Each tile gets its own buffer descriptor whose record count ends at the
+//   shard's last valid key row, so the rows past it read as zero.  LDS rows are
+//   XOR-swizzled in 16-byte chunks so that the 16 lanes served together read 16
+//   distinct bank groups.
 #include <hip/hip_runtime.h>
 
 #include <climits>
@@ -35,13 +44,16 @@
 #include "internal.h"
 
 namespace cpattn {
-namespace {
+namespace fwdk {
 
 typedef __bf16 bf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
+typedef __bf16 bf16x2 __attribute__((__vector_size__(2 * sizeof(__bf16))));
 typedef float f32x16 __attribute__((__vector_size__(16 * sizeof(float))));
 typedef float f32x4 __attribute__((__vector_size__(4 * sizeof(float))));
+typedef float f32x2 __attribute__((__vector_size__(2 * sizeof(float))));
 typedef unsigned int u32x4 __attribute__((__vector_size__(4 * sizeof(unsigned int))));
 typedef unsigned int u32x2 __attribute__((__vector_size__(2 * sizeof(unsigned int))));
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
@@ -51,6 +63,8 @@ constexpr int kListCap = 2048;          // active key tiles listed per pass
 constexpr float kRescaleLog2 = 8.0f;    // keep a stale running max while scores stay within 2^8 of it
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr int kInvalidKey = INT_MAX;    // position given to padding keys: never allowed
+constexpr int kBufferFlags = 0x00020000;  // buffer descriptor word 3 for gfx9: 32-bit data format
+constexpr int kSkip = 0, kPartial = 1, kFull = 2;
 
 struct KParams {
   const char* q;
@@ -59,6 +73,7 @@ struct KParams {
   const int* q_pos;
   const int* q_lo;          // may be null
   const int* k_pos;
+  const int* kpos_pad;      // bf16: key positions per tile slot, padding = kInvalidKey
   const int4* bounds;       // per key tile {min pos, max pos, valid rows, 0}
   char* o;
   float* lse;
@@ -93,30 +108,147 @@ __device__ __forceinline__ int wave_max(int x) {
   return x;
 }
 
-template <bool BF16, int D>
-struct Cfg {
-  static constexpr int ESZ = BF16 ? 2 : 4;
-  static constexpr int BN = BF16 ? kTileKeysBf16 : kTileKeysF32;  // keys per tile
-  static constexpr int NSUB = BN / 32;                             // 32-key S^T sub-tiles
-  static constexpr int KCHR = D * ESZ / 16;                        // 16-byte chunks per K row
-  static constexpr int K_CHUNKS = BN * KCHR;
-  static constexpr int VCHR = BF16 ? BN / 8 : D / 4;               // chunks per V^T row (bf16) / V row (fp32)
-  static constexpr int V_CHUNKS = BF16 ? D * VCHR : BN * VCHR;
-  static constexpr int KLD = K_CHUNKS / kThreads;                  // staged chunks per thread
-  static constexpr int VLD = V_CHUNKS / kThreads;
-  static constexpr int QREG = BF16 ? D / 16 : D / 2;               // Q operand registers (vectors)
-  static constexpr int DT = D / 32;                                // 32-wide output tiles of O^T
-  static_assert(K_CHUNKS % kThreads == 0 && V_CHUNKS % kThreads == 0, "tile not divisible");
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
+
+// Work item of this workgroup.  Workgroups are dealt round-robin over the 8
+// XCDs; each XCD gets a contiguous range of logical ids so that the query heads
+// sharing one K/V head (and the same key tiles) run on the same L2.  Within a
+// range, query tiles run from the last (most keys under a causal mask) to the
+// first.
+struct Item {
+  int b, h, kvh, qt;
+};
+__device__ __forceinline__ Item map_block(const KParams& p) {
+  const int nblk = gridDim.x;
+  const int bid = blockIdx.x;
+  const int per_xcd = nblk / 8;
+  const int logical = bid < per_xcd * 8 ? (bid % 8) * per_xcd + bid / 8 : bid;
+  const int g = p.Hq / p.Hkv;
+  const int hg = logical % g;
+  int rest = logical / g;
+  Item it;
+  it.qt = p.n_qtiles - 1 - rest % p.n_qtiles;
+  rest /= p.n_qtiles;
+  it.kvh = rest % p.Hkv;
+  it.b = rest / p.Hkv;
+  it.h = it.kvh * g + hg;
+  return it;
+}
+
+// Row bounds of every wave (sWb[w] = {min q_pos, max q_pos, min q_lo, max q_lo}
+// over the wave's valid rows).
+__device__ __forceinline__ void wave_bounds(int wave, int lane, bool valid, int qp, int ql, int (*sWb)[4]) {
+  const int a = wave_min(valid ? qp : INT_MAX);
+  const int b = wave_max(valid ? qp : INT_MIN);
+  const int c = wave_min(valid ? ql : INT_MAX);
+  const int d = wave_max(valid ? ql : INT_MIN);
+  if (lane == 0) {
+    sWb[wave][0] = a;
+    sWb[wave][1] = b;
+    sWb[wave][2] = c;
+    sWb[wave][3] = d;
+  }
+}
+
+// Lists, in ring order, the key tiles of schedule slots [u0, u1) that some wave
+// of this workgroup needs.  Entry = tile | class(wave w) << (24 + 2w).
+template <int BN>
+__device__ __forceinline__ int build_list(const KParams& p, int u0, int u1, int tid, int wave, int lane,
+                                          const int (*sWb)[4], int* sList, int* sCnt) {
+  int cnt = 0;
+  for (int base = u0; base < u1; base += kThreads) {
+    const int u = base + tid;
+    bool act = false;
+    unsigned entry = 0;
+    if (u < u1) {
+      const int t = u / p.tpr;
+      const int i = u - t * p.tpr;
+      int src = p.rank - t;
+      if (src < 0) src += p.cp;
+      const int tile = src * p.tpr + i;
+      const int4 bd = p.bounds[tile];
+      entry = (unsigned)tile;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        int cls = kSkip;
+        if (bd.z > 0 && bd.x <= sWb[w][1] && bd.y >= sWb[w][2])
+          cls = (bd.z == BN && bd.y <= sWb[w][0] && bd.x >= sWb[w][3]) ? kFull : kPartial;
+        entry |= (unsigned)cls << (24 + 2 * w);
+        act |= cls != kSkip;
+      }
+    }
+    const unsigned long long bal = __ballot(act);
+    const int before = __popcll(bal & ((1ull << lane) - 1ull));
+    if (lane == 0) sCnt[wave] = __popcll(bal);
+    __syncthreads();
+    int off = cnt, tot = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      off += w < wave ? sCnt[w] : 0;
+      tot += sCnt[w];
+    }
+    if (act) sList[off + before] = (int)entry;
+    cnt += tot;
+    __syncthreads();
+  }
+  return cnt;
+}
+
+template <int DT>
+__device__ __forceinline__ void store_out(const KParams& p, const Item& it, int row, int hi, float m_run,
+                                          float l_tot, const f32x16* oacc) {
+  const bool empty = !(l_tot > 0.f);
+  const float inv = empty ? 0.f : 1.f / l_tot;
+  if (hi == 0)
+    p.lse[((long long)it.b * p.Hq + it.h) * p.sq + row] = empty ? -INFINITY : (m_run + log2f(l_tot)) * kLn2;
+  const long long obase = (long long)it.b * p.o_sb + (long long)it.h * p.o_sh + (long long)row * p.o_ss;
+#pragma unroll
+  for (int t = 0; t < DT; ++t)
+#pragma unroll
+    for (int rg = 0; rg < 4; ++rg) {
+      const int dv = 32 * t + 8 * rg + 4 * hi;
+      const f32x4 val = {oacc[t][4 * rg] * inv, oacc[t][4 * rg + 1] * inv, oacc[t][4 * rg + 2] * inv,
+                         oacc[t][4 * rg + 3] * inv};
+      if (p.out_bf16) {
+        __bf16 bv[4] = {(__bf16)val[0], (__bf16)val[1], (__bf16)val[2], (__bf16)val[3]};
+        *reinterpret_cast<u32x2*>(p.o + (obase + dv) * 2) = __builtin_bit_cast(u32x2, bv);
+      } else {
+        *reinterpret_cast<f32x4*>(p.o + (obase + dv) * 4) = val;
+      }
+    }
+}
+
+// ============================================================================
+// bf16 kernel
+// ============================================================================
+template <int D>
+struct Bf16Cfg {
+  static constexpr int BN = kTileKeysBf16;       // keys per tile
+  static constexpr int KROW = D * 2;             // bytes per K row in LDS
+  static constexpr int KCHR = D / 8;             // 16-byte chunks per K row
+  static constexpr int VROW = BN * 2;            // bytes per V^T row in LDS (128)
+  static constexpr int VCHR = BN / 8;            // 8
+  static constexpr int KBYTES = BN * KROW;
+  static constexpr int VBYTES = D * VROW;
+  static constexpr int KPW = KBYTES / 1024 / kWaves;  // 1 KB DMA blocks per wave
+  static constexpr int VPW = VBYTES / 1024 / kWaves;
+  static constexpr int QREG = D / 16;
+  static constexpr int DT = D / 32;
+  static_assert(KPW >= 1 && VPW >= 1, "tile too small for the DMA split");
 };
 
-template <bool BF16, int D>
-__global__ __launch_bounds__(kThreads, 2) void fwd_kernel(KParams p) {
-  using C = Cfg<BF16, D>;
-  using QT = typename std::conditional<BF16, bf16x8, float>::type;
-
-  __shared__ __attribute__((aligned(16))) u32x4 sK[2][C::K_CHUNKS];
-  __shared__ __attribute__((aligned(16))) u32x4 sV[2][C::V_CHUNKS];
-  __shared__ __attribute__((aligned(16))) int sKpos[2][C::BN];
+template <int D>
+__global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(KParams p) {
+  // The body uses device-only buffer-descriptor types; the host pass only needs
+  // the launch stub.
+#if defined(__HIP_DEVICE_COMPILE__)
+  using C = Bf16Cfg<D>;
+  __shared__ __attribute__((aligned(1024))) char sK0[C::KBYTES];
+  __shared__ __attribute__((aligned(1024))) char sK1[C::KBYTES];
+  __shared__ __attribute__((aligned(1024))) char sV0[C::VBYTES];
+  __shared__ __attribute__((aligned(1024))) char sV1[C::VBYTES];
+  __shared__ __attribute__((aligned(16))) int sP0[C::BN];
+  __shared__ __attribute__((aligned(16))) int sP1[C::BN];
   __shared__ int sList[kListCap];
   __shared__ int sCnt[kWaves];
   __shared__ int sWb[kWaves][4];
@@ -126,68 +258,81 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(KParams p) {
   const int lane = tid & 63;
   const int l32 = lane & 31;
   const int hi = lane >> 5;
-
-  // ---- block -> (batch, kv head, query tile, query head) ------------------
-  // Workgroups are dealt round-robin over the 8 XCDs; give each XCD a
-  // contiguous range of logical ids so that the query heads sharing one K/V
-  // head (and the same key tiles) run on the same L2.  Within a range, query
-  // tiles run from the last (most keys under a causal mask) to the first.
-  const int nblk = gridDim.x;
-  const int bid = blockIdx.x;
-  const int per_xcd = nblk / 8;
-  const int logical = bid < per_xcd * 8 ? (bid % 8) * per_xcd + bid / 8 : bid;
-  const int g = p.Hq / p.Hkv;
-  const int hg = logical % g;
-  int rest = logical / g;
-  const int qt = p.n_qtiles - 1 - rest % p.n_qtiles;
-  rest /= p.n_qtiles;
-  const int kvh = rest % p.Hkv;
-  const int b = rest / p.Hkv;
-  const int h = kvh * g + hg;
-
-  const int row = qt * kBlockM + wave * kRowsPerWave + l32;
+  const Item it = map_block(p);
+  const int row = it.qt * kBlockM + wave * kRowsPerWave + l32;
   const bool valid = row < p.sq;
 
-  // ---- query operand in registers -----------------------------------------
-  QT qreg[C::QREG];
+  // ---- query operand (B of S^T = K Q^T) in registers ----------------------
+  bf16x8 qreg[C::QREG];
   {
-    const char* qrow = p.q + ((long long)b * p.q_sb + (long long)h * p.q_sh + (long long)row * p.q_ss) * C::ESZ;
-    if constexpr (BF16) {
+    const char* qrow = p.q + ((long long)it.b * p.q_sb + (long long)it.h * p.q_sh + (long long)row * p.q_ss) * 2;
 #pragma unroll
-      for (int kk = 0; kk < C::QREG; ++kk) {
-        u32x4 raw = valid ? *reinterpret_cast<const u32x4*>(qrow + (16 * kk + 8 * hi) * 2) : u32x4{0, 0, 0, 0};
-        qreg[kk] = __builtin_bit_cast(bf16x8, raw);
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < D / 8; ++j) {
-        f32x4 raw = valid ? *reinterpret_cast<const f32x4*>(qrow + (hi * (D / 2) + 4 * j) * 4) : f32x4{0, 0, 0, 0};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) qreg[4 * j + e] = raw[e];
-      }
+    for (int kk = 0; kk < C::QREG; ++kk) {
+      const u32x4 raw = valid ? *reinterpret_cast<const u32x4*>(qrow + (16 * kk + 8 * hi) * 2) : u32x4{0, 0, 0, 0};
+      qreg[kk] = __builtin_bit_cast(bf16x8, raw);
     }
   }
   const int qp = valid ? p.q_pos[row] : -1;
   const int ql = valid ? (p.q_lo ? p.q_lo[row] : 0) : INT_MAX;
-
-  // ---- position bounds of this wave's and this workgroup's rows -----------
-  const int wqmin = wave_min(valid ? qp : INT_MAX);
-  const int wqmax = wave_max(valid ? qp : INT_MIN);
-  const int wlmin = wave_min(valid ? ql : INT_MAX);
-  const int wlmax = wave_max(valid ? ql : INT_MIN);
-  if (lane == 0) {
-    sWb[wave][0] = wqmin;
-    sWb[wave][1] = wqmax;
-    sWb[wave][2] = wlmin;
-    sWb[wave][3] = wlmax;
-  }
+  wave_bounds(wave, lane, valid, qp, ql, sWb);
   __syncthreads();
-  int gqmax = INT_MIN, glmin = INT_MAX;
+
+  // ---- per-lane constant addresses ------------------------------------------
+  // DMA: this lane's 16-byte slot in each of the wave's 1 KB blocks.
+  const long long k_row_bytes = p.k_ss * 2;
+  int voffK[C::KPW], voffV[C::VPW];
 #pragma unroll
-  for (int w = 0; w < kWaves; ++w) {
-    gqmax = max(gqmax, sWb[w][1]);
-    glmin = min(glmin, sWb[w][2]);
+  for (int j = 0; j < C::KPW; ++j) {
+    const int c = (wave + kWaves * j) * 64 + lane;  // physical chunk index within the K tile
+    const int r = c / C::KCHR, ph = c % C::KCHR;
+    voffK[j] = (int)(r * k_row_bytes) + 16 * swz<C::KCHR>(r, ph);
   }
+  const long long vt_row_bytes = p.v_ss * 2;
+#pragma unroll
+  for (int j = 0; j < C::VPW; ++j) {
+    const int c = (wave + kWaves * j) * 64 + lane;
+    const int r = c / C::VCHR, ph = c % C::VCHR;
+    voffV[j] = (int)(r * vt_row_bytes) + 16 * swz<C::VCHR>(r, ph);
+  }
+  // LDS reads: K operand rows key_perm(l32) (+32 for the second sub-tile),
+  // V^T operand rows l32 (+32 per output tile).
+  const int krow = key_perm(l32);
+  int kaddr[C::QREG];
+#pragma unroll
+  for (int kk = 0; kk < C::QREG; ++kk) kaddr[kk] = krow * C::KROW + 16 * swz<C::KCHR>(krow, 2 * kk + hi);
+  int vaddr[4];
+#pragma unroll
+  for (int kg = 0; kg < 4; ++kg) vaddr[kg] = l32 * C::VROW + 16 * swz<C::VCHR>(l32, 2 * kg + hi);
+
+  const char* kbase = p.k + ((long long)it.b * p.k_sb + (long long)it.kvh * p.k_sh) * 2;
+  const char* vtbase = p.v + ((long long)it.b * p.v_sb + (long long)it.kvh * p.v_sh) * 2;
+  const __amdgpu_buffer_rsrc_t rsV =
+      __builtin_amdgcn_make_buffer_rsrc((void*)vtbase, 0, (int)(D * vt_row_bytes), kBufferFlags);
+  const __amdgpu_buffer_rsrc_t rsP =
+      __builtin_amdgcn_make_buffer_rsrc((void*)p.kpos_pad, 0, 0x7fffffff, kBufferFlags);
+
+  // Copies tile `tile` (uniform) into LDS buffer `buf` (static).
+  auto issue = [&](auto bufc, int tile) {
+    constexpr int buf = decltype(bufc)::value;
+    char* sK = buf ? sK1 : sK0;
+    char* sV = buf ? sV1 : sV0;
+    int* sP = buf ? sP1 : sP0;
+    const int src = tile / p.tpr;
+    const int i = tile - src * p.tpr;
+    const int r0 = src * p.R + i * C::BN;
+    const int nval = min(C::BN, p.R - i * C::BN);
+    const __amdgpu_buffer_rsrc_t rsK = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(kbase + (long long)r0 * k_row_bytes), 0, (int)(nval * k_row_bytes), kBufferFlags);
+#pragma unroll
+    for (int j = 0; j < C::KPW; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsK, (lds_ptr_t)(sK + (wave + kWaves * j) * 1024), 16, voffK[j], 0, 0, 0);
+#pragma unroll
+    for (int j = 0; j < C::VPW; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsV, (lds_ptr_t)(sV + (wave + kWaves * j) * 1024), 16, voffV[j],
+                                               tile * C::BN * 2, 0, 0);
+    if (wave == 0)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsP, (lds_ptr_t)sP, 4, lane * 4, tile * C::BN * 4, 0, 0);
+  };
 
   // ---- online softmax state ------------------------------------------------
   f32x16 oacc[C::DT];
@@ -195,117 +340,54 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(KParams p) {
   for (int t = 0; t < C::DT; ++t)
 #pragma unroll
     for (int r = 0; r < 16; ++r) oacc[t][r] = 0.f;
-  float m_run = -INFINITY;  // running max of scale*log2(e)*s, shared by lanes l and l^32
+  float m_run = -INFINITY;  // running max of scale*log2(e)*s, equal in lanes l and l^32
   float l_run = 0.f;        // this lane's part of the running sum
 
-  const long long kbase = (long long)b * p.k_sb + (long long)kvh * p.k_sh;
-  const long long vbase = (long long)b * p.v_sb + (long long)kvh * p.v_sh;
+  auto compute = [&](auto bufc, int cls) {
+    constexpr int buf = decltype(bufc)::value;
+    const char* sK = buf ? sK1 : sK0;
+    const char* sV = buf ? sV1 : sV0;
+    const int* sP = buf ? sP1 : sP0;
+    if (cls == kSkip) return;
 
-  // Staging registers for the next tile.
-  u32x4 kst[C::KLD];
-  u32x4 vst[C::VLD];
-  int kpst = kInvalidKey;
-  int4 bd_next = {0, 0, 0, 0};
-
-  auto stage_load = [&](int tile) {
-    const int src = tile / p.tpr;
-    const int i = tile - src * p.tpr;
-    const int r0 = src * p.R + i * C::BN;  // first key row of the tile
-    const int nval = min(C::BN, p.R - i * C::BN);
+    f32x16 s0, s1;
 #pragma unroll
-    for (int j = 0; j < C::KLD; ++j) {
-      const int c = tid + j * kThreads;
-      const int r = c / C::KCHR, ch = c % C::KCHR;
-      kst[j] = r < nval ? *reinterpret_cast<const u32x4*>(p.k + ((kbase + (long long)(r0 + r) * p.k_ss) * C::ESZ + ch * 16))
-                        : u32x4{0, 0, 0, 0};
+    for (int r = 0; r < 16; ++r) {
+      s0[r] = 0.f;
+      s1[r] = 0.f;
     }
 #pragma unroll
-    for (int j = 0; j < C::VLD; ++j) {
-      const int c = tid + j * kThreads;
-      if constexpr (BF16) {
-        const int dv = c / C::VCHR, ch = c % C::VCHR;
-        vst[j] = *reinterpret_cast<const u32x4*>(p.v + ((vbase + (long long)dv * p.v_ss + (long long)tile * C::BN) * 2 + ch * 16));
-      } else {
-        const int r = c / C::VCHR, ch = c % C::VCHR;
-        vst[j] = r < nval ? *reinterpret_cast<const u32x4*>(p.v + ((vbase + (long long)(r0 + r) * p.v_ss) * 4 + ch * 16))
-                          : u32x4{0, 0, 0, 0};
-      }
-    }
-    if (tid < C::BN) kpst = tid < nval ? p.k_pos[r0 + tid] : kInvalidKey;
-    bd_next = p.bounds[tile];
-  };
-
-  auto stage_store = [&](int buf) {
-#pragma unroll
-    for (int j = 0; j < C::KLD; ++j) {
-      const int c = tid + j * kThreads;
-      const int r = c / C::KCHR, ch = c % C::KCHR;
-      sK[buf][r * C::KCHR + swz<C::KCHR>(r, ch)] = kst[j];
+    for (int kk = 0; kk < C::QREG; ++kk) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(sK + kaddr[kk]);
+      s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[kk], s0, 0, 0, 0);
     }
 #pragma unroll
-    for (int j = 0; j < C::VLD; ++j) {
-      const int c = tid + j * kThreads;
-      if constexpr (BF16) {
-        const int dv = c / C::VCHR, ch = c % C::VCHR;
-        sV[buf][dv * C::VCHR + swz<C::VCHR>(dv, ch)] = vst[j];
-      } else {
-        sV[buf][c] = vst[j];
-      }
+    for (int kk = 0; kk < C::QREG; ++kk) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(sK + kaddr[kk] + 32 * C::KROW);
+      s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[kk], s1, 0, 0, 0);
     }
-    if (tid < C::BN) sKpos[buf][tid] = kpst;
-  };
-
-  auto compute = [&](int buf, int4 bd) {
-    // Wave-level class of this tile: skip, full (no mask) or partial.
-    if (bd.x > wqmax || bd.y < wlmin) return;
-    const bool full = bd.z == C::BN && bd.y <= wqmin && bd.x >= wlmax;
-
-    f32x16 sacc[C::NSUB];
-#pragma unroll
-    for (int sub = 0; sub < C::NSUB; ++sub) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) sacc[sub][r] = 0.f;
-      const int krow = 32 * sub + key_perm(l32);
-      if constexpr (BF16) {
-#pragma unroll
-        for (int kk = 0; kk < C::QREG; ++kk) {
-          const bf16x8 a = __builtin_bit_cast(bf16x8, sK[buf][krow * C::KCHR + swz<C::KCHR>(krow, 2 * kk + hi)]);
-          sacc[sub] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[kk], sacc[sub], 0, 0, 0);
-        }
-      } else {
-#pragma unroll
-        for (int j = 0; j < D / 8; ++j) {
-          const f32x4 a = __builtin_bit_cast(f32x4, sK[buf][krow * C::KCHR + swz<C::KCHR>(krow, hi * (D / 8) + j)]);
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            sacc[sub] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[e], qreg[4 * j + e], sacc[sub], 0, 0, 0);
-        }
-      }
-    }
-
     // Register r of sub-tile sub holds key 32*sub + 16*(r/8) + 8*hi + r%8.
-    if (!full) {
+    if (cls == kPartial) {
 #pragma unroll
-      for (int sub = 0; sub < C::NSUB; ++sub)
+      for (int gg = 0; gg < 4; ++gg) {
+        const int* kp = sP + 16 * gg + 8 * hi;
+        const int4 k0 = *reinterpret_cast<const int4*>(kp);
+        const int4 k1 = *reinterpret_cast<const int4*>(kp + 4);
+        const int kv[8] = {k0.x, k0.y, k0.z, k0.w, k1.x, k1.y, k1.z, k1.w};
 #pragma unroll
-        for (int gg = 0; gg < 2; ++gg) {
-          const int* kp = &sKpos[buf][32 * sub + 16 * gg + 8 * hi];
-          const int4 k0 = *reinterpret_cast<const int4*>(kp);
-          const int4 k1 = *reinterpret_cast<const int4*>(kp + 4);
-          const int kv[8] = {k0.x, k0.y, k0.z, k0.w, k1.x, k1.y, k1.z, k1.w};
-#pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            const bool ok = kv[j] >= ql && kv[j] <= qp;
-            sacc[sub][8 * gg + j] = ok ? sacc[sub][8 * gg + j] : -INFINITY;
-          }
+        for (int j = 0; j < 8; ++j) {
+          const bool ok = kv[j] >= ql && kv[j] <= qp;
+          if (gg < 2) s0[8 * gg + j] = ok ? s0[8 * gg + j] : -INFINITY;
+          else s1[8 * (gg - 2) + j] = ok ? s1[8 * (gg - 2) + j] : -INFINITY;
         }
+      }
     }
 
-    float mx = -INFINITY;
+    float mx = fmaxf(s0[0], s0[1]);
 #pragma unroll
-    for (int sub = 0; sub < C::NSUB; ++sub)
+    for (int r = 2; r < 16; ++r) mx = fmaxf(mx, s0[r]);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[sub][r]);
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s1[r]);
     mx = fmaxf(mx, __shfl_xor(mx, 32));
     const float mnew = fmaxf(m_run, mx * p.c2);
     const bool need = mnew > m_run + kRescaleLog2;
@@ -318,129 +400,254 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(KParams p) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[t][r] *= alpha;
     }
-    const float m_use = m_run == -INFINITY ? 0.f : m_run;
-#pragma unroll
-    for (int sub = 0; sub < C::NSUB; ++sub)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[sub][r], p.c2, -m_use));
-        l_run += e;
-        sacc[sub][r] = e;
-      }
+    const float nm = m_run == -INFINITY ? 0.f : -m_run;
 
-    // O^T += V^T P^T
-    if constexpr (BF16) {
+    // P = exp2(c2*s - m).  The row sum adds the fp32 values (the LSE needs
+    // them); P enters the PV product rounded to bf16.  O^T += V^T P^T per
+    // 16-key group.
 #pragma unroll
-      for (int kg = 0; kg < 2 * C::NSUB; ++kg) {
-        bf16x8 pb;
+    for (int kg = 0; kg < 4; ++kg) {
+      const f32x16& sv = kg < 2 ? s0 : s1;
+      const int base = 8 * (kg & 1);
+      bf16x8 pb;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) pb[j] = (__bf16)sacc[kg >> 1][8 * (kg & 1) + j];
-#pragma unroll
-        for (int t = 0; t < C::DT; ++t) {
-          const int vr = 32 * t + l32;
-          const bf16x8 a = __builtin_bit_cast(bf16x8, sV[buf][vr * C::VCHR + swz<C::VCHR>(vr, 2 * kg + hi)]);
-          oacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, oacc[t], 0, 0, 0);
-        }
+      for (int j = 0; j < 8; j += 2) {
+        const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[base + j], p.c2, nm));
+        const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[base + j + 1], p.c2, nm));
+        const bf16x2 pr = __builtin_convertvector((f32x2){e0, e1}, bf16x2);
+        l_run += e0 + e1;
+        pb[j] = pr[0];
+        pb[j + 1] = pr[1];
       }
-    } else {
-      const float* vf = reinterpret_cast<const float*>(&sV[buf][0]);
 #pragma unroll
-      for (int s = 0; s < 16; ++s) {
-        const int key = 16 * (s >> 3) + 8 * hi + (s & 7);
-#pragma unroll
-        for (int t = 0; t < C::DT; ++t)
-          oacc[t] = __builtin_amdgcn_mfma_f32_32x32x2f32(vf[key * D + 32 * t + l32], sacc[0][s], oacc[t], 0, 0, 0);
+      for (int t = 0; t < C::DT; ++t) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(sV + vaddr[kg] + t * 32 * C::VROW);
+        oacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, oacc[t], 0, 0, 0);
       }
     }
   };
 
-  // ---- walk the ring: list the active key tiles, then stream them ---------
+  // ---- walk the ring: list the needed key tiles, then stream them ---------
   const int total = p.cp * p.tpr;
+  const int csh = 24 + 2 * wave;
   for (int u0 = 0; u0 < total; u0 += kListCap) {
-    const int u1 = min(total, u0 + kListCap);
-    int cnt = 0;
-    for (int base = u0; base < u1; base += kThreads) {
-      const int u = base + tid;
-      bool act = false;
-      int tile = 0;
-      if (u < u1) {
-        const int t = u / p.tpr;
-        const int i = u - t * p.tpr;
-        int src = p.rank - t;
-        if (src < 0) src += p.cp;
-        tile = src * p.tpr + i;
-        const int4 bd = p.bounds[tile];
-        act = bd.z > 0 && bd.x <= gqmax && bd.y >= glmin;
-      }
-      const unsigned long long bal = __ballot(act);
-      const int before = __popcll(bal & ((1ull << lane) - 1ull));
-      if (lane == 0) sCnt[wave] = __popcll(bal);
-      __syncthreads();
-      int off = cnt, tot = 0;
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
-        off += w < wave ? sCnt[w] : 0;
-        tot += sCnt[w];
-      }
-      if (act) sList[off + before] = tile;
-      cnt += tot;
-      __syncthreads();
-    }
+    const int cnt = build_list<C::BN>(p, u0, min(total, u0 + kListCap), tid, wave, lane, sWb, sList, sCnt);
     if (cnt == 0) continue;
-    stage_load(sList[0]);
+    int e = __builtin_amdgcn_readfirstlane(sList[0]);
+    issue(std::integral_constant<int, 0>{}, e & 0xFFFFFF);
+    wait_vmem();
+    __syncthreads();
+    for (int j = 0;;) {
+      // tile j sits in buffer 0
+      int e1 = 0;
+      if (j + 1 < cnt) {
+        e1 = __builtin_amdgcn_readfirstlane(sList[j + 1]);
+        issue(std::integral_constant<int, 1>{}, e1 & 0xFFFFFF);
+      }
+      compute(std::integral_constant<int, 0>{}, ((unsigned)e >> csh) & 3);
+      wait_vmem();
+      __syncthreads();
+      if (++j >= cnt) break;
+      // tile j sits in buffer 1
+      if (j + 1 < cnt) {
+        e = __builtin_amdgcn_readfirstlane(sList[j + 1]);
+        issue(std::integral_constant<int, 0>{}, e & 0xFFFFFF);
+      }
+      compute(std::integral_constant<int, 1>{}, ((unsigned)e1 >> csh) & 3);
+      wait_vmem();
+      __syncthreads();
+      if (++j >= cnt) break;
+    }
+  }
+
+  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  if (valid) store_out<C::DT>(p, it, row, hi, m_run, l_tot, oacc);
+#endif
+}
+
+// ============================================================================
+// fp32 kernel (exact-precision path: P stays fp32; staged through registers)
+// ============================================================================
+template <int D>
+struct F32Cfg {
+  static constexpr int BN = kTileKeysF32;        // 32 keys per tile
+  static constexpr int KCHR = D / 4;             // 16-byte chunks per row
+  static constexpr int CHUNKS = BN * KCHR;       // per tile, for K and for V
+  static constexpr int LD = CHUNKS / kThreads;   // staged chunks per thread
+  static constexpr int QREG = D / 2;
+  static constexpr int DT = D / 32;
+  static_assert(CHUNKS % kThreads == 0, "tile not divisible");
+};
+
+template <int D>
+__global__ __launch_bounds__(kThreads, 2) void fwd_f32_kernel(KParams p) {
+  using C = F32Cfg<D>;
+  __shared__ __attribute__((aligned(16))) u32x4 sK[2][C::CHUNKS];
+  __shared__ __attribute__((aligned(16))) u32x4 sV[2][C::CHUNKS];
+  __shared__ __attribute__((aligned(16))) int sKpos[2][C::BN];
+  __shared__ int sList[kListCap];
+  __shared__ int sCnt[kWaves];
+  __shared__ int sWb[kWaves][4];
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int l32 = lane & 31;
+  const int hi = lane >> 5;
+  const Item it = map_block(p);
+  const int row = it.qt * kBlockM + wave * kRowsPerWave + l32;
+  const bool valid = row < p.sq;
+
+  // Lane half hi holds d indices hi*D/2 .. hi*D/2 + D/2 - 1 of its row.
+  float qreg[C::QREG];
+  {
+    const char* qrow = p.q + ((long long)it.b * p.q_sb + (long long)it.h * p.q_sh + (long long)row * p.q_ss) * 4;
+#pragma unroll
+    for (int j = 0; j < D / 8; ++j) {
+      const f32x4 raw = valid ? *reinterpret_cast<const f32x4*>(qrow + (hi * (D / 2) + 4 * j) * 4) : f32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) qreg[4 * j + e] = raw[e];
+    }
+  }
+  const int qp = valid ? p.q_pos[row] : -1;
+  const int ql = valid ? (p.q_lo ? p.q_lo[row] : 0) : INT_MAX;
+  wave_bounds(wave, lane, valid, qp, ql, sWb);
+  __syncthreads();
+
+  f32x16 oacc[C::DT];
+#pragma unroll
+  for (int t = 0; t < C::DT; ++t)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) oacc[t][r] = 0.f;
+  float m_run = -INFINITY;
+  float l_run = 0.f;
+
+  const long long kbase = (long long)it.b * p.k_sb + (long long)it.kvh * p.k_sh;
+  const long long vbase = (long long)it.b * p.v_sb + (long long)it.kvh * p.v_sh;
+  u32x4 kst[C::LD];
+  u32x4 vst[C::LD];
+  int kpst = kInvalidKey;
+
+  auto stage_load = [&](int tile) {
+    const int src = tile / p.tpr;
+    const int i = tile - src * p.tpr;
+    const int r0 = src * p.R + i * C::BN;
+    const int nval = min(C::BN, p.R - i * C::BN);
+#pragma unroll
+    for (int j = 0; j < C::LD; ++j) {
+      const int c = tid + j * kThreads;
+      const int r = c / C::KCHR, ch = c % C::KCHR;
+      kst[j] = r < nval ? *reinterpret_cast<const u32x4*>(p.k + ((kbase + (long long)(r0 + r) * p.k_ss) * 4 + ch * 16))
+                        : u32x4{0, 0, 0, 0};
+      vst[j] = r < nval ? *reinterpret_cast<const u32x4*>(p.v + ((vbase + (long long)(r0 + r) * p.v_ss) * 4 + ch * 16))
+                        : u32x4{0, 0, 0, 0};
+    }
+    if (tid < C::BN) kpst = tid < nval ? p.k_pos[r0 + tid] : kInvalidKey;
+  };
+  auto stage_store = [&](int buf) {
+#pragma unroll
+    for (int j = 0; j < C::LD; ++j) {
+      const int c = tid + j * kThreads;
+      const int r = c / C::KCHR, ch = c % C::KCHR;
+      sK[buf][r * C::KCHR + swz<C::KCHR>(r, ch)] = kst[j];
+      sV[buf][c] = vst[j];
+    }
+    if (tid < C::BN) sKpos[buf][tid] = kpst;
+  };
+
+  auto compute = [&](int buf, int cls) {
+    if (cls == kSkip) return;
+    f32x16 s;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[r] = 0.f;
+    const int kr = key_perm(l32);
+#pragma unroll
+    for (int j = 0; j < D / 8; ++j) {
+      const f32x4 a = __builtin_bit_cast(f32x4, sK[buf][kr * C::KCHR + swz<C::KCHR>(kr, hi * (D / 8) + j)]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) s = __builtin_amdgcn_mfma_f32_32x32x2f32(a[e], qreg[4 * j + e], s, 0, 0, 0);
+    }
+    if (cls == kPartial) {
+#pragma unroll
+      for (int gg = 0; gg < 2; ++gg) {
+        const int* kp = &sKpos[buf][16 * gg + 8 * hi];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const bool ok = kp[j] >= ql && kp[j] <= qp;
+          s[8 * gg + j] = ok ? s[8 * gg + j] : -INFINITY;
+        }
+      }
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[r]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float mnew = fmaxf(m_run, mx * p.c2);
+    const bool need = mnew > m_run + kRescaleLog2;
+    if (__any(need)) {
+      const float alpha = need ? __builtin_amdgcn_exp2f(m_run - mnew) : 1.f;
+      m_run = need ? mnew : m_run;
+      l_run *= alpha;
+#pragma unroll
+      for (int t = 0; t < C::DT; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[t][r] *= alpha;
+    }
+    const float nm = m_run == -INFINITY ? 0.f : -m_run;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], p.c2, nm));
+      l_run += e;
+      s[r] = e;
+    }
+    const float* vf = reinterpret_cast<const float*>(&sV[buf][0]);
+#pragma unroll
+    for (int st = 0; st < 16; ++st) {
+      const int key = 16 * (st >> 3) + 8 * hi + (st & 7);
+#pragma unroll
+      for (int t = 0; t < C::DT; ++t)
+        oacc[t] = __builtin_amdgcn_mfma_f32_32x32x2f32(vf[key * D + 32 * t + l32], s[st], oacc[t], 0, 0, 0);
+    }
+  };
+
+  const int total = p.cp * p.tpr;
+  const int csh = 24 + 2 * wave;
+  for (int u0 = 0; u0 < total; u0 += kListCap) {
+    const int cnt = build_list<C::BN>(p, u0, min(total, u0 + kListCap), tid, wave, lane, sWb, sList, sCnt);
+    if (cnt == 0) continue;
+    stage_load(sList[0] & 0xFFFFFF);
     stage_store(0);
-    int4 bd_cur = bd_next;
     __syncthreads();
     for (int j = 0; j < cnt; ++j) {
       const int cur = j & 1;
       const bool has_next = j + 1 < cnt;
-      if (has_next) stage_load(sList[j + 1]);
-      compute(cur, bd_cur);
+      const int e = __builtin_amdgcn_readfirstlane(sList[j]);
+      if (has_next) stage_load(sList[j + 1] & 0xFFFFFF);
+      compute(cur, ((unsigned)e >> csh) & 3);
       if (has_next) stage_store(cur ^ 1);
-      bd_cur = bd_next;
       __syncthreads();
     }
   }
 
-  // ---- epilogue: normalise and store O and LSE ----------------------------
   const float l_tot = l_run + __shfl_xor(l_run, 32);
-  const bool empty = !(l_tot > 0.f);
-  const float inv = empty ? 0.f : 1.f / l_tot;
-  if (valid) {
-    if (hi == 0)
-      p.lse[((long long)b * p.Hq + h) * p.sq + row] = empty ? -INFINITY : (m_run + log2f(l_tot)) * kLn2;
-    const long long obase = (long long)b * p.o_sb + (long long)h * p.o_sh + (long long)row * p.o_ss;
-#pragma unroll
-    for (int t = 0; t < C::DT; ++t)
-#pragma unroll
-      for (int rg = 0; rg < 4; ++rg) {
-        const int dv = 32 * t + 8 * rg + 4 * hi;
-        const f32x4 val = {oacc[t][4 * rg] * inv, oacc[t][4 * rg + 1] * inv, oacc[t][4 * rg + 2] * inv,
-                           oacc[t][4 * rg + 3] * inv};
-        if (p.out_bf16) {
-          __bf16 bv[4] = {(__bf16)val[0], (__bf16)val[1], (__bf16)val[2], (__bf16)val[3]};
-          *reinterpret_cast<u32x2*>(p.o + (obase + dv) * 2) = __builtin_bit_cast(u32x2, bv);
-        } else {
-          *reinterpret_cast<f32x4*>(p.o + (obase + dv) * 4) = val;
-        }
-      }
-  }
+  if (valid) store_out<C::DT>(p, it, row, hi, m_run, l_tot, oacc);
 }
 
-// Per key tile: position bounds and count of valid rows; for bf16 inputs also
-// V transposed into the workspace ([b][kv head][d][tile * BN + key], zero in
-// the padding of a shard's last tile) so the kernel above can read V^T rows.
+// Per key tile: position bounds and count of valid rows.  For bf16 inputs also
+// the key positions padded per tile slot and V transposed into the workspace
+// ([b][kv head][d][tile * BN + key], zero in the padding of a shard's last
+// tile) so the kernel above can read V^T rows.
 template <bool BF16, int D>
 __global__ __launch_bounds__(256) void prep_kernel(const int* __restrict__ k_pos, const char* __restrict__ v,
                                                    long long v_sb, long long v_sh, long long v_ss, int Hkv,
-                                                   int R, int tpr, int4* __restrict__ bounds, __bf16* vt,
-                                                   long long vt_row) {
-  using C = Cfg<BF16, D>;
+                                                   int R, int tpr, int4* __restrict__ bounds,
+                                                   int* __restrict__ kpos_pad, __bf16* vt, long long vt_row) {
+  constexpr int BN = BF16 ? kTileKeysBf16 : kTileKeysF32;
   const int tile = blockIdx.x;
   const int src = tile / tpr;
   const int i = tile - src * tpr;
-  const int r0 = src * R + i * C::BN;
-  const int nval = min(C::BN, R - i * C::BN);
+  const int r0 = src * R + i * BN;
+  const int nval = min(BN, R - i * BN);
   const int tid = threadIdx.x;
   if (blockIdx.y == 0 && tid < 64) {
     const bool ok = tid < nval;
@@ -448,22 +655,23 @@ __global__ __launch_bounds__(256) void prep_kernel(const int* __restrict__ k_pos
     const int mn = wave_min(ok ? kp : INT_MAX);
     const int mx = wave_max(ok ? kp : INT_MIN);
     if (tid == 0) bounds[tile] = int4{mn, mx, nval, 0};
+    if (BF16 && tid < BN) kpos_pad[tile * BN + tid] = ok ? kp : kInvalidKey;
   }
   if constexpr (BF16) {
-    __shared__ __bf16 s[C::BN][D + 8];
+    __shared__ __bf16 s[BN][D + 8];
     const int b = blockIdx.y / Hkv, kvh = blockIdx.y % Hkv;
     const char* vb = v + ((long long)b * v_sb + (long long)kvh * v_sh) * 2;
     constexpr int CH = D / 8;  // 16-byte chunks per V row
-    for (int c = tid; c < C::BN * CH; c += 256) {
+    for (int c = tid; c < BN * CH; c += 256) {
       const int r = c / CH, ch = c % CH;
-      u32x4 raw = r < nval ? *reinterpret_cast<const u32x4*>(vb + ((long long)(r0 + r) * v_ss + ch * 8) * 2)
-                           : u32x4{0, 0, 0, 0};
+      const u32x4 raw = r < nval ? *reinterpret_cast<const u32x4*>(vb + ((long long)(r0 + r) * v_ss + ch * 8) * 2)
+                                 : u32x4{0, 0, 0, 0};
       *reinterpret_cast<u32x4*>(&s[r][ch * 8]) = raw;
     }
     __syncthreads();
-    __bf16* out = vt + ((long long)blockIdx.y * D) * vt_row + (long long)tile * C::BN;
-    for (int c = tid; c < D * (C::BN / 8); c += 256) {
-      const int dv = c / (C::BN / 8), kc = c % (C::BN / 8);
+    __bf16* out = vt + ((long long)blockIdx.y * D) * vt_row + (long long)tile * BN;
+    for (int c = tid; c < D * (BN / 8); c += 256) {
+      const int dv = c / (BN / 8), kc = c % (BN / 8);
       bf16x8 w;
 #pragma unroll
       for (int j = 0; j < 8; ++j) w[j] = s[kc * 8 + j][dv];
@@ -474,17 +682,17 @@ __global__ __launch_bounds__(256) void prep_kernel(const int* __restrict__ k_pos
 
 template <bool BF16, int D>
 hipError_t launch_t(const FwdArgs& a, hipStream_t stream) {
-  using C = Cfg<BF16, D>;
   const FwdWorkspace w = fwd_workspace_layout(a.b, a.hkv, a.d, a.sk, a.cp, a.in_dtype);
   char* ws = static_cast<char*>(a.ws);
   int4* bounds = reinterpret_cast<int4*>(ws + w.bounds_off);
+  int* kpos_pad = reinterpret_cast<int*>(ws + w.kpos_off);
   __bf16* vt = reinterpret_cast<__bf16*>(ws + w.vt_off);
   const int ntiles = a.cp * a.tiles_per_rank;
   if (ntiles > 0) {
     dim3 grid(ntiles, BF16 ? a.b * a.hkv : 1);
     hipLaunchKernelGGL((prep_kernel<BF16, D>), grid, dim3(256), 0, stream, a.k_pos,
                        static_cast<const char*>(a.v), (long long)a.v_str[0], (long long)a.v_str[1],
-                       (long long)a.v_str[2], a.hkv, a.rows_per_rank, a.tiles_per_rank, bounds, vt,
+                       (long long)a.v_str[2], a.hkv, a.rows_per_rank, a.tiles_per_rank, bounds, kpos_pad, vt,
                        (long long)w.vt_row);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -495,6 +703,7 @@ hipError_t launch_t(const FwdArgs& a, hipStream_t stream) {
   p.q_pos = a.q_pos;
   p.q_lo = a.q_lo;
   p.k_pos = a.k_pos;
+  p.kpos_pad = kpos_pad;
   p.bounds = bounds;
   p.o = static_cast<char*>(a.o);
   p.lse = a.lse;
@@ -531,13 +740,17 @@ hipError_t launch_t(const FwdArgs& a, hipStream_t stream) {
   p.out_bf16 = a.out_dtype == CP_BF16;
   p.c2 = a.scale_log2;
   const long long nblk = (long long)p.n_qtiles * a.hq * a.b;
-  hipLaunchKernelGGL((fwd_kernel<BF16, D>), dim3((unsigned)nblk), dim3(kThreads), 0, stream, p);
+  if constexpr (BF16)
+    hipLaunchKernelGGL((fwd_bf16_kernel<D>), dim3((unsigned)nblk), dim3(kThreads), 0, stream, p);
+  else
+    hipLaunchKernelGGL((fwd_f32_kernel<D>), dim3((unsigned)nblk), dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 
-}  // namespace
+}  // namespace fwdk
 
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream) {
+  using namespace fwdk;
   if (a.in_dtype == CP_BF16) return a.d == 64 ? launch_t<true, 64>(a, stream) : launch_t<true, 128>(a, stream);
   return a.d == 64 ? launch_t<false, 64>(a, stream) : launch_t<false, 128>(a, stream);
 }

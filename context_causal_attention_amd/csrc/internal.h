@@ -47,6 +47,7 @@ struct FwdArgs {
 
 struct FwdWorkspace {
   size_t bounds_off;   // int4 per key tile: {min pos, max pos, valid rows, 0}
+  size_t kpos_off;     // int32 per key slot of every tile, padding slots = INT32_MAX (bf16 inputs only)
   size_t vt_off;       // bf16 V^T [b][hkv][d][cp * tiles_per_rank * tile_keys] (bf16 inputs only)
   size_t total;
   int64_t vt_row;      // elements per V^T row
