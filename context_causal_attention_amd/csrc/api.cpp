@@ -150,8 +150,11 @@ int run_fwd(const cp_shape* s, int32_t cp, int32_t rank, const void* q, const vo
   // The bf16 kernel addresses one (batch, kv head) of K with 32-bit buffer offsets.
   if (s->in_dtype == CP_BF16 && (double)s->sk * (double)s->k_str[2] * 2.0 >= 4294967040.0)
     return fail(CP_EINVAL, "key rows x row stride exceed the 4 GiB reach of one buffer descriptor");
-  if (s->sk / cp / tile_keys(s->in_dtype) * (int64_t)cp >= (1 << 24))
-    return fail(CP_EINVAL, "too many key tiles (sk too large)");
+  // Listed key tiles carry the ring rank in 8 bits and the tile index within
+  // the rank's shard in 16 bits.
+  if (cp > 255) return fail(CP_EINVAL, "cp must be <= 255 (got %d)", cp);
+  if ((s->sk / cp + tile_keys(s->in_dtype) - 1) / tile_keys(s->in_dtype) > 65535)
+    return fail(CP_EINVAL, "a shard of %lld key rows has more than 65535 key tiles", (long long)(s->sk / cp));
   const FwdWorkspace w = fwd_workspace_layout(s->b, s->hkv, s->d, s->sk, cp, s->in_dtype);
   if (!ws) return fail(CP_EWORKSPACE, "workspace is null (%zu bytes needed)", w.total);
   if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0) return fail(CP_EWORKSPACE, "workspace is not 256-byte aligned");

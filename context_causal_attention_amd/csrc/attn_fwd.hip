@@ -151,7 +151,8 @@ __device__ __forceinline__ void wave_bounds(int wave, int lane, bool valid, int 
 }
 
 // Lists, in ring order, the key tiles of schedule slots [u0, u1) that some wave
-// of this workgroup needs.  Entry = tile | class(wave w) << (24 + 2w).
+// of this workgroup needs.  Entry = src | i << 8 | class(wave w) << (24 + 2w)
+// for key tile i of rank src's shard.
 template <int BN>
 __device__ __forceinline__ int build_list(const KParams& p, int u0, int u1, int tid, int wave, int lane,
                                           const int (*sWb)[4], int* sList, int* sCnt) {
@@ -167,7 +168,7 @@ __device__ __forceinline__ int build_list(const KParams& p, int u0, int u1, int 
       if (src < 0) src += p.cp;
       const int tile = src * p.tpr + i;
       const int4 bd = p.bounds[tile];
-      entry = (unsigned)tile;
+      entry = (unsigned)src | ((unsigned)i << 8);
 #pragma unroll
       for (int w = 0; w < kWaves; ++w) {
         int cls = kSkip;
@@ -254,7 +255,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(KParams p) {
   __shared__ int sWb[kWaves][4];
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps tile-class branches scalar
   const int lane = tid & 63;
   const int l32 = lane & 31;
   const int hi = lane >> 5;
@@ -311,14 +312,14 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(KParams p) {
   const __amdgpu_buffer_rsrc_t rsP =
       __builtin_amdgcn_make_buffer_rsrc((void*)p.kpos_pad, 0, 0x7fffffff, kBufferFlags);
 
-  // Copies tile `tile` (uniform) into LDS buffer `buf` (static).
-  auto issue = [&](auto bufc, int tile) {
+  // List entry: src | i << 8 | class(wave w) << (24 + 2w) for key tile i of
+  // rank src's shard (tile id src * tpr + i).
+  auto tile_of = [&](int e) { return (e & 0xFF) * p.tpr + ((e >> 8) & 0xFFFF); };
+  // Copies K of list entry e (uniform) into LDS buffer `buf` (static).
+  auto issue_k = [&](auto bufc, int e) {
     constexpr int buf = decltype(bufc)::value;
     char* sK = buf ? sK1 : sK0;
-    char* sV = buf ? sV1 : sV0;
-    int* sP = buf ? sP1 : sP0;
-    const int src = tile / p.tpr;
-    const int i = tile - src * p.tpr;
+    const int src = e & 0xFF, i = (e >> 8) & 0xFFFF;
     const int r0 = src * p.R + i * C::BN;
     const int nval = min(C::BN, p.R - i * C::BN);
     const __amdgpu_buffer_rsrc_t rsK = __builtin_amdgcn_make_buffer_rsrc(
@@ -326,6 +327,13 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(KParams p) {
 #pragma unroll
     for (int j = 0; j < C::KPW; ++j)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rsK, (lds_ptr_t)(sK + (wave + kWaves * j) * 1024), 16, voffK[j], 0, 0, 0);
+  };
+  // Copies V^T and the key positions of list entry e into LDS buffer `buf`.
+  auto issue_v = [&](auto bufc, int e) {
+    constexpr int buf = decltype(bufc)::value;
+    char* sV = buf ? sV1 : sV0;
+    int* sP = buf ? sP1 : sP0;
+    const int tile = tile_of(e);
 #pragma unroll
     for (int j = 0; j < C::VPW; ++j)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rsV, (lds_ptr_t)(sV + (wave + kWaves * j) * 1024), 16, voffV[j],
@@ -340,17 +348,19 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(KParams p) {
   for (int t = 0; t < C::DT; ++t)
 #pragma unroll
     for (int r = 0; r < 16; ++r) oacc[t][r] = 0.f;
-  float m_run = -INFINITY;  // running max of scale*log2(e)*s, equal in lanes l and l^32
-  float l_run = 0.f;        // this lane's part of the running sum
+  // Running max of scale*log2(e)*s (equal in lanes l and l^32) and this lane's
+  // part of the running sum.  Exponentials of a tile are taken against the
+  // running max as it stands; only when a lane's partial sum for the tile is
+  // not finite or exceeds 2^40 (first tile of a row, or scores far above the
+  // running max) is the tile's true max taken and the tile redone.
+  float m_run = -INFINITY;
+  float l_run = 0.f;
+  constexpr float kRedo = 1099511627776.0f;  // 2^40
 
-  auto compute = [&](auto bufc, int cls) {
-    constexpr int buf = decltype(bufc)::value;
-    const char* sK = buf ? sK1 : sK0;
-    const char* sV = buf ? sV1 : sV0;
-    const int* sP = buf ? sP1 : sP0;
-    if (cls == kSkip) return;
-
-    f32x16 s0, s1;
+  // S^T = K Q^T of the tile in K buffer kb: 16 MFMAs into (s0, s1).
+  auto scores = [&](auto kbc, f32x16& s0, f32x16& s1) {
+    constexpr int kb = decltype(kbc)::value;
+    const char* sK = kb ? sK1 : sK0;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       s0[r] = 0.f;
@@ -359,15 +369,36 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(KParams p) {
 #pragma unroll
     for (int kk = 0; kk < C::QREG; ++kk) {
       const bf16x8 a = *reinterpret_cast<const bf16x8*>(sK + kaddr[kk]);
+      const bf16x8 b = *reinterpret_cast<const bf16x8*>(sK + kaddr[kk] + 32 * C::KROW);
       s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[kk], s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b, qreg[kk], s1, 0, 0, 0);
     }
+  };
+  // P = exp2(c2*s - m) of group kg (8 keys) rounded to bf16; the fp32 values
+  // go into the tile's row sum (the LSE needs them unrounded).
+  auto expg = [&](const f32x16& c0, const f32x16& c1, int kg, float nm, bf16x8& pb, float& lj) {
+    const f32x16& sv = kg < 2 ? c0 : c1;
+    const int base = 8 * (kg & 1);
 #pragma unroll
-    for (int kk = 0; kk < C::QREG; ++kk) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(sK + kaddr[kk] + 32 * C::KROW);
-      s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[kk], s1, 0, 0, 0);
+    for (int j = 0; j < 8; j += 2) {
+      const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[base + j], p.c2, nm));
+      const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[base + j + 1], p.c2, nm));
+      const bf16x2 pr = __builtin_convertvector((f32x2){e0, e1}, bf16x2);
+      lj += e0 + e1;
+      pb[j] = pr[0];
+      pb[j + 1] = pr[1];
     }
+  };
+
+  // One pipeline stage: tile j's scores (c0, c1) are masked, exponentiated
+  // and multiplied into O (V^T from buffer vb) while tile j+1's scores are
+  // computed into (n0, n1) from K buffer kb.
+  auto stage = [&](auto kbc, auto vbc, f32x16& c0, f32x16& c1, f32x16& n0, f32x16& n1, int cls_cur) {
+    constexpr int vb = decltype(vbc)::value;
+    const char* sV = vb ? sV1 : sV0;
+    const int* sP = vb ? sP1 : sP0;
     // Register r of sub-tile sub holds key 32*sub + 16*(r/8) + 8*hi + r%8.
-    if (cls == kPartial) {
+    if (cls_cur == kPartial) {
 #pragma unroll
       for (int gg = 0; gg < 4; ++gg) {
         const int* kp = sP + 16 * gg + 8 * hi;
@@ -377,85 +408,142 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(KParams p) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           const bool ok = kv[j] >= ql && kv[j] <= qp;
-          if (gg < 2) s0[8 * gg + j] = ok ? s0[8 * gg + j] : -INFINITY;
-          else s1[8 * (gg - 2) + j] = ok ? s1[8 * (gg - 2) + j] : -INFINITY;
+          if (gg < 2) c0[8 * gg + j] = ok ? c0[8 * gg + j] : -INFINITY;
+          else c1[8 * (gg - 2) + j] = ok ? c1[8 * (gg - 2) + j] : -INFINITY;
         }
       }
     }
-
-    float mx = fmaxf(s0[0], s0[1]);
+    // One straight-line block: the next tile's scores are computed even when
+    // there is no next tile or this wave skips it, and this tile's
+    // exponentials even when this wave skips it; such results go unused.
+    bf16x8 pb[4];
+    float lj = 0.f;
+    const float nm = -m_run;
+    {
+      // 16 chunks, fenced from each other: chunk m reads the K operand of MFMA
+      // m+4, issues MFMA m of the next tile's scores (sub-tile m%2, d-slice
+      // m/2), and exponentiates scores 2m, 2m+1 of this tile.
+      constexpr int kb = decltype(kbc)::value;
+      const char* sK = kb ? sK1 : sK0;
 #pragma unroll
-    for (int r = 2; r < 16; ++r) mx = fmaxf(mx, s0[r]);
+      for (int r = 0; r < 16; ++r) {
+        n0[r] = 0.f;
+        n1[r] = 0.f;
+      }
+      auto kop = [&](int m) {
+        return *reinterpret_cast<const bf16x8*>(sK + kaddr[m >> 1] + (m & 1) * 32 * C::KROW);
+      };
+      constexpr int NM = 2 * C::QREG;  // MFMAs per tile
+      constexpr int PF = 4;            // operand reads in flight
+      bf16x8 ops[NM];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s1[r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float mnew = fmaxf(m_run, mx * p.c2);
-    const bool need = mnew > m_run + kRescaleLog2;
-    if (__any(need)) {
-      const float alpha = need ? __builtin_amdgcn_exp2f(m_run - mnew) : 1.f;
-      m_run = need ? mnew : m_run;
+      for (int m = 0; m < PF; ++m) ops[m] = kop(m);
+#pragma unroll
+      for (int m = 0; m < NM; ++m) {
+        if (m + PF < NM) ops[m + PF] = kop(m + PF);
+        if (m & 1) n1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ops[m], qreg[m >> 1], n1, 0, 0, 0);
+        else n0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ops[m], qreg[m >> 1], n0, 0, 0, 0);
+#pragma unroll
+        for (int q = 0; q < 32 / NM; q += 2) {
+          const int x = (32 / NM) * m + q;  // score index: sub-tile x/16, register x%16
+          const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(x < 16 ? c0[x] : c1[x - 16], p.c2, nm));
+          const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(x < 16 ? c0[x + 1] : c1[x - 15], p.c2, nm));
+          const bf16x2 pr = __builtin_convertvector((f32x2){e0, e1}, bf16x2);
+          lj += e0 + e1;
+          pb[x >> 3][x & 7] = pr[0];
+          pb[x >> 3][(x & 7) + 1] = pr[1];
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    // Pin the exponentials to this block: without a use here the compiler
+    // sinks them past the skip test below, out of the interleave.
+#pragma unroll
+    for (int kg = 0; kg < 4; ++kg) asm volatile("" : : "v"(__builtin_bit_cast(u32x4, pb[kg])));
+    asm volatile("" : : "v"(lj));
+    if (cls_cur == kSkip) return;
+    // Redo against the tile's own max where a lane's sum is not finite or too
+    // large; both lanes of a row take the same decision.
+    const unsigned long long bal = __ballot(!(lj <= kRedo));
+    const unsigned long long both = bal | (bal >> 32) | (bal << 32);
+    if (both) {
+      const bool mine = (both >> lane) & 1ull;
+      float mx = -INFINITY;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, fmaxf(c0[r], c1[r]));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float mnew = mine ? fmaxf(m_run, mx * p.c2) : m_run;
+      const float alpha = mnew == m_run ? 1.f : __builtin_amdgcn_exp2f(m_run - mnew);
+      m_run = mnew;
       l_run *= alpha;
 #pragma unroll
       for (int t = 0; t < C::DT; ++t)
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[t][r] *= alpha;
+      const float nm2 = m_run == -INFINITY ? 0.f : -m_run;
+      lj = 0.f;
+#pragma unroll
+      for (int kg = 0; kg < 4; ++kg) expg(c0, c1, kg, nm2, pb[kg], lj);
     }
-    const float nm = m_run == -INFINITY ? 0.f : -m_run;
-
-    // P = exp2(c2*s - m).  The row sum adds the fp32 values (the LSE needs
-    // them); P enters the PV product rounded to bf16.  O^T += V^T P^T per
-    // 16-key group.
+    l_run += lj;
+    // O^T += V^T P^T
+    bf16x8 va[C::DT];
+#pragma unroll
+    for (int t = 0; t < C::DT; ++t) va[t] = *reinterpret_cast<const bf16x8*>(sV + vaddr[0] + t * 32 * C::VROW);
 #pragma unroll
     for (int kg = 0; kg < 4; ++kg) {
-      const f32x16& sv = kg < 2 ? s0 : s1;
-      const int base = 8 * (kg & 1);
-      bf16x8 pb;
-#pragma unroll
-      for (int j = 0; j < 8; j += 2) {
-        const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[base + j], p.c2, nm));
-        const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[base + j + 1], p.c2, nm));
-        const bf16x2 pr = __builtin_convertvector((f32x2){e0, e1}, bf16x2);
-        l_run += e0 + e1;
-        pb[j] = pr[0];
-        pb[j + 1] = pr[1];
-      }
 #pragma unroll
       for (int t = 0; t < C::DT; ++t) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(sV + vaddr[kg] + t * 32 * C::VROW);
-        oacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, oacc[t], 0, 0, 0);
+        oacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[t], pb[kg], oacc[t], 0, 0, 0);
+        if (kg < 3) va[t] = *reinterpret_cast<const bf16x8*>(sV + vaddr[kg + 1] + t * 32 * C::VROW);
       }
     }
   };
 
   // ---- walk the ring: list the needed key tiles, then stream them ---------
+  // Iteration j reads K of tile j+1 and V^T of tile j while tile j+2's K and
+  // tile j+1's V^T are copied in; buffers alternate, so the loop is unrolled
+  // by two with static buffer and register roles.
+  f32x16 sa0, sa1, sb0, sb1;
   const int total = p.cp * p.tpr;
   const int csh = 24 + 2 * wave;
+  auto cls_of = [&](int e) { return (int)(((unsigned)e >> csh) & 3); };
   for (int u0 = 0; u0 < total; u0 += kListCap) {
     const int cnt = build_list<C::BN>(p, u0, min(total, u0 + kListCap), tid, wave, lane, sWb, sList, sCnt);
     if (cnt == 0) continue;
-    int e = __builtin_amdgcn_readfirstlane(sList[0]);
-    issue(std::integral_constant<int, 0>{}, e & 0xFFFFFF);
+    auto entry = [&](int j) { return j < cnt ? __builtin_amdgcn_readfirstlane(sList[j]) : 0; };
+    int e_cur = entry(0), e_nxt = entry(1);
+    issue_k(std::integral_constant<int, 0>{}, e_cur);
+    issue_v(std::integral_constant<int, 0>{}, e_cur);
+    if (cnt > 1) issue_k(std::integral_constant<int, 1>{}, e_nxt);
     wait_vmem();
     __syncthreads();
+    if (cls_of(e_cur) != kSkip) scores(std::integral_constant<int, 0>{}, sa0, sa1);
+    __syncthreads();
     for (int j = 0;;) {
-      // tile j sits in buffer 0
-      int e1 = 0;
-      if (j + 1 < cnt) {
-        e1 = __builtin_amdgcn_readfirstlane(sList[j + 1]);
-        issue(std::integral_constant<int, 1>{}, e1 & 0xFFFFFF);
+      // K of tile j+1 in buffer 1, V^T of tile j in buffer 0; scores of tile j in sa.
+      {
+        const int e2 = entry(j + 2);
+        if (j + 2 < cnt) issue_k(std::integral_constant<int, 0>{}, e2);
+        if (j + 1 < cnt) issue_v(std::integral_constant<int, 1>{}, e_nxt);
+        stage(std::integral_constant<int, 1>{}, std::integral_constant<int, 0>{}, sa0, sa1, sb0, sb1, cls_of(e_cur));
+        wait_vmem();
+        __syncthreads();
+        e_cur = e_nxt;
+        e_nxt = e2;
       }
-      compute(std::integral_constant<int, 0>{}, ((unsigned)e >> csh) & 3);
-      wait_vmem();
-      __syncthreads();
       if (++j >= cnt) break;
-      // tile j sits in buffer 1
-      if (j + 1 < cnt) {
-        e = __builtin_amdgcn_readfirstlane(sList[j + 1]);
-        issue(std::integral_constant<int, 0>{}, e & 0xFFFFFF);
+      // K of tile j+1 in buffer 0, V^T of tile j in buffer 1; scores of tile j in sb.
+      {
+        const int e2 = entry(j + 2);
+        if (j + 2 < cnt) issue_k(std::integral_constant<int, 1>{}, e2);
+        if (j + 1 < cnt) issue_v(std::integral_constant<int, 0>{}, e_nxt);
+        stage(std::integral_constant<int, 0>{}, std::integral_constant<int, 1>{}, sb0, sb1, sa0, sa1, cls_of(e_cur));
+        wait_vmem();
+        __syncthreads();
+        e_cur = e_nxt;
+        e_nxt = e2;
       }
-      compute(std::integral_constant<int, 1>{}, ((unsigned)e1 >> csh) & 3);
-      wait_vmem();
-      __syncthreads();
       if (++j >= cnt) break;
     }
   }
@@ -612,17 +700,18 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_f32_kernel(KParams p) {
 
   const int total = p.cp * p.tpr;
   const int csh = 24 + 2 * wave;
+  auto entry_tile = [&](int e) { return (e & 0xFF) * p.tpr + ((e >> 8) & 0xFFFF); };
   for (int u0 = 0; u0 < total; u0 += kListCap) {
     const int cnt = build_list<C::BN>(p, u0, min(total, u0 + kListCap), tid, wave, lane, sWb, sList, sCnt);
     if (cnt == 0) continue;
-    stage_load(sList[0] & 0xFFFFFF);
+    stage_load(entry_tile(sList[0]));
     stage_store(0);
     __syncthreads();
     for (int j = 0; j < cnt; ++j) {
       const int cur = j & 1;
       const bool has_next = j + 1 < cnt;
       const int e = __builtin_amdgcn_readfirstlane(sList[j]);
-      if (has_next) stage_load(sList[j + 1] & 0xFFFFFF);
+      if (has_next) stage_load(entry_tile(sList[j + 1]));
       compute(cur, ((unsigned)e >> csh) & 3);
       if (has_next) stage_store(cur ^ 1);
       __syncthreads();
