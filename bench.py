@@ -24,9 +24,42 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "causal ring-attention TFLOP/s per virtual rank (fwd, fwd+bwd); % bf16 MFMA peak"
-PEAK_BF16_TFLOPS = 2516.6   # 256 CU x 4096 flop/clk x 2.4 GHz, dense bf16 MFMA
+PEAK_BF16_TFLOPS = 2516.6   # 256 CU x 4096 flop/clk x 2.4 GHz, dense bf16 MFMA (published)
 PEAK_F32_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
+PROFILES = os.path.join(ROOT, "profiles")
+KERNEL_SOURCES = {"fwd": ["context_causal_attention_amd/csrc/attn_fwd.hip"]}
+
+
+def source_hash(paths):
+    """sha256 over the kernel sources, to tell whether stored counters still
+    describe the kernel being timed."""
+    import hashlib
+    h = hashlib.sha256()
+    for rel in paths:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(kind, workload):
+    """HBM bytes per launch from the committed counter summary
+    profiles/<kind>_traffic_<workload>.txt (lines 'key: value'), or None when
+    the summary is missing or was taken on a different kernel source."""
+    path = os.path.join(PROFILES, f"{kind}_traffic_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if ":" in line:
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("source_sha256_16") != source_hash(KERNEL_SOURCES[kind]):
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def parse():
@@ -158,8 +191,9 @@ def main():
         "pct_peak": round(100 * value / peak, 2),
         "per_rank_ms": {str(r): round(x, 4) for r, x in per_rank_ms.items()},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak, "unit": "TFLOP/s",
-                     "frac": round(achieved / peak, 4), "traffic": None,
-                     "kernel": "cp_attn_ring_fwd (prep + fwd_kernel), HIP events on the launch stream"},
+                     "frac": round(achieved / peak, 4), "traffic": stored_traffic("fwd", w.name),
+                     "kernel": "cp_attn_ring_fwd launch (V-transpose prep + fwd_bf16_kernel), HIP events "
+                               "on the launch stream; traffic = calibrated FETCH_SIZE + WRITE_SIZE per launch"},
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
