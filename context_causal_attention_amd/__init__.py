@@ -27,6 +27,7 @@ __all__ = [
     "lib", "cp_version", "cp_last_error", "cp_shard_zigzag", "cp_unshard_zigzag",
     "cp_varlen_index", "cp_ring_source", "cp_pairs", "cp_attn_fwd_workspace",
     "cp_attn_partial_fwd", "cp_attn_merge", "cp_attn_ring_fwd", "RingFwdPlan",
+    "cp_attn_bwd_workspace", "cp_attn_bwd_delta", "cp_attn_partial_bwd", "cp_attn_ring_bwd", "RingBwdPlan",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -80,8 +81,15 @@ def lib() -> ctypes.CDLL:
         L.cp_attn_merge.argtypes = [c_int64, c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]
         L.cp_attn_ring_fwd.argtypes = [POINTER(CpShape), c_int32, c_int32] + [c_void_p] * 6 + \
             [c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]
+        L.cp_attn_bwd_workspace.argtypes = [POINTER(CpShape), c_int32]
+        L.cp_attn_bwd_workspace.restype = c_size_t
+        L.cp_attn_bwd_delta.argtypes = [POINTER(CpShape), c_void_p, c_void_p, c_void_p, c_void_p]
+        L.cp_attn_partial_bwd.argtypes = [POINTER(CpShape)] + [c_void_p] * 12 + [c_void_p, c_size_t, c_void_p]
+        L.cp_attn_ring_bwd.argtypes = [POINTER(CpShape), c_int32, c_int32] + [c_void_p] * 12 + \
+            [c_void_p, c_size_t, c_void_p]
         for name in ("cp_shard_zigzag", "cp_unshard_zigzag", "cp_varlen_index", "cp_ring_source",
-                     "cp_attn_partial_fwd", "cp_attn_merge", "cp_attn_ring_fwd"):
+                     "cp_attn_partial_fwd", "cp_attn_merge", "cp_attn_ring_fwd", "cp_attn_bwd_delta",
+                     "cp_attn_partial_bwd", "cp_attn_ring_bwd"):
             getattr(L, name).restype = c_int32
         _lib_handle = L
     return _lib_handle
@@ -277,4 +285,114 @@ def cp_attn_ring_fwd(q_loc, k_all, v_all, cp, rank, q_pos, q_lo, k_pos_all, scal
                      out=None, lse=None, workspace=None):
     """A virtual rank's whole ring with every K/V shard resident: final (O, LSE)."""
     return RingFwdPlan(q_loc, k_all, v_all, cp, rank, q_pos, q_lo, k_pos_all, scale, out_dtype, out, lse,
+                       workspace).run()
+
+
+# ------------------------------------------------------------------ backward
+def _bwd_shape(q, k, v, dout, scale) -> CpShape:
+    if dout.dtype != q.dtype or dout.shape != q.shape or dout.stride() != q.stride():
+        raise ValueError("dout must match q in dtype, shape and strides")
+    return _shape(q, k, v, (ctypes.c_int64 * 3)(0, 0, 0), scale, torch.float32)
+
+
+def _grad_buf(t, shape, device, what):
+    if t is None:
+        return torch.zeros(*shape, dtype=torch.float32, device=device)
+    if t.dtype != torch.float32 or not t.is_contiguous() or tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{what} must be contiguous float32 {tuple(shape)}")
+    return t
+
+
+def _rows_f32(t, shape, what):
+    if t.dtype != torch.float32 or not t.is_contiguous() or tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{what} must be contiguous float32 {tuple(shape)}")
+    return t
+
+
+def cp_attn_bwd_workspace(q, k, v, cp: int = 1) -> int:
+    s = _shape(q, k, v, (ctypes.c_int64 * 3)(0, 0, 0), None, torch.float32)
+    n = int(lib().cp_attn_bwd_workspace(ctypes.byref(s), cp))
+    if n == 0:
+        raise ValueError(cp_last_error() or "invalid shape")
+    return n
+
+
+def cp_attn_bwd_delta(dout, o, delta=None):
+    """delta = rowsum(dO * O) as contiguous float32 [B, Hq, rows]."""
+    if o.dtype not in _DT or tuple(o.shape) != tuple(dout.shape):
+        raise ValueError("o must be float32 or bfloat16 with dout's shape")
+    B, Hq, Sq, D = dout.shape
+    delta = torch.empty(B, Hq, Sq, dtype=torch.float32, device=dout.device) if delta is None else delta
+    _rows_f32(delta, (B, Hq, Sq), "delta")
+    s = CpShape()
+    s.b, s.hq, s.hkv, s.d = B, Hq, Hq, D
+    s.sq, s.sk, s.scale = Sq, 0, 1.0
+    s.in_dtype = _DT.get(dout.dtype, -1)
+    s.out_dtype = _DT[o.dtype]
+    s.q_str, s.o_str = _strides(dout), _strides(o)
+    s.k_str = s.v_str = (ctypes.c_int64 * 3)(0, 0, 0)
+    _check(lib().cp_attn_bwd_delta(ctypes.byref(s), dout.data_ptr(), o.data_ptr(), delta.data_ptr(),
+                                   _stream(dout.device)))
+    return delta
+
+
+def cp_attn_partial_bwd(q, k, v, dout, lse, delta, q_pos, q_lo, k_pos, dq=None, dk=None, dv=None, scale=None,
+                        workspace=None):
+    """Backward of one ring step; adds into (and returns) fp32 dq, dk, dv."""
+    dev = q.device
+    B, Hq, Sq, D = q.shape
+    s = _bwd_shape(q, k, v, dout, scale)
+    _rows_f32(lse, (B, Hq, Sq), "lse")
+    _rows_f32(delta, (B, Hq, Sq), "delta")
+    dq = _grad_buf(dq, q.shape, dev, "dq")
+    dk = _grad_buf(dk, k.shape, dev, "dk")
+    dv = _grad_buf(dv, v.shape, dev, "dv")
+    qp, kp = _dev_i32(q_pos, dev), _dev_i32(k_pos, dev)
+    ql = None if q_lo is None else _dev_i32(q_lo, dev)
+    ws = _workspace(int(lib().cp_attn_bwd_workspace(ctypes.byref(s), 1)) or 256, dev, workspace)
+    _check(lib().cp_attn_partial_bwd(ctypes.byref(s), q.data_ptr(), k.data_ptr(), v.data_ptr(), dout.data_ptr(),
+                                     lse.data_ptr(), delta.data_ptr(), qp.data_ptr(),
+                                     None if ql is None else ql.data_ptr(), kp.data_ptr(), dq.data_ptr(),
+                                     dk.data_ptr(), dv.data_ptr(), ws.data_ptr(), ws.numel(), _stream(dev)))
+    return dq, dk, dv
+
+
+class RingBwdPlan:
+    """A validated cp_attn_ring_bwd call with its workspace and fp32 gradient
+    buffers, replayable with no Python-side allocation.  Each run() adds into
+    the buffers; zero them (``zero_()``) to start over."""
+
+    def __init__(self, q_loc, k_all, v_all, dout, lse, delta, cp, rank, q_pos, q_lo, k_pos_all, scale=None,
+                 dq=None, dk=None, dv=None, workspace=None):
+        dev = q_loc.device
+        B, Hq, Sq, D = q_loc.shape
+        self.shape = _bwd_shape(q_loc, k_all, v_all, dout, scale)
+        _rows_f32(lse, (B, Hq, Sq), "lse")
+        _rows_f32(delta, (B, Hq, Sq), "delta")
+        self.dq = _grad_buf(dq, q_loc.shape, dev, "dq")
+        self.dk = _grad_buf(dk, k_all.shape, dev, "dk")
+        self.dv = _grad_buf(dv, v_all.shape, dev, "dv")
+        self.qp = _dev_i32(q_pos, dev)
+        self.ql = None if q_lo is None else _dev_i32(q_lo, dev)
+        self.kp = _dev_i32(k_pos_all, dev)
+        nws = int(lib().cp_attn_bwd_workspace(ctypes.byref(self.shape), cp))
+        self.ws = _workspace(nws or 256, dev, workspace)
+        self.keep = (q_loc, k_all, v_all, dout, lse, delta)
+        self.args = (ctypes.byref(self.shape), cp, rank, q_loc.data_ptr(), k_all.data_ptr(), v_all.data_ptr(),
+                     dout.data_ptr(), lse.data_ptr(), delta.data_ptr(), self.qp.data_ptr(),
+                     None if self.ql is None else self.ql.data_ptr(), self.kp.data_ptr(), self.dq.data_ptr(),
+                     self.dk.data_ptr(), self.dv.data_ptr(), self.ws.data_ptr(), self.ws.numel())
+        self.device = dev
+
+    def run(self, stream=None):
+        st = _stream(self.device) if stream is None else stream
+        _check(lib().cp_attn_ring_bwd(*self.args, st))
+        return self.dq, self.dk, self.dv
+
+
+def cp_attn_ring_bwd(q_loc, k_all, v_all, dout, lse, delta, cp, rank, q_pos, q_lo, k_pos_all, scale=None,
+                     dq=None, dk=None, dv=None, workspace=None):
+    """A virtual rank's whole ring backward: adds into (and returns) fp32
+    dq [B,Hq,rows,D] and dk, dv [B,Hkv,S,D] (rank-major rows like k_all)."""
+    return RingBwdPlan(q_loc, k_all, v_all, dout, lse, delta, cp, rank, q_pos, q_lo, k_pos_all, scale, dq, dk, dv,
                        workspace).run()

@@ -118,13 +118,42 @@ FwdWorkspace fwd_workspace_layout(int32_t b, int32_t hkv, int32_t d, int64_t sk,
   return w;
 }
 
+BwdWorkspace bwd_workspace_layout(int32_t b, int32_t hq, int32_t hkv, int32_t d, int64_t sq, int64_t sk,
+                                  int32_t cp) {
+  BwdWorkspace w{};
+  const int64_t per = cp > 0 ? sk / cp : 0;
+  const int64_t tpr = (per + kBwdTile - 1) / kBwdTile;
+  const int64_t nkt = tpr * cp;
+  w.kt_row = nkt * kBwdTile;
+  w.sq_pad = (sq + kBwdTile - 1) / kBwdTile * kBwdTile;
+  const int64_t nqt = w.sq_pad / kBwdTile;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off += align_up(bytes, 256);
+    return at;
+  };
+  w.kbounds_off = take((size_t)nkt * 16);
+  w.kpos_off = take((size_t)w.kt_row * 4);
+  w.kt_off = take((size_t)b * hkv * d * (size_t)w.kt_row * 2);
+  w.qbounds_off = take((size_t)nqt * 16);
+  w.qpos_off = take((size_t)w.sq_pad * 4);
+  w.qlo_off = take((size_t)w.sq_pad * 4);
+  w.lse2_off = take((size_t)b * hq * (size_t)w.sq_pad * 4);
+  w.dlt_off = take((size_t)b * hq * (size_t)w.sq_pad * 4);
+  w.qt_off = take((size_t)b * hq * d * (size_t)w.sq_pad * 2);
+  w.dot_off = take((size_t)b * hq * d * (size_t)w.sq_pad * 2);
+  w.total = off < 256 ? 256 : off;
+  return w;
+}
+
 }  // namespace cpattn
 
 using namespace cpattn;
 
 extern "C" const char* cp_last_error(void) { return g_last_error.c_str(); }
 
-extern "C" int cp_version(void) { return 100; }
+extern "C" int cp_version(void) { return 200; }
 
 extern "C" size_t cp_attn_fwd_workspace(const cp_shape* s, int32_t cp) {
   if (check_shape(s) != CP_OK || cp < 1) return 0;
@@ -212,4 +241,119 @@ extern "C" int cp_attn_merge(int64_t rows, int32_t d, float* o_acc, float* lse_a
   if (!lse_acc || !lse_p) return fail(CP_EINVAL, "lse pointer is null");
   if (rows == 0) return CP_OK;
   return hip_status(launch_merge(rows, d, o_acc, lse_acc, o_p, lse_p, stream), "merge launch");
+}
+
+extern "C" size_t cp_attn_bwd_workspace(const cp_shape* s, int32_t cp) {
+  if (check_shape(s) != CP_OK || cp < 1) return 0;
+  return bwd_workspace_layout(s->b, s->hq, s->hkv, s->d, s->sq, s->sk, cp).total;
+}
+
+extern "C" int cp_attn_bwd_delta(const cp_shape* s, const void* dout, const void* o, float* delta,
+                                 hipStream_t stream) {
+  clear_error();
+  if (int rc = check_shape(s)) return rc;
+  if (s->in_dtype != CP_BF16) return fail(CP_EDTYPE, "the backward takes bf16 inputs (in_dtype must be CP_BF16)");
+  if (s->sq == 0) return CP_OK;
+  if (int rc = check_ptrs16({{dout, "dout"}, {o, "o"}})) return rc;
+  if (!delta) return fail(CP_EINVAL, "delta is null");
+  if (int rc = check_strides(s->o_str, s->out_dtype, "o")) return rc;
+  if (s->o_str[2] < s->d || s->q_str[2] < s->d) return fail(CP_EINVAL, "dout/o row strides must be at least d");
+  BwdArgs a{};
+  for (int i = 0; i < 3; ++i) {
+    a.q_str[i] = s->q_str[i];
+    a.o_str[i] = s->o_str[i];
+  }
+  a.dout = dout;
+  a.o = o;
+  a.delta_out = delta;
+  a.b = s->b;
+  a.hq = s->hq;
+  a.d = s->d;
+  a.sq = (int32_t)s->sq;
+  a.out_dtype = s->out_dtype;
+  return hip_status(launch_delta(a, stream), "delta launch");
+}
+
+namespace {
+
+int run_bwd(const cp_shape* s, int32_t cp, int32_t rank, const void* q, const void* k, const void* v,
+            const void* dout, const float* lse, const float* delta, const int32_t* q_pos, const int32_t* q_lo,
+            const int32_t* k_pos, float* dq, float* dk, float* dv, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (s->in_dtype != CP_BF16) return fail(CP_EDTYPE, "the backward takes bf16 inputs (in_dtype must be CP_BF16)");
+  if (cp > 255) return fail(CP_EINVAL, "cp must be <= 255 (got %d)", cp);
+  if (s->sq == 0 || s->sk == 0) return CP_OK;  // no allowed pair: every gradient contribution is zero
+  if (int rc = check_ptrs16({{q, "q"}, {k, "k"}, {v, "v"}, {dout, "dout"}, {dq, "dq"}, {dk, "dk"}, {dv, "dv"}}))
+    return rc;
+  if (!lse || !delta) return fail(CP_EINVAL, "lse or delta is null");
+  if (!q_pos || !k_pos) return fail(CP_EINVAL, "q_pos or k_pos is null");
+  if (s->q_str[2] < s->d || s->k_str[2] < s->d || s->v_str[2] < s->d)
+    return fail(CP_EINVAL, "q/k/v row strides must be at least d");
+  const int64_t per = s->sk / cp;
+  if ((per + kBwdTile - 1) / kBwdTile > 65535)
+    return fail(CP_EINVAL, "a shard of %lld key rows has more than 65535 key tiles", (long long)per);
+  const BwdWorkspace w = bwd_workspace_layout(s->b, s->hq, s->hkv, s->d, s->sq, s->sk, cp);
+  // The kernels address the transposed copies and the padded per-row arrays
+  // with 32-bit buffer offsets.
+  if ((double)s->d * (double)w.kt_row * 2.0 >= 2147483648.0 ||
+      (double)s->b * s->hq * (double)w.sq_pad * 4.0 >= 2147483648.0)
+    return fail(CP_EINVAL, "sequence too long for 32-bit buffer offsets (sq=%lld, sk=%lld)", (long long)s->sq,
+                (long long)s->sk);
+  if (!ws) return fail(CP_EWORKSPACE, "workspace is null (%zu bytes needed)", w.total);
+  if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0) return fail(CP_EWORKSPACE, "workspace is not 256-byte aligned");
+  if (ws_bytes < w.total) return fail(CP_EWORKSPACE, "workspace too small: %zu < %zu bytes", ws_bytes, w.total);
+  BwdArgs a{};
+  for (int i = 0; i < 3; ++i) {
+    a.q_str[i] = s->q_str[i];
+    a.k_str[i] = s->k_str[i];
+    a.v_str[i] = s->v_str[i];
+  }
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.dout = dout;
+  a.q_pos = q_pos;
+  a.q_lo = q_lo;
+  a.k_pos = k_pos;
+  a.lse = lse;
+  a.delta = delta;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.b = s->b;
+  a.hq = s->hq;
+  a.hkv = s->hkv;
+  a.d = s->d;
+  a.sq = (int32_t)s->sq;
+  a.sk = (int32_t)s->sk;
+  a.cp = cp;
+  a.rank = rank;
+  a.rows_per_rank = (int32_t)per;
+  a.scale = s->scale;
+  a.ws = ws;
+  return hip_status(launch_bwd(a, stream), "backward launch");
+}
+
+}  // namespace
+
+extern "C" int cp_attn_partial_bwd(const cp_shape* s, const void* q, const void* k, const void* v, const void* dout,
+                                   const float* lse, const float* delta, const int32_t* q_pos, const int32_t* q_lo,
+                                   const int32_t* k_pos, float* dq, float* dk, float* dv, void* ws, size_t ws_bytes,
+                                   hipStream_t stream) {
+  clear_error();
+  if (int rc = check_shape(s)) return rc;
+  return run_bwd(s, 1, 0, q, k, v, dout, lse, delta, q_pos, q_lo, k_pos, dq, dk, dv, ws, ws_bytes, stream);
+}
+
+extern "C" int cp_attn_ring_bwd(const cp_shape* s, int32_t cp, int32_t rank, const void* q_loc, const void* k_all,
+                                const void* v_all, const void* dout, const float* lse, const float* delta,
+                                const int32_t* q_pos, const int32_t* q_lo, const int32_t* k_pos_all, float* dq,
+                                float* dk_all, float* dv_all, void* ws, size_t ws_bytes, hipStream_t stream) {
+  clear_error();
+  if (int rc = check_shape(s)) return rc;
+  if (cp < 1) return fail(CP_EINVAL, "cp must be >= 1 (got %d)", cp);
+  if (rank < 0 || rank >= cp) return fail(CP_EINVAL, "rank %d outside [0, %d)", rank, cp);
+  if (s->sk % (2 * (int64_t)cp) != 0)
+    return fail(CP_ESHAPE, "key rows %lld are not a multiple of 2*cp = %lld", (long long)s->sk, 2 * (long long)cp);
+  return run_bwd(s, cp, rank, q_loc, k_all, v_all, dout, lse, delta, q_pos, q_lo, k_pos_all, dq, dk_all, dv_all, ws,
+                 ws_bytes, stream);
 }

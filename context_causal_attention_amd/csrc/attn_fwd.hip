@@ -41,30 +41,20 @@
 #include <climits>
 #include <type_traits>
 
+#include "device_common.h"
 #include "internal.h"
 
 namespace cpattn {
 namespace fwdk {
 
-typedef __bf16 bf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
-typedef __bf16 bf16x2 __attribute__((__vector_size__(2 * sizeof(__bf16))));
-typedef float f32x16 __attribute__((__vector_size__(16 * sizeof(float))));
-typedef float f32x4 __attribute__((__vector_size__(4 * sizeof(float))));
-typedef float f32x2 __attribute__((__vector_size__(2 * sizeof(float))));
-typedef unsigned int u32x4 __attribute__((__vector_size__(4 * sizeof(unsigned int))));
-typedef unsigned int u32x2 __attribute__((__vector_size__(2 * sizeof(unsigned int))));
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
+using namespace dev;
 
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
 constexpr int kRowsPerWave = 32;
 constexpr int kBlockM = kWaves * kRowsPerWave;
-constexpr int kListCap = 2048;          // active key tiles listed per pass
+constexpr int kListCap = 1024;          // active key tiles listed per pass
 constexpr float kRescaleLog2 = 8.0f;    // keep a stale running max while scores stay within 2^8 of it
-constexpr float kLn2 = 0.69314718055994530942f;
-constexpr int kInvalidKey = INT_MAX;    // position given to padding keys: never allowed
-constexpr int kBufferFlags = 0x00020000;  // buffer descriptor word 3 for gfx9: 32-bit data format
-constexpr int kSkip = 0, kPartial = 1, kFull = 2;
 
 struct KParams {
   const char* q;
@@ -85,31 +75,6 @@ struct KParams {
   float c2;                 // softmax scale * log2(e)
 };
 
-// 16-byte-chunk XOR swizzle of an LDS row of C chunks, chosen so that 16 lanes
-// reading the same logical chunk of 16 consecutive rows hit 16 distinct
-// positions of a 256-byte bank line.
-template <int C>
-__device__ __forceinline__ int swz(int row, int chunk) {
-  if constexpr (C >= 16) return chunk ^ (row & 15);
-  else return chunk ^ ((row >> 1) & 7);
-}
-
-// Key order of the S^T accumulator rows: bits 2 and 3 of the row index swapped.
-__device__ __forceinline__ int key_perm(int m) { return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1); }
-
-__device__ __forceinline__ int wave_min(int x) {
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) x = min(x, __shfl_xor(x, o));
-  return x;
-}
-__device__ __forceinline__ int wave_max(int x) {
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) x = max(x, __shfl_xor(x, o));
-  return x;
-}
-
-__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
-
 // Work item of this workgroup.  Workgroups are dealt round-robin over the 8
 // XCDs; each XCD gets a contiguous range of logical ids so that the query heads
 // sharing one K/V head (and the same key tiles) run on the same L2.  Within a
@@ -119,10 +84,7 @@ struct Item {
   int b, h, kvh, qt;
 };
 __device__ __forceinline__ Item map_block(const KParams& p) {
-  const int nblk = gridDim.x;
-  const int bid = blockIdx.x;
-  const int per_xcd = nblk / 8;
-  const int logical = bid < per_xcd * 8 ? (bid % 8) * per_xcd + bid / 8 : bid;
+  const int logical = xcd_logical_block();
   const int g = p.Hq / p.Hkv;
   const int hg = logical % g;
   int rest = logical / g;
@@ -148,51 +110,6 @@ __device__ __forceinline__ void wave_bounds(int wave, int lane, bool valid, int 
     sWb[wave][2] = c;
     sWb[wave][3] = d;
   }
-}
-
-// Lists, in ring order, the key tiles of schedule slots [u0, u1) that some wave
-// of this workgroup needs.  Entry = src | i << 8 | class(wave w) << (24 + 2w)
-// for key tile i of rank src's shard.
-template <int BN>
-__device__ __forceinline__ int build_list(const KParams& p, int u0, int u1, int tid, int wave, int lane,
-                                          const int (*sWb)[4], int* sList, int* sCnt) {
-  int cnt = 0;
-  for (int base = u0; base < u1; base += kThreads) {
-    const int u = base + tid;
-    bool act = false;
-    unsigned entry = 0;
-    if (u < u1) {
-      const int t = u / p.tpr;
-      const int i = u - t * p.tpr;
-      int src = p.rank - t;
-      if (src < 0) src += p.cp;
-      const int tile = src * p.tpr + i;
-      const int4 bd = p.bounds[tile];
-      entry = (unsigned)src | ((unsigned)i << 8);
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
-        int cls = kSkip;
-        if (bd.z > 0 && bd.x <= sWb[w][1] && bd.y >= sWb[w][2])
-          cls = (bd.z == BN && bd.y <= sWb[w][0] && bd.x >= sWb[w][3]) ? kFull : kPartial;
-        entry |= (unsigned)cls << (24 + 2 * w);
-        act |= cls != kSkip;
-      }
-    }
-    const unsigned long long bal = __ballot(act);
-    const int before = __popcll(bal & ((1ull << lane) - 1ull));
-    if (lane == 0) sCnt[wave] = __popcll(bal);
-    __syncthreads();
-    int off = cnt, tot = 0;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      off += w < wave ? sCnt[w] : 0;
-      tot += sCnt[w];
-    }
-    if (act) sList[off + before] = (int)entry;
-    cnt += tot;
-    __syncthreads();
-  }
-  return cnt;
 }
 
 template <int DT>
@@ -250,7 +167,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(KParams p) {
   __shared__ __attribute__((aligned(1024))) char sV1[C::VBYTES];
   __shared__ __attribute__((aligned(16))) int sP0[C::BN];
   __shared__ __attribute__((aligned(16))) int sP1[C::BN];
-  __shared__ int sList[kListCap];
+  __shared__ int2 sList[kListCap];
   __shared__ int sCnt[kWaves];
   __shared__ int sWb[kWaves][4];
 
@@ -506,16 +423,25 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(KParams p) {
   // by two with static buffer and register roles.
   f32x16 sa0, sa1, sb0, sb1;
   const int total = p.cp * p.tpr;
-  const int csh = 24 + 2 * wave;
-  auto cls_of = [&](int e) { return (int)(((unsigned)e >> csh) & 3); };
+  const int csh = 2 * wave;
+  auto cls_of = [&](int2 e) { return (int)(((unsigned)e.y >> csh) & 3); };
   for (int u0 = 0; u0 < total; u0 += kListCap) {
-    const int cnt = build_list<C::BN>(p, u0, min(total, u0 + kListCap), tid, wave, lane, sWb, sList, sCnt);
+    const int cnt = build_key_list<C::BN, kWaves>(p.bounds, p.tpr, p.rank, p.cp, u0, min(total, u0 + kListCap), tid,
+                                                  wave, lane, sWb, sList, sCnt);
     if (cnt == 0) continue;
-    auto entry = [&](int j) { return j < cnt ? __builtin_amdgcn_readfirstlane(sList[j]) : 0; };
-    int e_cur = entry(0), e_nxt = entry(1);
-    issue_k(std::integral_constant<int, 0>{}, e_cur);
-    issue_v(std::integral_constant<int, 0>{}, e_cur);
-    if (cnt > 1) issue_k(std::integral_constant<int, 1>{}, e_nxt);
+    // Entry of list slot j (x: tile, y: classes), read as scalars.
+    auto entry = [&](int j) {
+      int2 e = {0, 0};
+      if (j < cnt) {
+        e.x = __builtin_amdgcn_readfirstlane(sList[j].x);
+        e.y = __builtin_amdgcn_readfirstlane(sList[j].y);
+      }
+      return e;
+    };
+    int2 e_cur = entry(0), e_nxt = entry(1);
+    issue_k(std::integral_constant<int, 0>{}, e_cur.x);
+    issue_v(std::integral_constant<int, 0>{}, e_cur.x);
+    if (cnt > 1) issue_k(std::integral_constant<int, 1>{}, e_nxt.x);
     wait_vmem();
     __syncthreads();
     if (cls_of(e_cur) != kSkip) scores(std::integral_constant<int, 0>{}, sa0, sa1);
@@ -523,9 +449,9 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(KParams p) {
     for (int j = 0;;) {
       // K of tile j+1 in buffer 1, V^T of tile j in buffer 0; scores of tile j in sa.
       {
-        const int e2 = entry(j + 2);
-        if (j + 2 < cnt) issue_k(std::integral_constant<int, 0>{}, e2);
-        if (j + 1 < cnt) issue_v(std::integral_constant<int, 1>{}, e_nxt);
+        const int2 e2 = entry(j + 2);
+        if (j + 2 < cnt) issue_k(std::integral_constant<int, 0>{}, e2.x);
+        if (j + 1 < cnt) issue_v(std::integral_constant<int, 1>{}, e_nxt.x);
         stage(std::integral_constant<int, 1>{}, std::integral_constant<int, 0>{}, sa0, sa1, sb0, sb1, cls_of(e_cur));
         wait_vmem();
         __syncthreads();
@@ -535,9 +461,9 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(KParams p) {
       if (++j >= cnt) break;
       // K of tile j+1 in buffer 0, V^T of tile j in buffer 1; scores of tile j in sb.
       {
-        const int e2 = entry(j + 2);
-        if (j + 2 < cnt) issue_k(std::integral_constant<int, 1>{}, e2);
-        if (j + 1 < cnt) issue_v(std::integral_constant<int, 0>{}, e_nxt);
+        const int2 e2 = entry(j + 2);
+        if (j + 2 < cnt) issue_k(std::integral_constant<int, 1>{}, e2.x);
+        if (j + 1 < cnt) issue_v(std::integral_constant<int, 0>{}, e_nxt.x);
         stage(std::integral_constant<int, 0>{}, std::integral_constant<int, 1>{}, sb0, sb1, sa0, sa1, cls_of(e_cur));
         wait_vmem();
         __syncthreads();
@@ -573,7 +499,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_f32_kernel(KParams p) {
   __shared__ __attribute__((aligned(16))) u32x4 sK[2][C::CHUNKS];
   __shared__ __attribute__((aligned(16))) u32x4 sV[2][C::CHUNKS];
   __shared__ __attribute__((aligned(16))) int sKpos[2][C::BN];
-  __shared__ int sList[kListCap];
+  __shared__ int2 sList[kListCap];
   __shared__ int sCnt[kWaves];
   __shared__ int sWb[kWaves][4];
 
@@ -699,10 +625,11 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_f32_kernel(KParams p) {
   };
 
   const int total = p.cp * p.tpr;
-  const int csh = 24 + 2 * wave;
-  auto entry_tile = [&](int e) { return (e & 0xFF) * p.tpr + ((e >> 8) & 0xFFFF); };
+  const int csh = 2 * wave;
+  auto entry_tile = [&](int2 e) { return (e.x & 0xFF) * p.tpr + ((e.x >> 8) & 0xFFFF); };
   for (int u0 = 0; u0 < total; u0 += kListCap) {
-    const int cnt = build_list<C::BN>(p, u0, min(total, u0 + kListCap), tid, wave, lane, sWb, sList, sCnt);
+    const int cnt = build_key_list<C::BN, kWaves>(p.bounds, p.tpr, p.rank, p.cp, u0, min(total, u0 + kListCap), tid,
+                                                  wave, lane, sWb, sList, sCnt);
     if (cnt == 0) continue;
     stage_load(entry_tile(sList[0]));
     stage_store(0);
@@ -710,7 +637,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_f32_kernel(KParams p) {
     for (int j = 0; j < cnt; ++j) {
       const int cur = j & 1;
       const bool has_next = j + 1 < cnt;
-      const int e = __builtin_amdgcn_readfirstlane(sList[j]);
+      const int e = __builtin_amdgcn_readfirstlane(sList[j].y);
       if (has_next) stage_load(entry_tile(sList[j + 1]));
       compute(cur, ((unsigned)e >> csh) & 3);
       if (has_next) stage_store(cur ^ 1);

@@ -1,0 +1,116 @@
+// Device-side helpers shared by the forward and backward attention kernels
+// (gfx950): vector types, LDS swizzles, the key-order permutation of the MFMA
+// accumulator rows, wave reductions, the XCD-aware block remap and the
+// ring-ordered key-tile list.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <climits>
+
+namespace cpattn {
+namespace dev {
+
+typedef __bf16 bf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
+typedef __bf16 bf16x2 __attribute__((__vector_size__(2 * sizeof(__bf16))));
+typedef float f32x16 __attribute__((__vector_size__(16 * sizeof(float))));
+typedef float f32x4 __attribute__((__vector_size__(4 * sizeof(float))));
+typedef float f32x2 __attribute__((__vector_size__(2 * sizeof(float))));
+typedef unsigned int u32x4 __attribute__((__vector_size__(4 * sizeof(unsigned int))));
+typedef unsigned int u32x2 __attribute__((__vector_size__(2 * sizeof(unsigned int))));
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+constexpr int kInvalidKey = INT_MAX;      // position given to padding keys: never allowed
+constexpr int kBufferFlags = 0x00020000;  // buffer descriptor word 3 for gfx9: 32-bit data format
+constexpr int kSkip = 0, kPartial = 1, kFull = 2;
+constexpr float kLog2e = 1.44269504088896340736f;
+constexpr float kLn2 = 0.69314718055994530942f;
+
+// 16-byte-chunk XOR swizzle of an LDS row of C chunks, chosen so that 16 lanes
+// reading the same logical chunk of 16 consecutive rows hit 16 distinct
+// positions of a 256-byte bank line.
+template <int C>
+__device__ __forceinline__ int swz(int row, int chunk) {
+  if constexpr (C >= 16) return chunk ^ (row & 15);
+  else return chunk ^ ((row >> 1) & 7);
+}
+
+// Row order of a 32x32 MFMA operand that makes each lane's 8 consecutive
+// accumulator registers cover 8 consecutive rows: bits 2 and 3 of the row
+// index swapped.  With the 32x32 accumulator layout (register r of lane half h
+// holds row 8*(r/4) + 4*h + r%4), register r then holds row 16*(r/8) + 8*h + r%8.
+__device__ __forceinline__ int key_perm(int m) { return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1); }
+
+__device__ __forceinline__ int wave_min(int x) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) x = min(x, __shfl_xor(x, o));
+  return x;
+}
+__device__ __forceinline__ int wave_max(int x) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) x = max(x, __shfl_xor(x, o));
+  return x;
+}
+
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
+
+// Workgroups are dealt round-robin over the 8 XCDs; this gives each XCD a
+// contiguous range of logical ids (neighbouring ids share K/V, hence L2).
+__device__ __forceinline__ int xcd_logical_block() {
+  const int nblk = gridDim.x;
+  const int bid = blockIdx.x;
+  const int per_xcd = nblk / 8;
+  return bid < per_xcd * 8 ? (bid % 8) * per_xcd + bid / 8 : bid;
+}
+
+// Lists, in ring order, the key tiles of schedule slots [u0, u1) that some wave
+// of this workgroup needs.  Slot u is ring step u / tpr (rank (rank - step) mod
+// cp) and tile u % tpr of that rank's shard.  Entry .x = src | i << 8; .y =
+// class(wave w) << 2w, from the tile bounds {min pos, max pos, valid rows} and
+// each wave's row bounds sWb[w] = {min q_pos, max q_pos, min q_lo, max q_lo}.
+template <int BN, int NW>
+__device__ __forceinline__ int build_key_list(const int4* bounds, int tpr, int rank, int cp, int u0, int u1,
+                                              int tid, int wave, int lane, const int (*sWb)[4], int2* sList,
+                                              int* sCnt) {
+  int cnt = 0;
+  for (int base = u0; base < u1; base += NW * 64) {
+    const int u = base + tid;
+    bool act = false;
+    int2 entry = {0, 0};
+    if (u < u1) {
+      const int t = u / tpr;
+      const int i = u - t * tpr;
+      int src = rank - t;
+      if (src < 0) src += cp;
+      const int4 bd = bounds[src * tpr + i];
+      entry.x = src | (i << 8);
+      unsigned cls_bits = 0;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        int cls = kSkip;
+        if (bd.z > 0 && bd.x <= sWb[w][1] && bd.y >= sWb[w][2])
+          cls = (bd.z == BN && bd.y <= sWb[w][0] && bd.x >= sWb[w][3]) ? kFull : kPartial;
+        cls_bits |= (unsigned)cls << (2 * w);
+        act |= cls != kSkip;
+      }
+      entry.y = (int)cls_bits;
+    }
+    const unsigned long long bal = __ballot(act);
+    const int before = __popcll(bal & ((1ull << lane) - 1ull));
+    if (lane == 0) sCnt[wave] = __popcll(bal);
+    __syncthreads();
+    int off = cnt, tot = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      off += w < wave ? sCnt[w] : 0;
+      tot += sCnt[w];
+    }
+    if (act) sList[off + before] = entry;
+    cnt += tot;
+    __syncthreads();
+  }
+  return cnt;
+}
+
+}  // namespace dev
+}  // namespace cpattn

@@ -56,7 +56,57 @@ struct FwdWorkspace {
 FwdWorkspace fwd_workspace_layout(int32_t b, int32_t hkv, int32_t d, int64_t sk, int32_t cp,
                                   int32_t in_dtype);
 
-// Kernel launchers (attn_fwd.hip, merge.hip).  Return hipError_t codes.
+// Everything the backward launches need, resolved and validated on the host.
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* dout;        // same strides as q
+  const void* o;           // final output (delta only), dtype out_dtype, strides o_str
+  const int32_t* q_pos;
+  const int32_t* q_lo;     // may be null
+  const int32_t* k_pos;
+  const float* lse;        // [b, hq, sq] contiguous
+  const float* delta;      // [b, hq, sq] contiguous
+  float* delta_out;        // delta kernel output
+  float* dq;               // [b, hq, sq, d] contiguous fp32, accumulated
+  float* dk;               // [b, hkv, sk, d] contiguous fp32, accumulated
+  float* dv;
+  int64_t q_str[3], k_str[3], v_str[3], o_str[3];
+  int32_t b, hq, hkv, d;
+  int32_t sq, sk;
+  int32_t cp, rank;
+  int32_t rows_per_rank;   // sk / cp
+  float scale;
+  int32_t out_dtype;
+  void* ws;
+};
+
+// Backward key tiles and query tiles both have 64 rows.
+constexpr int kBwdTile = 64;
+
+struct BwdWorkspace {
+  size_t kbounds_off;  // int4 per key tile: {min pos, max pos, valid rows, 0}
+  size_t kpos_off;     // int32 per key slot, padding = INT32_MAX
+  size_t kt_off;       // bf16 K^T [b][hkv][d][kt_row]
+  size_t qbounds_off;  // int4 per query tile: {min pos, max pos, min lo, max lo}
+  size_t qpos_off;     // int32 [sq_pad], padding = -1
+  size_t qlo_off;      // int32 [sq_pad], padding = INT32_MAX
+  size_t lse2_off;     // fp32 [b][hq][sq_pad]: LSE * log2(e)
+  size_t dlt_off;      // fp32 [b][hq][sq_pad]: delta
+  size_t qt_off;       // bf16 Q^T [b][hq][d][sq_pad]
+  size_t dot_off;      // bf16 dO^T [b][hq][d][sq_pad]
+  size_t total;
+  int64_t kt_row;      // cp * ceil((sk / cp) / 64) * 64
+  int64_t sq_pad;      // ceil(sq / 64) * 64
+};
+
+BwdWorkspace bwd_workspace_layout(int32_t b, int32_t hq, int32_t hkv, int32_t d, int64_t sq, int64_t sk,
+                                  int32_t cp);
+
+// Kernel launchers (attn_fwd.hip, attn_bwd.hip, merge.hip).  Return hipError_t codes.
+hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream);
+hipError_t launch_delta(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_merge(int64_t rows, int32_t d, float* o_acc, float* lse_acc, const float* o_p,
                         const float* lse_p, hipStream_t stream);

@@ -166,6 +166,61 @@ int cp_attn_ring_fwd(const cp_shape* s, int32_t cp, int32_t rank, const void* q_
                      const int32_t* q_lo, const int32_t* k_pos_all, void* o, float* lse,
                      void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* ---------------------------------------------------------------- backward
+ * Gradients of the ring forward above with respect to q, k and v.  The pages
+ * train through context-parallel attention (the Accelerate guide wraps the
+ * training step, loss.backward() included, in the context-parallel context;
+ * the Megatron-Bridge skill warns that ranks attending only their local chunk
+ * give broken gradients) but print no backward formula; these calls compute
+ * the exact gradient of softmax attention over the allowed keys, recomputing
+ * the probabilities from the final LSE of the forward:
+ *   P_ij = exp(scale q_i.k_j - LSE_i)     delta_i = dO_i . O_i
+ *   dS_ij = P_ij (dO_i.v_j - delta_i)
+ *   dq_i += scale sum_j dS_ij k_j   dk_j += scale sum_i dS_ij q_i   dv_j += sum_i P_ij dO_i
+ * with key/value heads summing over the query heads that read them.  The
+ * backward takes bf16 q, k, v and dO (in_dtype CP_BF16, else CP_EDTYPE);
+ * gradients accumulate in fp32. */
+
+/* Workspace bytes needed by cp_attn_partial_bwd (cp = 1) and cp_attn_ring_bwd
+ * (cp = ring size).  Returns 0 for an invalid descriptor. */
+size_t cp_attn_bwd_workspace(const cp_shape* s, int32_t cp);
+
+/* delta_i = sum_d dO[i,d] O[i,d] for the sq rows of every (batch, query head).
+ * dout (device bf16, strides q_str) [b,hq,sq,d]; o (device, out_dtype, strides
+ * o_str) the final merged output of the forward; writes delta (device fp32,
+ * contiguous [b,hq,sq]). */
+int cp_attn_bwd_delta(const cp_shape* s, const void* dout, const void* o, float* delta,
+                      hipStream_t stream);
+
+/* Backward of one ring step (the partial of cp_attn_partial_fwd): adds this
+ * step's contributions to dq (device fp32, contiguous [b,hq,sq,d]) and to dk,
+ * dv (device fp32, contiguous [b,hkv,sk,d]).  q, dout (device bf16, strides
+ * q_str); k, v (device bf16) [b,hkv,sk,d]; lse, delta (device fp32, contiguous
+ * [b,hq,sq]) are the final LSE of the whole ring and cp_attn_bwd_delta's
+ * output, so that the step's probabilities are the final ones restricted to its
+ * keys.  Positions as in the forward.  ws (device) of at least
+ * cp_attn_bwd_workspace(s, 1) bytes, 256-byte aligned.  dq, dk, dv must not
+ * overlap each other or the inputs. */
+int cp_attn_partial_bwd(const cp_shape* s, const void* q, const void* k, const void* v,
+                        const void* dout, const float* lse, const float* delta,
+                        const int32_t* q_pos, const int32_t* q_lo, const int32_t* k_pos,
+                        float* dq, float* dk, float* dv, void* ws, size_t ws_bytes,
+                        hipStream_t stream);
+
+/* A virtual rank's whole ring backward with every K/V shard resident: the
+ * contributions of all cp steps (shards in the order of cp_attn_ring_fwd) are
+ * added to dq (device fp32, contiguous [b,hq,sq,d]) and to dk_all, dv_all
+ * (device fp32, contiguous [b,hkv,sk,d], rank-major like k_all).  On a cluster
+ * the rows of shard r would travel back to rank r; summing every rank's call
+ * gives the full key/value gradients.  Other arguments as in
+ * cp_attn_partial_bwd and cp_attn_ring_fwd.  CP_ESHAPE unless sk % (2cp) == 0.
+ * ws (device) of at least cp_attn_bwd_workspace(s, cp) bytes. */
+int cp_attn_ring_bwd(const cp_shape* s, int32_t cp, int32_t rank, const void* q_loc,
+                     const void* k_all, const void* v_all, const void* dout, const float* lse,
+                     const float* delta, const int32_t* q_pos, const int32_t* q_lo,
+                     const int32_t* k_pos_all, float* dq, float* dk_all, float* dv_all,
+                     void* ws, size_t ws_bytes, hipStream_t stream);
+
 /* Message of the last failed call on this thread ("" if none). */
 const char* cp_last_error(void);
 

@@ -39,6 +39,7 @@ class Rank:
         pi = torch.from_numpy(self.pos.astype(np.int64))
         ai = torch.from_numpy(self.allp.astype(np.int64))
         self.q_loc = q.index_select(2, pi).cuda()
+        self.do_loc = full[3].index_select(2, pi).cuda() if len(full) > 3 else None
         self.k_all = k.index_select(2, ai).cuda()
         self.v_all = v.index_select(2, ai).cuda()
         self.scale = 1.0 / math.sqrt(d)
@@ -46,6 +47,28 @@ class Rank:
     def ring_fwd(self, out_dtype=None):
         return cpa.cp_attn_ring_fwd(self.q_loc, self.k_all, self.v_all, self.cp, self.rank, self.pos, self.lo,
                                     self.allp, scale=self.scale, out_dtype=out_dtype)
+
+    def ring_bwd(self):
+        """Forward, delta and ring backward of this rank's rows: (o, lse, dq, dk_all, dv_all)."""
+        o, lse = self.ring_fwd()
+        delta = cpa.cp_attn_bwd_delta(self.do_loc, o)
+        dq, dk, dv = cpa.cp_attn_ring_bwd(self.q_loc, self.k_all, self.v_all, self.do_loc, lse, delta, self.cp,
+                                          self.rank, self.pos, self.lo, self.allp, scale=self.scale)
+        return o, lse, dq, dk, dv
+
+    def oracle_grads(self, q_heads=None):
+        """Oracle gradients of this rank's loss sum_i dO_i . O_i over its rows:
+        dq for its rows, dk and dv in rank-major (k_all) order.  q_heads
+        restricts the check to whole groups of query heads (a slice that starts
+        and ends on a group boundary)."""
+        q, k, v, do = (t.double().numpy() for t in self.full[:4])
+        if q_heads is not None:
+            g = self.Hq // self.Hkv
+            assert q_heads.start % g == 0 and q_heads.stop % g == 0
+            kv = slice(q_heads.start // g, q_heads.stop // g)
+            q, do, k, v = q[:, q_heads], do[:, q_heads], k[:, kv], v[:, kv]
+        dq, dk, dv = orc.attention_bwd(q, k, v, do[:, :, self.pos], self.scale, cu_seqlens=self.cu, rows=self.pos)
+        return dq, dk[:, :, self.allp], dv[:, :, self.allp]
 
     def oracle(self, rows_idx=None):
         """Oracle O, LSE for this rank's rows (or the subset rows_idx of them)."""

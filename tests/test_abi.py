@@ -220,3 +220,73 @@ def test_python_wrappers_raise_value_error():
         cpa.cp_attn_fwd_workspace(q, q, q, 1)
     with pytest.raises(ValueError):
         cpa.cp_attn_merge(torch.zeros(4, 64), torch.zeros(3), torch.zeros(4, 64), torch.zeros(4))
+
+
+# ------------------------------------------------------------------ backward validation (no launch)
+def _ring_bwd(s, cp=2, rank=0, ws=FAKE, ws_bytes=1 << 40, q=FAKE, dout=FAKE, lse=FAKE, dk=FAKE):
+    L = cpa.lib()
+    return L.cp_attn_ring_bwd(ctypes.byref(s) if s is not None else None, cp, rank, q, FAKE, FAKE, dout, lse, FAKE,
+                              FAKE, None, FAKE, FAKE, dk, FAKE, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(hq=3, hkv=2), cpa.CP_EINVAL),
+    (dict(d=96), cpa.CP_EINVAL),
+    (dict(scale=-1.0), cpa.CP_EINVAL),
+    (dict(in_dtype=cpa.CP_F32), cpa.CP_EDTYPE),
+    (dict(q_row=129), cpa.CP_EINVAL),
+    (dict(sk=502), cpa.CP_ESHAPE),
+])
+def test_ring_bwd_rejects_bad_shapes(kw, code):
+    assert _ring_bwd(_shape(**kw)) == code
+    assert cpa.cp_last_error() != ""
+
+
+def test_ring_bwd_rejects_bad_args():
+    s = _shape()
+    assert _ring_bwd(None) == cpa.CP_EINVAL
+    assert _ring_bwd(s, cp=0) == cpa.CP_EINVAL
+    assert _ring_bwd(s, rank=2) == cpa.CP_EINVAL
+    assert _ring_bwd(s, q=0) == cpa.CP_EINVAL
+    assert _ring_bwd(s, dout=FAKE + 4) == cpa.CP_EINVAL
+    assert _ring_bwd(s, lse=0) == cpa.CP_EINVAL
+    assert _ring_bwd(s, dk=0) == cpa.CP_EINVAL
+    assert _ring_bwd(s, ws=0) == cpa.CP_EWORKSPACE
+    assert _ring_bwd(s, ws=FAKE + 16) == cpa.CP_EWORKSPACE
+    need = cpa.lib().cp_attn_bwd_workspace(ctypes.byref(s), 2)
+    assert need > 0
+    assert _ring_bwd(s, ws_bytes=need - 1) == cpa.CP_EWORKSPACE
+
+
+def test_bwd_workspace_query():
+    s = _shape(sk=131072, sq=16384, hq=32, hkv=8)
+    n = cpa.lib().cp_attn_bwd_workspace(ctypes.byref(s), 8)
+    # K^T (8 kv heads), Q^T and dO^T (32 heads) in bf16, plus per-row tables
+    kt = 8 * 128 * 131072 * 2
+    qt = 2 * 32 * 128 * 16384 * 2
+    assert kt + qt <= n < kt + qt + (8 << 20)
+    assert cpa.lib().cp_attn_bwd_workspace(ctypes.byref(_shape(d=96)), 8) == 0
+
+
+def test_bwd_delta_and_partial_validation():
+    L = cpa.lib()
+    s = _shape()
+    assert L.cp_attn_bwd_delta(ctypes.byref(_shape(in_dtype=cpa.CP_F32)), FAKE, FAKE, FAKE, None) == cpa.CP_EDTYPE
+    assert L.cp_attn_bwd_delta(ctypes.byref(s), 0, FAKE, FAKE, None) == cpa.CP_EINVAL
+    assert L.cp_attn_bwd_delta(ctypes.byref(s), FAKE, FAKE, 0, None) == cpa.CP_EINVAL
+    assert L.cp_attn_bwd_delta(ctypes.byref(_shape(sq=0)), 0, 0, 0, None) == cpa.CP_OK
+    s5 = _shape(hq=5, hkv=2)
+    assert L.cp_attn_partial_bwd(ctypes.byref(s5), *([FAKE] * 6), FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                 1 << 30, None) == cpa.CP_EINVAL
+    # no query rows or no keys: nothing to add, and nothing is read
+    assert L.cp_attn_partial_bwd(ctypes.byref(_shape(sq=0)), *([0] * 6), 0, None, 0, 0, 0, 0, 0, 0,
+                                 None) == cpa.CP_OK
+
+
+def test_bwd_python_wrappers_raise_value_error():
+    q = torch.zeros(1, 2, 8, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        cpa.cp_attn_bwd_workspace(torch.zeros(1, 2, 8, 96), torch.zeros(1, 2, 8, 96), torch.zeros(1, 2, 8, 96))
+    with pytest.raises(ValueError):  # dout strides differ from q's
+        cpa.cp_attn_partial_bwd(q, q, q, q.transpose(1, 2).contiguous().transpose(1, 2), torch.zeros(1, 2, 8),
+                                torch.zeros(1, 2, 8), [0] * 8, None, [0] * 8)

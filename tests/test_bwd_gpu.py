@@ -1,0 +1,173 @@
+"""GPU parity of the backward (cp_attn_bwd_delta, cp_attn_partial_bwd,
+cp_attn_ring_bwd) against the fp64 oracle's gradients, through the C ABI.
+Gradients of bf16 inputs must be within 5e-2 max-abs of the oracle."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as orc
+import seeded_inputs as si
+import context_causal_attention_amd as cpa
+from gpu_cases import Rank, announce, max_err
+
+pytestmark = pytest.mark.gpu
+
+GTOL = 5e-2
+
+
+def _np(t):
+    return t.double().cpu().numpy()
+
+
+def _check_grads(got, ref, what):
+    errs = []
+    for name, g, r in zip(("dq", "dk", "dv"), got, ref):
+        e = max_err(g, r)
+        errs.append(e)
+        assert np.isfinite(e) and e <= GTOL, f"{what}: {name} max-abs error {e:.3e} > {GTOL}"
+    return errs
+
+
+@pytest.mark.parametrize("o_dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("d", [64, 128])
+def test_delta_matches_oracle(o_dtype, d):
+    announce(f"delta d={d} o={o_dtype}")
+    g = torch.Generator().manual_seed(3)
+    B, H, S = 2, 3, 333
+    dout = torch.randn(B, S, H, d, generator=g).to(torch.bfloat16).transpose(1, 2)  # strided rows
+    o = torch.randn(B, H, S, d, generator=g).to(o_dtype)
+    delta = cpa.cp_attn_bwd_delta(dout.cuda(), o.cuda())
+    ref = orc.bwd_delta(_np(dout), _np(o))
+    assert max_err(delta, ref) <= 1e-4
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,S,d,cp", [
+    (1, 2, 1, 1024, 64, 2),     # the C0 shape, bf16
+    (1, 4, 2, 768, 128, 3),     # 256 rows a rank: 4 full 64-row tiles
+    (1, 2, 2, 1200, 64, 3),     # 400 rows a rank: ragged key and query tiles
+    (2, 8, 2, 640, 128, 5),     # batch 2, four query heads a group
+    (1, 4, 1, 4096, 128, 1),    # cp = 1: plain causal attention
+])
+def test_ring_bwd_all_ranks_sum_to_full_gradients(B, Hq, Hkv, S, d, cp):
+    """Every rank's ring backward, summed, gives the gradients of the whole
+    sequence: dq row by row, dk and dv from every rank's contribution."""
+    q, k, v, do = si.make_qkv(B, Hq, Hkv, S, d, "bf16", seed=4, with_dout=True)
+    scale = 1 / math.sqrt(d)
+    dq_ref, dk_ref, dv_ref = orc.attention_bwd(_np(q), _np(k), _np(v), _np(do), scale)
+    dk_sum = dv_sum = None
+    for rank in range(cp):
+        announce(f"ring bwd B={B} Hq={Hq} Hkv={Hkv} S={S} d={d} cp={cp} rank {rank}")
+        R = Rank(B, Hq, Hkv, S, d, cp, rank, "bf16", full=(q, k, v, do))
+        _, _, dq, dk, dv = R.ring_bwd()
+        e = max_err(dq, dq_ref[:, :, R.pos])
+        assert e <= GTOL, f"rank {rank}: dq max-abs error {e:.3e}"
+        dk_sum = dk if dk_sum is None else dk_sum + dk
+        dv_sum = dv if dv_sum is None else dv_sum + dv
+    allp = cpa.cp_unshard_zigzag(S, cp)
+    for name, g, r in (("dk", dk_sum, dk_ref[:, :, allp]), ("dv", dv_sum, dv_ref[:, :, allp])):
+        e = max_err(g, r)
+        assert e <= GTOL, f"{name} summed over ranks: max-abs error {e:.3e}"
+
+
+@pytest.mark.parametrize("rank", [0, 7])
+def test_ring_bwd_32k_cp8_per_rank(rank):
+    """The backward on the Llama-3-8B-shaped 32 768-token cp=8 workload (32
+    query / 8 kv heads, d = 128, bf16): the whole ring of one virtual rank,
+    checked on the first kv group (query heads 0-3, kv head 0) against the
+    oracle's gradients of that rank's loss."""
+    w = si.WORKLOADS["bwd_s32k_cp8"]
+    announce(f"ring bwd 32k cp8 rank {rank}")
+    R = Rank(w.B, w.Hq, w.Hkv, w.S, w.d, w.cp, rank, "bf16", seed=w.seed, with_dout=True)
+    _, _, dq, dk, dv = R.ring_bwd()
+    torch.cuda.synchronize()
+    g = w.Hq // w.Hkv
+    ref = R.oracle_grads(q_heads=slice(0, g))
+    _check_grads((dq[:, :g], dk[:, :1], dv[:, :1]), ref, f"32k rank {rank}")
+    for t in (dq, dk, dv):
+        assert torch.isfinite(t).all()
+
+
+@pytest.mark.parametrize("mode", [cpa.CP_STREAM, cpa.CP_PER_DOC])
+def test_ring_bwd_varlen(mode):
+    """Block-diagonal document masks: each rank's loss against the oracle with
+    the same cu_seqlens."""
+    cp, d = 2, 128
+    lens = [256, 512, 128, 640, 512] if mode == cpa.CP_STREAM else [256, 512, 128, 640, 512]
+    cu = si.cu_seqlens_from_lengths(lens)
+    S = int(cu[-1])
+    full = si.make_qkv(1, 4, 2, S, d, "bf16", seed=5, with_dout=True)
+    for rank in range(cp):
+        announce(f"ring bwd varlen mode={mode} rank {rank}")
+        R = Rank(1, 4, 2, S, d, cp, rank, "bf16", cu=cu, mode=mode, full=full)
+        _, _, dq, dk, dv = R.ring_bwd()
+        _check_grads((dq, dk, dv), R.oracle_grads(), f"varlen mode {mode} rank {rank}")
+
+
+def test_partial_bwd_steps_match_ring():
+    """The per-step path (one cp_attn_partial_bwd a ring step, each with the
+    final LSE and delta) adds up to the fused ring backward and to the oracle."""
+    B, Hq, Hkv, S, d, cp = 1, 4, 1, 1536, 64, 3
+    full = si.make_qkv(B, Hq, Hkv, S, d, "bf16", seed=6, with_dout=True)
+    for rank in range(cp):
+        announce(f"partial bwd steps rank {rank}")
+        R = Rank(B, Hq, Hkv, S, d, cp, rank, "bf16", full=full)
+        o, lse, dq_r, dk_r, dv_r = R.ring_bwd()
+        delta = cpa.cp_attn_bwd_delta(R.do_loc, o)
+        n = S // cp
+        dq = torch.zeros_like(dq_r)
+        dk = torch.zeros_like(dk_r)
+        dv = torch.zeros_like(dv_r)
+        for t in range(cp):
+            src = cpa.cp_ring_source(cp, rank, t)
+            sl = slice(src * n, (src + 1) * n)
+            cpa.cp_attn_partial_bwd(R.q_loc, R.k_all[:, :, sl], R.v_all[:, :, sl], R.do_loc, lse, delta, R.pos,
+                                    None, R.allp[sl], dq=dq, dk=dk[:, :, sl], dv=dv[:, :, sl], scale=R.scale)
+        for a, b_ in ((dq, dq_r), (dk, dk_r), (dv, dv_r)):
+            assert (a - b_).abs().max().item() <= 1e-3
+        _check_grads((dq, dk, dv), R.oracle_grads(), f"partial steps rank {rank}")
+
+
+def test_bwd_accumulates_and_is_deterministic():
+    """Calls add into the gradient buffers: a second identical call doubles
+    them exactly, and two fresh runs agree bit for bit."""
+    R = Rank(1, 4, 2, 1024, 128, 2, 1, "bf16", seed=7, with_dout=True)
+    announce("bwd accumulate / determinism")
+    o, lse = R.ring_fwd()
+    delta = cpa.cp_attn_bwd_delta(R.do_loc, o)
+    args = (R.q_loc, R.k_all, R.v_all, R.do_loc, lse, delta, R.cp, R.rank, R.pos, R.lo, R.allp)
+    dq1, dk1, dv1 = cpa.cp_attn_ring_bwd(*args, scale=R.scale)
+    dq1, dk1, dv1 = dq1.clone(), dk1.clone(), dv1.clone()
+    dq2, dk2, dv2 = cpa.cp_attn_ring_bwd(*args, scale=R.scale)
+    assert torch.equal(dq2, dq1) and torch.equal(dk2, dk1) and torch.equal(dv2, dv1)
+    cpa.cp_attn_ring_bwd(*args, scale=R.scale, dq=dq2, dk=dk2, dv=dv2)
+    assert torch.equal(dq2, 2 * dq1) and torch.equal(dk2, 2 * dk1) and torch.equal(dv2, 2 * dv1)
+
+
+def test_bwd_strided_inputs():
+    """q and dO as [B, S, H, D] storage viewed as [B, H, S, D] (row stride H*D)."""
+    B, Hq, Hkv, S, d, cp = 1, 4, 2, 1024, 128, 2
+    q, k, v, do = si.make_qkv(B, Hq, Hkv, S, d, "bf16", seed=8, with_dout=True)
+    for rank in range(cp):
+        announce(f"bwd strided rank {rank}")
+        R = Rank(B, Hq, Hkv, S, d, cp, rank, "bf16", full=(q, k, v, do))
+        R.q_loc = R.q_loc.transpose(1, 2).contiguous().transpose(1, 2)
+        R.do_loc = R.do_loc.transpose(1, 2).contiguous().transpose(1, 2)
+        R.k_all = R.k_all.transpose(1, 2).contiguous().transpose(1, 2)
+        _, _, dq, dk, dv = R.ring_bwd()
+        _check_grads((dq, dk, dv), R.oracle_grads(), f"strided rank {rank}")
+
+
+def test_bwd_empty_inputs():
+    announce("bwd empty inputs")
+    q = torch.zeros(1, 2, 0, 64, dtype=torch.bfloat16, device="cuda")
+    k = torch.randn(1, 1, 64, 64, device="cuda").to(torch.bfloat16)
+    e = torch.zeros(1, 2, 0, device="cuda")
+    dq, dk, dv = cpa.cp_attn_partial_bwd(q, k, k, q, e, e, [], None, list(range(64)))
+    assert dq.numel() == 0 and torch.all(dk == 0) and torch.all(dv == 0)
+    q = torch.randn(1, 2, 64, 64, device="cuda").to(torch.bfloat16)
+    k0 = torch.zeros(1, 1, 0, 64, dtype=torch.bfloat16, device="cuda")
+    l = torch.zeros(1, 2, 64, device="cuda")
+    dq, dk, dv = cpa.cp_attn_partial_bwd(q, k0, k0, q, l, l, list(range(64)), None, [])
+    assert torch.all(dq == 0)
