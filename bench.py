@@ -1,12 +1,16 @@
 """Throughput of the causal context-parallel attention hot path on one MI355X.
 
-A step is one pass of the hot path over one batch of synthetic input: the ring
-forward of every virtual rank r = 0..cp-1 of the workload, one after another,
-with every K/V shard already resident in HBM (index maps are built once, in
-set-up).  ``value`` is the algorithmic work of those passes (4*d*Hq per
-unmasked (query, key) pair, exact pair counts from the index builder) divided
-by the time of the timed steps, in TFLOP/s: the time-weighted mean throughput
-of one virtual rank.
+A step is one pass of the hot path over one batch of synthetic input, for every
+virtual rank r = 0..cp-1 of the workload, one after another, with every K/V
+shard already resident in HBM (index maps are built once, in set-up):
+  --pass fwdbwd (default): zero the fp32 gradient buffers, then per rank the
+      ring forward (final O, LSE), delta = rowsum(dO * O) and the ring backward
+      (dQ of the rank's rows, dK/dV of every shard accumulated in place);
+  --pass fwd: the ring forward of each rank only.
+``value`` is the algorithmic work of a step divided by the time of the timed
+steps, in TFLOP/s: 4*d*Hq flops per allowed (query, key) pair for the forward
+(Q K^T and P V) and 10*d*Hq for the backward (Q K^T, dO V^T, P^T dO, dS K and
+dS^T Q), with exact pair counts from the index builder.
 
 Prints one JSON line.  ``--gpus N`` with N > 1 exits: this build runs on one
 GPU and every figure is that GPU's.
@@ -28,7 +32,11 @@ PEAK_BF16_TFLOPS = 2516.6   # 256 CU x 4096 flop/clk x 2.4 GHz, dense bf16 MFMA 
 PEAK_F32_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
 PROFILES = os.path.join(ROOT, "profiles")
-KERNEL_SOURCES = {"fwd": ["context_causal_attention_amd/csrc/attn_fwd.hip"]}
+KERNEL_SOURCES = {
+    "fwd": ["context_causal_attention_amd/csrc/attn_fwd.hip", "context_causal_attention_amd/csrc/device_common.h"],
+    "bwd": ["context_causal_attention_amd/csrc/attn_bwd.hip", "context_causal_attention_amd/csrc/device_common.h"],
+}
+FLOPS_PER_PAIR_HEAD_DIM = {"fwd": 4.0, "bwd": 10.0}
 
 
 def source_hash(paths):
@@ -69,6 +77,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="llama8b_s128k_cp8")
     ap.add_argument("--ranks", default="all", help="'all' or a comma list of virtual ranks")
+    ap.add_argument("--pass", dest="mode", choices=["fwd", "fwdbwd"], default="fwdbwd")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time for the cpu_baseline sample")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -107,10 +116,14 @@ def main():
     import seeded_inputs as si
 
     w = si.WORKLOADS[args.workload]
+    bwd = args.mode == "fwdbwd"
+    if bwd and w.dtype != "bf16":
+        print(f"the backward takes bf16 inputs; {w.name} is {w.dtype} (use --pass fwd)", file=sys.stderr)
+        sys.exit(2)
     dev = torch.device("cuda:0")
     t0 = time.time()
-    full = si.make_qkv(w.B, w.Hq, w.Hkv, w.S, w.d, w.dtype, seed=w.seed)
-    q, k, v = full
+    full = si.make_qkv(w.B, w.Hq, w.Hkv, w.S, w.d, w.dtype, seed=w.seed, with_dout=bwd)
+    q, k, v = full[:3]
     cu = si.cu_seqlens_from_lengths(si.doc_lengths(total=w.S, seed=w.seed)) if w.varlen else None
     ranks = list(range(w.cp)) if args.ranks == "all" else [int(x) for x in args.ranks.split(",")]
 
@@ -123,32 +136,53 @@ def main():
     ai = torch.from_numpy(allp.astype(np.int64))
     k_all = k.index_select(2, ai).to(dev)
     v_all = v.index_select(2, ai).to(dev)
-    plans, flops = {}, {}
+    passes = ["fwd", "bwd"] if bwd else ["fwd"]
+    fplans, bplans, deltas, pairs = {}, {}, {}, {}
+    dk_all = torch.zeros(k_all.shape, dtype=torch.float32, device=dev) if bwd else None
+    dv_all = torch.zeros(v_all.shape, dtype=torch.float32, device=dev) if bwd else None
     for r in ranks:
         pos, lo = idx[r]
-        q_loc = q.index_select(2, torch.from_numpy(pos.astype(np.int64))).to(dev)
-        plans[r] = cpa.RingFwdPlan(q_loc, k_all, v_all, w.cp, r, pos, lo, allp, scale=w.scale)
-        flops[r] = 4.0 * w.d * w.Hq * w.B * cpa.cp_pairs(pos, lo, allp)
+        pi = torch.from_numpy(pos.astype(np.int64))
+        q_loc = q.index_select(2, pi).to(dev)
+        fplans[r] = cpa.RingFwdPlan(q_loc, k_all, v_all, w.cp, r, pos, lo, allp, scale=w.scale)
+        pairs[r] = cpa.cp_pairs(pos, lo, allp)
+        if bwd:
+            do_loc = full[3].index_select(2, pi).to(dev)
+            deltas[r] = (do_loc, torch.empty(fplans[r].lse.shape, dtype=torch.float32, device=dev))
+            bplans[r] = cpa.RingBwdPlan(q_loc, k_all, v_all, do_loc, fplans[r].lse, deltas[r][1], w.cp, r, pos, lo,
+                                        allp, scale=w.scale, dk=dk_all, dv=dv_all)
+    flops = {ps: {r: FLOPS_PER_PAIR_HEAD_DIM[ps] * w.d * w.Hq * w.B * pairs[r] for r in ranks} for ps in passes}
     torch.cuda.synchronize()
     setup_s = time.time() - t0
-    print(f"[bench] set-up {setup_s:.1f}s: {w.name} ranks {ranks}", file=sys.stderr, flush=True)
+    print(f"[bench] set-up {setup_s:.1f}s: {w.name} ranks {ranks} pass {args.mode}", file=sys.stderr, flush=True)
 
     stream = torch.cuda.current_stream(dev)
 
     def step(events=None):
+        if bwd:
+            dk_all.zero_()
+            dv_all.zero_()
         for r in ranks:
             if events is not None:
-                events[r][0].record(stream)
-            plans[r].run()
+                events["fwd"][r][0].record(stream)
+            o, _ = fplans[r].run()
             if events is not None:
-                events[r][1].record(stream)
+                events["fwd"][r][1].record(stream)
+            if bwd:
+                bplans[r].dq.zero_()
+                cpa.cp_attn_bwd_delta(deltas[r][0], o, deltas[r][1])
+                if events is not None:
+                    events["bwd"][r][0].record(stream)
+                bplans[r].run()
+                if events is not None:
+                    events["bwd"][r][1].record(stream)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
-    ev = [{r: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for r in ranks}
-          for _ in range(args.steps)]
+    ev = [{ps: {r: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for r in ranks}
+           for ps in passes} for _ in range(args.steps)]
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     for s in range(args.steps):
@@ -156,22 +190,40 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
 
-    per_rank_ms = {r: float(np.mean([ev[s][r][0].elapsed_time(ev[s][r][1]) for s in range(args.steps)]))
-                   for r in ranks}
-    step_flops = sum(flops.values())
+    launch_ms = {ps: {r: float(np.mean([ev[s][ps][r][0].elapsed_time(ev[s][ps][r][1]) for s in range(args.steps)]))
+                      for r in ranks} for ps in passes}
+    step_flops = sum(sum(f.values()) for f in flops.values())
     ms_per_step = wall * 1e3 / args.steps
     value = step_flops / (wall / args.steps) / 1e12
-    launch_ms = float(np.mean(list(per_rank_ms.values())))
-    launch_flops = step_flops / len(ranks)
-    achieved = launch_flops / (launch_ms * 1e-3) / 1e12
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
-    print(f"[bench] per-rank ms: " + ", ".join(f"{r}:{per_rank_ms[r]:.3f}" for r in ranks), file=sys.stderr,
-          flush=True)
+    for ps in passes:
+        print(f"[bench] {ps} per-rank ms: " + ", ".join(f"{r}:{launch_ms[ps][r]:.3f}" for r in ranks),
+              file=sys.stderr, flush=True)
+
+    def roof(ps):
+        ms = float(np.mean(list(launch_ms[ps].values())))
+        fl = sum(flops[ps].values()) / len(ranks)
+        ach = fl / (ms * 1e-3) / 1e12
+        kern = {"fwd": "cp_attn_ring_fwd launch (prep_kernel: bounds and V^T; fwd_bf16_kernel)",
+                "bwd": "cp_attn_ring_bwd launch (key_prep_kernel, query_prep_kernel, dkdv_kernel, dq_kernel)"}[ps]
+        return {"bound": "mfma", "achieved": round(ach, 3), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(ach / peak, 4), "traffic": stored_traffic(ps, w.name), "launch_ms": round(ms, 4),
+                "kernel": kern + "; achieved = algorithmic flops per launch / mean launch time from HIP events "
+                "on the launch stream; traffic = calibrated FETCH_SIZE + WRITE_SIZE bytes per launch"}
+
+    rooflines = {ps: roof(ps) for ps in passes}
+    dominant = max(passes, key=lambda ps: rooflines[ps]["launch_ms"])
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(w, full, idx[ranks[0]], allp, cu, args.cpu_seconds, ranks[0])
+        cpu = cpu_baseline(w, full, idx[ranks[0]], allp, cu, args.cpu_seconds, ranks[0], bwd)
 
+    per_pass = {}
+    for ps in passes:
+        tot_ms = sum(launch_ms[ps].values())
+        per_pass[ps] = {"TFLOP/s": round(sum(flops[ps].values()) / (tot_ms * 1e-3) / 1e12, 3),
+                        "pct_peak": round(100 * sum(flops[ps].values()) / (tot_ms * 1e-3) / 1e12 / peak, 2),
+                        "per_rank_ms": {str(r): round(x, 4) for r, x in launch_ms[ps].items()}}
     out = {
         "metric": METRIC,
         "value": round(value, 3),
@@ -185,36 +237,43 @@ def main():
         "vs_baseline": None,
         "dtype": w.dtype,
         "data": "synthetic",
-        "config": {"workload": w.name, "pass": "fwd", "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "d": w.d, "S": w.S,
-                   "cp": w.cp, "ranks": ranks, "varlen": w.varlen,
-                   "step": "ring forward of each listed virtual rank, sequential, K/V resident"},
+        "config": {"workload": w.name, "pass": "fwd+bwd" if bwd else "fwd", "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv,
+                   "d": w.d, "S": w.S, "cp": w.cp, "ranks": ranks, "varlen": w.varlen,
+                   "step": ("per rank: ring forward, delta, ring backward (fp32 dQ/dK/dV zeroed once a step)"
+                            if bwd else "ring forward of each listed virtual rank") +
+                           ", ranks sequential, K/V resident"},
         "pct_peak": round(100 * value / peak, 2),
-        "per_rank_ms": {str(r): round(x, 4) for r, x in per_rank_ms.items()},
-        "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak, "unit": "TFLOP/s",
-                     "frac": round(achieved / peak, 4), "traffic": stored_traffic("fwd", w.name),
-                     "kernel": "cp_attn_ring_fwd launch (V-transpose prep + fwd_bf16_kernel), HIP events "
-                               "on the launch stream; traffic = calibrated FETCH_SIZE + WRITE_SIZE per launch"},
+        "passes": per_pass,
+        "roofline": rooflines[dominant],
+        "roofline_by_pass": rooflines,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
 
 
-def cpu_baseline(w, full, idx_r, allp, cu, target_s, rank_id):
-    """The fp64 oracle, as it stands, on a bounded sample of the same workload:
-    one virtual rank's rows for as many query heads as fit in ~target_s."""
+def cpu_baseline(w, full, idx_r, allp, cu, target_s, rank_id, bwd):
+    """The fp64 oracle, as it stands, on a bounded sample of the same workload,
+    one query head at a time until ~target_s have passed: the forward
+    (attention_fwd) over all of one virtual rank's rows, or for --pass fwdbwd
+    the backward (attention_bwd, which runs its own forward) over every 16th
+    of those rows; flops counted like the GPU's, from the exact pair count of
+    the rows sampled."""
     import numpy as np
     import oracle as orc
     import context_causal_attention_amd as cpa
 
     pos, lo = idx_r
-    q, k, v = full
+    q, k, v = full[:3]
     try:
         from threadpoolctl import threadpool_info
         cores = max(int(i.get("num_threads", 1)) for i in threadpool_info() if i.get("user_api") == "blas")
     except Exception:
         cores = len(os.sched_getaffinity(0))
     g = w.Hq // w.Hkv
-    pairs = cpa.cp_pairs(pos, lo, allp)
+    stride = 16 if bwd else 1
+    rows = pos[::stride]
+    pairs = cpa.cp_pairs(rows, None if lo is None else lo[::stride], allp)
+    per_pair = 14.0 if bwd else 4.0
     t0 = time.perf_counter()
     done = 0
     while done < w.Hq:
@@ -222,14 +281,19 @@ def cpu_baseline(w, full, idx_r, allp, cu, target_s, rank_id):
         qh = q[:, h:h + 1].double().numpy()
         kh = k[:, h // g:h // g + 1].double().numpy()
         vh = v[:, h // g:h // g + 1].double().numpy()
-        orc.attention_fwd(qh, kh, vh, w.scale, cu_seqlens=cu, rows=pos)
+        if bwd:
+            do = full[3][:, h:h + 1].double().numpy()[:, :, rows]
+            orc.attention_bwd(qh, kh, vh, do, w.scale, cu_seqlens=cu, rows=rows)
+        else:
+            orc.attention_fwd(qh, kh, vh, w.scale, cu_seqlens=cu, rows=rows)
         done += 1
         if time.perf_counter() - t0 >= target_s:
             break
     el = time.perf_counter() - t0
-    fl = 4.0 * w.d * done * pairs
+    fl = per_pair * w.d * done * pairs
+    what = (f"forward+backward (attention_bwd) of every {stride}th row" if bwd else "forward of the rows")
     return {"value": round(fl / el / 1e12, 5), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
-            "sample": f"{w.name}: the rows of virtual rank {rank_id}, {done} of {w.Hq} query heads, "
+            "sample": f"{w.name}: {what} of virtual rank {rank_id}, {done} of {w.Hq} query heads, "
                       f"fp64 numpy, {el:.1f}s"}
 
 

@@ -137,12 +137,10 @@ BwdWorkspace bwd_workspace_layout(int32_t b, int32_t hq, int32_t hkv, int32_t d,
   w.kpos_off = take((size_t)w.kt_row * 4);
   w.kt_off = take((size_t)b * hkv * d * (size_t)w.kt_row * 2);
   w.qbounds_off = take((size_t)nqt * 16);
-  w.qpos_off = take((size_t)w.sq_pad * 4);
   w.qlo_off = take((size_t)w.sq_pad * 4);
-  w.lse2_off = take((size_t)b * hq * (size_t)w.sq_pad * 4);
+  w.qspan_off = take((size_t)w.sq_pad * 4);
+  w.nl2_off = take((size_t)b * hq * (size_t)w.sq_pad * 4);
   w.dlt_off = take((size_t)b * hq * (size_t)w.sq_pad * 4);
-  w.qt_off = take((size_t)b * hq * d * (size_t)w.sq_pad * 2);
-  w.dot_off = take((size_t)b * hq * d * (size_t)w.sq_pad * 2);
   w.total = off < 256 ? 256 : off;
   return w;
 }
@@ -291,6 +289,10 @@ int run_bwd(const cp_shape* s, int32_t cp, int32_t rank, const void* q, const vo
   const int64_t per = s->sk / cp;
   if ((per + kBwdTile - 1) / kBwdTile > 65535)
     return fail(CP_EINVAL, "a shard of %lld key rows has more than 65535 key tiles", (long long)per);
+  // The dK/dV kernel lists (query head, query tile) pairs in 16 + 15 bits.
+  if ((s->sq + kBwdTile - 1) / kBwdTile > 65535 || s->hq / s->hkv > 32767)
+    return fail(CP_EINVAL, "%lld query rows or %d query heads per kv head are too many for the backward",
+                (long long)s->sq, s->hq / s->hkv);
   const BwdWorkspace w = bwd_workspace_layout(s->b, s->hq, s->hkv, s->d, s->sq, s->sk, cp);
   // The kernels address the transposed copies and the padded per-row arrays
   // with 32-bit buffer offsets.

@@ -13,12 +13,14 @@
 //     Scores are computed as S = Q K^T so that a lane owns one key: K and V of
 //     the wave's keys are resident MFMA operands, and P and dS come out of the
 //     accumulators already in the operand layout of dV^T += dO^T P and
-//     dK^T += Q^T dS (query rows read in the permuted order of key_perm).
+//     dK^T += Q^T dS (query rows read in the permuted order of key_perm); the
+//     dO^T and Q^T operands are read from the row-major tiles with transposing
+//     LDS reads.
 //   * dq_kernel: a workgroup owns 256 query rows (32 a wave) of one head and
 //     walks the ring's key tiles like the forward; S^T = K Q^T, dP^T = V dO^T,
 //     dQ^T += K^T dS^T, with Q and dO of the wave's rows resident.
 // Operand tiles are copied HBM -> LDS by buffer loads with the LDS-direct bit;
-// transposed copies (Q^T, dO^T, K^T) come from a preparation pass.
+// K^T comes from a preparation pass.
 #include <hip/hip_runtime.h>
 
 #include <climits>
@@ -48,12 +50,10 @@ struct BParams {
   const int* kpos_pad;   // per key slot, padding = kInvalidKey
   const char* kt;        // bf16 K^T [b][hkv][d][kt_row]
   const int4* qbounds;   // per 64-row query tile {min pos, max pos, min lo, max lo}
-  const int* qpos_pad;   // per query slot [sq_pad], padding = -1
-  const int* qlo_pad;    // padding = INT_MAX
-  const float* lse2;     // [b][hq][sq_pad]: LSE * log2(e), 0 in padding
+  const int* qlo_pad;    // per query slot [sq_pad]: document start (padding INT_MIN)
+  const int* qspan_pad;  // position - document start (padding 0)
+  const float* nl2;      // [b][hq][sq_pad]: -LSE * log2(e), 0 in padding
   const float* dlt;      // [b][hq][sq_pad]: delta, 0 in padding
-  const char* qt;        // bf16 Q^T  [b][hq][d][sq_pad]
-  const char* dot;       // bf16 dO^T [b][hq][d][sq_pad]
   float* dq;             // fp32 [b, hq, sq, d] contiguous, accumulated
   float* dk;             // fp32 [b, hkv, sk, d] contiguous, accumulated
   float* dv;
@@ -108,60 +108,32 @@ __global__ __launch_bounds__(256) void key_prep_kernel(BParams p, int4* __restri
   }
 }
 
-// Query side, per 64-row tile of one (batch, query head): Q^T and dO^T, LSE in
-// base 2 and delta padded to the tile grid; for the first (batch, head) also the
-// tile's position bounds and the padded positions.
-template <int D>
-__global__ __launch_bounds__(256) void query_prep_kernel(BParams p, const float* __restrict__ lse,
-                                                         const float* __restrict__ delta, int4* __restrict__ qbounds,
-                                                         int* __restrict__ qpos_pad, int* __restrict__ qlo_pad,
-                                                         float* __restrict__ lse2, float* __restrict__ dlt,
-                                                         __bf16* __restrict__ qt, __bf16* __restrict__ dot) {
+// Query side, per 64-row tile of one (batch, query head): -LSE in base 2 and
+// delta padded to the tile grid; for the first (batch, head) also the tile's
+// position bounds and each row's document start and span (position minus
+// document start), the form the dK/dV kernel's mask test takes.
+__global__ __launch_bounds__(64) void query_prep_kernel(BParams p, const float* __restrict__ lse,
+                                                        const float* __restrict__ delta, int4* __restrict__ qbounds,
+                                                        int* __restrict__ qlo_pad, int* __restrict__ qspan_pad,
+                                                        float* __restrict__ nl2, float* __restrict__ dlt) {
   const int tile = blockIdx.x;
   const int r0 = tile * kQT;
   const int nval = min(kQT, p.sq - r0);
   const int tid = threadIdx.x;
   const int bh = blockIdx.y;  // b * Hq + h
-  if (bh == 0 && tid < 64) {
-    const bool ok = tid < nval;
+  const bool ok = tid < nval;
+  if (bh == 0) {
     const int qp = ok ? p.q_pos[r0 + tid] : -1;
     const int ql = ok ? (p.q_lo ? p.q_lo[r0 + tid] : 0) : INT_MAX;
     const int a = wave_min(ok ? qp : INT_MAX), b = wave_max(ok ? qp : INT_MIN);
     const int c = wave_min(ok ? ql : INT_MAX), d = wave_max(ok ? ql : INT_MIN);
     if (tid == 0) qbounds[tile] = int4{a, b, c, d};
-    qpos_pad[r0 + tid] = qp;
-    qlo_pad[r0 + tid] = ql;
+    qlo_pad[r0 + tid] = ok ? ql : INT_MIN;
+    qspan_pad[r0 + tid] = ok ? (int)((unsigned)qp - (unsigned)ql) : 0;
   }
-  if (tid < 64) {
-    const bool ok = tid < nval;
-    const long long idx = (long long)bh * p.sq + r0 + tid;
-    lse2[(long long)bh * p.sq_pad + r0 + tid] = ok ? lse[idx] * kLog2e : 0.f;
-    dlt[(long long)bh * p.sq_pad + r0 + tid] = ok ? delta[idx] : 0.f;
-  }
-  __shared__ __bf16 s[2][kQT][D + 8];
-  const int b = bh / p.Hq, h = bh % p.Hq;
-  constexpr int CH = D / 8;
-  for (int c = tid; c < 2 * kQT * CH; c += 256) {
-    const int which = c / (kQT * CH);
-    const int cc = c % (kQT * CH);
-    const int r = cc / CH, ch = cc % CH;
-    const char* src = which ? p.dout : p.q;
-    const u32x4 raw = r < nval ? *reinterpret_cast<const u32x4*>(
-                                     src + ((long long)b * p.q_sb + (long long)h * p.q_sh + (long long)(r0 + r) * p.q_ss + ch * 8) * 2)
-                               : u32x4{0, 0, 0, 0};
-    *reinterpret_cast<u32x4*>(&s[which][r][ch * 8]) = raw;
-  }
-  __syncthreads();
-  for (int c = tid; c < 2 * D * (kQT / 8); c += 256) {
-    const int which = c / (D * (kQT / 8));
-    const int cc = c % (D * (kQT / 8));
-    const int dd = cc / (kQT / 8), qc = cc % (kQT / 8);
-    bf16x8 w;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) w[j] = s[which][qc * 8 + j][dd];
-    __bf16* out = (which ? dot : qt) + ((long long)bh * D + dd) * p.sq_pad + r0 + qc * 8;
-    *reinterpret_cast<bf16x8*>(out) = w;
-  }
+  const long long idx = (long long)bh * p.sq + r0 + tid;
+  nl2[(long long)bh * p.sq_pad + r0 + tid] = ok ? -lse[idx] * kLog2e : 0.f;
+  dlt[(long long)bh * p.sq_pad + r0 + tid] = ok ? delta[idx] : 0.f;
 }
 
 // delta_q = sum_d dO[q, d] * O[q, d]; one half-wave (32 lanes) per row.
@@ -192,35 +164,47 @@ __global__ __launch_bounds__(256) void delta_kernel(const char* __restrict__ dou
 // ============================================================================
 // dK, dV
 // ============================================================================
+// A workgroup of 8 waves owns 256 keys (32 a wave) of one K/V head and streams
+// 64-row query tiles of the group's query heads through two LDS buffers.  Per
+// 32-row half tile a wave computes S = Q K^T and dP = dO V^T (its keys as the
+// MFMA columns: K from registers, V from LDS), then P and dS, then
+// dV^T += dO^T P and dK^T += Q^T dS.  Two waves share each SIMD, so one wave's
+// exponentials run while the other's MFMAs do, and LDS reads of two waves
+// are in flight at once.
+//
+// LDS layout of a tile (and of the workgroup's V rows): 16-byte chunk c of row
+// r at c * col + 16 r, one column per chunk, columns 64 bytes apart modulo 256.
+// 16 rows of one chunk are 256 contiguous bytes (row reads) and 4 rows x 4
+// chunks fall in 16 different bank groups (transposed reads), so neither
+// pattern has bank conflicts; a 64-row tile column is exactly what one
+// LDS-direct DMA instruction writes, and every address is a per-lane pointer
+// plus an immediate.
+constexpr int kColBytes = kQT * 16 + 64;  // a column of a 64-row tile
+constexpr int kKeysPerWg = 256;
+constexpr int kVColBytes = kKeysPerWg * 16 + 64;
+
 template <int D>
 struct KvCfg {
-  static constexpr int NW = 4;
-  static constexpr int ROW = D * 2;            // bytes per row of the Q / dO tiles
-  static constexpr int CHR = D / 8;            // 16-byte chunks per such row
-  static constexpr int TROW = kQT * 2;         // bytes per row of the Q^T / dO^T tiles (128)
-  static constexpr int TCHR = kQT / 8;         // 8
-  static constexpr int RBYTES = kQT * ROW;     // a row-major tile
-  static constexpr int TBYTES = D * TROW;      // a transposed tile
-  static constexpr int RPW = RBYTES / 1024 / NW;
-  static constexpr int TPW = TBYTES / 1024 / NW;
-  static constexpr int KREG = D / 16;
-  static constexpr int DT = D / 32;
+  static constexpr int NW = 8;
+  static constexpr int CHR = D / 8;              // 16-byte chunks (columns) per row
+  static constexpr int TILE = CHR * kColBytes;   // one Q or dO tile
+  static constexpr int VTILE = CHR * kVColBytes; // the workgroup's V rows
+  static constexpr int KREG = D / 16;            // 16-wide d slices
+  static constexpr int DT = D / 32;              // 32-row blocks of dK^T / dV^T
   static constexpr int LIST = 1024;
+  static_assert(CHR % NW == 0 || NW % CHR == 0, "column split");
 };
 
 template <int D>
-__global__ __launch_bounds__(256, 1) void dkdv_kernel(BParams p) {
+__global__ __launch_bounds__(512, 1) void dkdv_kernel(BParams p) {
 #if defined(__HIP_DEVICE_COMPILE__)
   using C = KvCfg<D>;
   constexpr int NW = C::NW;
-  __shared__ __attribute__((aligned(1024))) char sQ[2][C::RBYTES];
-  __shared__ __attribute__((aligned(1024))) char sDO[2][C::RBYTES];
-  __shared__ __attribute__((aligned(1024))) char sQT[2][C::TBYTES];
-  __shared__ __attribute__((aligned(1024))) char sDOT[2][C::TBYTES];
-  __shared__ __attribute__((aligned(16))) float sL[2][kQT];
-  __shared__ __attribute__((aligned(16))) float sDl[2][kQT];
-  __shared__ __attribute__((aligned(16))) int sQp[2][kQT];
-  __shared__ __attribute__((aligned(16))) int sQl[2][kQT];
+  __shared__ __attribute__((aligned(1024))) char sQ[2][C::TILE];
+  __shared__ __attribute__((aligned(1024))) char sO[2][C::TILE];
+  __shared__ __attribute__((aligned(1024))) char sV[C::VTILE];
+  // Per row of each buffered tile: -LSE*log2(e), delta, document start, span.
+  __shared__ __attribute__((aligned(16))) float sRow[2][4][kQT];
   __shared__ int2 sList[C::LIST];
   __shared__ int sCnt[NW];
   __shared__ int sKb[NW][3];  // per wave: min key pos, max key pos, all keys valid
@@ -230,34 +214,50 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BParams p) {
   const int lane = tid & 63;
   const int l32 = lane & 31;
   const int hi = lane >> 5;
+  const int s16 = lane & 15;
   const int g = p.Hq / p.Hkv;
 
-  // ---- work item: 128 keys of rank src's shard, for one (batch, kv head) ----
-  const int t128 = (p.R + 127) / 128;  // 128-key groups per shard
+  // ---- work item: 256 keys of rank src's shard, for one (batch, kv head) ----
+  const int tg = (p.R + kKeysPerWg - 1) / kKeysPerWg;
   int logical = xcd_logical_block();
-  const int grp = logical % (p.cp * t128);
-  logical /= p.cp * t128;
+  const int grp = logical % (p.cp * tg);
+  logical /= p.cp * tg;
   const int kvh = logical % p.Hkv;
   const int b = logical / p.Hkv;
-  const int src = grp / t128;
-  const int ig = grp - src * t128;
-  const int kloc = ig * 128 + wave * 32 + l32;   // row within the shard
-  const bool kvalid = kloc < p.R;
-  const int krow = src * p.R + kloc;             // row in k_all
+  const int src = grp / tg;
+  const int ig = grp - src * tg;
+  const int key0 = src * p.R + ig * kKeysPerWg;         // first key row of the workgroup in k_all
+  const int nkeys = min(kKeysPerWg, p.R - ig * kKeysPerWg);
+  const int kloc = wave * 32 + l32;
+  const bool kvalid = kloc < nkeys;
+  const int krow = key0 + kloc;
   const int kp = kvalid ? p.k_pos[krow] : kInvalidKey;
 
-  // K and V of this lane's key as B operands (k-slots: d = 16kk + 8hi + j).
-  bf16x8 kreg[C::KREG], vreg[C::KREG];
+  // V rows of the workgroup into LDS (64 keys x one chunk per DMA instruction);
+  // rows past the shard read as zero.
+  {
+    const long long v_row_bytes = p.v_ss * 2;
+    const char* vb = p.v + ((long long)b * p.v_sb + (long long)kvh * p.v_sh + (long long)key0 * p.v_ss) * 2;
+    const __amdgpu_buffer_rsrc_t rsV =
+        __builtin_amdgcn_make_buffer_rsrc((void*)vb, 0, (int)(nkeys * v_row_bytes), kBufferFlags);
+    constexpr int NI = C::CHR * (kKeysPerWg / 64);  // DMA instructions for V
+#pragma unroll
+    for (int j = 0; j < NI / NW; ++j) {
+      const int i = wave + NW * j;
+      const int col = i / (kKeysPerWg / 64), part = i % (kKeysPerWg / 64);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsV, (lds_ptr_t)(sV + col * kVColBytes + part * 1024), 16,
+                                               (int)((part * 64 + lane) * v_row_bytes), col * 16, 0, 0);
+    }
+  }
+
+  // K of this lane's key as the B operand of S (k-slots: d = 16kk + 8hi + j).
+  bf16x8 kreg[C::KREG];
   {
     const char* kr = p.k + ((long long)b * p.k_sb + (long long)kvh * p.k_sh + (long long)krow * p.k_ss) * 2;
-    const char* vr = p.v + ((long long)b * p.v_sb + (long long)kvh * p.v_sh + (long long)krow * p.v_ss) * 2;
 #pragma unroll
-    for (int kk = 0; kk < C::KREG; ++kk) {
+    for (int kk = 0; kk < C::KREG; ++kk)
       kreg[kk] = __builtin_bit_cast(bf16x8, kvalid ? *reinterpret_cast<const u32x4*>(kr + (16 * kk + 8 * hi) * 2)
                                                    : u32x4{0, 0, 0, 0});
-      vreg[kk] = __builtin_bit_cast(bf16x8, kvalid ? *reinterpret_cast<const u32x4*>(vr + (16 * kk + 8 * hi) * 2)
-                                                   : u32x4{0, 0, 0, 0});
-    }
   }
   {
     const int a = wave_min(kvalid ? kp : INT_MAX);
@@ -269,36 +269,26 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BParams p) {
       sKb[wave][2] = all_valid ? 1 : 0;
     }
   }
-  __syncthreads();
+  __syncthreads();  // the list builder reads every wave's key bounds
 
-  // ---- per-lane constant addresses ----------------------------------------
-  int voffR[C::RPW], voffT[C::TPW];
+  // ---- per-lane constant offsets ----------------------------------------
   const long long q_row_bytes = p.q_ss * 2;
-  const long long t_row_bytes = (long long)p.sq_pad * 2;
-#pragma unroll
-  for (int j = 0; j < C::RPW; ++j) {
-    const int c = (wave + NW * j) * 64 + lane;
-    const int r = c / C::CHR, ph = c % C::CHR;
-    voffR[j] = (int)(r * q_row_bytes) + 16 * swz<C::CHR>(r, ph);
-  }
-#pragma unroll
-  for (int j = 0; j < C::TPW; ++j) {
-    const int c = (wave + NW * j) * 64 + lane;
-    const int r = c / C::TCHR, ph = c % C::TCHR;
-    voffT[j] = (int)(r * t_row_bytes) + 16 * swz<C::TCHR>(r, ph);
-  }
-  const int qrow = key_perm(l32);  // A-operand row of the row-major tiles
-  int raddr[C::KREG];
-#pragma unroll
-  for (int kk = 0; kk < C::KREG; ++kk) raddr[kk] = qrow * C::ROW + 16 * swz<C::CHR>(qrow, 2 * kk + hi);
-  int taddr[4];
-#pragma unroll
-  for (int kg = 0; kg < 4; ++kg) taddr[kg] = l32 * C::TROW + 16 * swz<C::TCHR>(l32, 2 * kg + hi);
+  const int voff = (int)(lane * q_row_bytes);  // DMA: lane l copies row l of a tile column
+  // Row reads (A of S = Q K^T and dP = dO V^T): row key_perm(l32) (+32 sub) at
+  // chunk 2kk + hi: nbase + kk * 2 kColBytes + sub * 512.
+  const int nbase = hi * kColBytes + key_perm(l32) * 16;
+  // V operand (B of dP): this lane's key at chunk 2kk + hi.
+  const int vbase = hi * kVColBytes + kloc * 16;
+  // Transposed reads (A of dV^T += dO^T P, dK^T += Q^T dS): lane s16 of its
+  // 16-lane group reads row 8hi + 4h + s16/4 (+16gg + 32sub) at column 32t +
+  // 16*(bit 4 of lane) + 4*(s16%4): tbase + t * 4 kColBytes + h * 64 + gg * 256
+  // + sub * 512; the lane then holds column 32t + l32 at rows 8hi + 4h + 0..3.
+  const int tbase = (2 * ((lane >> 4) & 1) + ((s16 & 3) >> 1)) * kColBytes + (8 * hi + (s16 >> 2)) * 16 + 8 * (s16 & 1);
 
   // ---- list of (query head, query tile) pairs this workgroup needs ---------
-  // Slot u = hg * nqt + t.  Class per wave from the tile bounds and the wave's
-  // key bounds: skip when no key of the wave lies in [min lo, max pos], full
-  // when every key lies in [max lo, min pos] for every row.
+  // Entry .x = t | hg << 16 for tile t of query head kvh*g + hg; .y = class of
+  // wave w << 2w: skip when no key of the wave lies in [min lo, max pos] of the
+  // tile, full when every key lies in [max lo, min pos] and the tile is whole.
   auto build = [&](int u0, int u1) {
     int cnt = 0;
     for (int base = u0; base < u1; base += NW * 64) {
@@ -306,10 +296,11 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BParams p) {
       bool act = false;
       int2 entry = {0, 0};
       if (u < u1) {
-        const int t = u % p.nqt;
+        const int hg = u / p.nqt;
+        const int t = u - hg * p.nqt;
         const int4 qb = p.qbounds[t];
         const bool tile_full = (t + 1) * kQT <= p.sq;
-        entry.x = u;
+        entry.x = t | (hg << 16);
         unsigned bits = 0;
 #pragma unroll
         for (int w = 0; w < NW; ++w) {
@@ -349,129 +340,156 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BParams p) {
       dka[t][r] = 0.f;
     }
 
-  const __amdgpu_buffer_rsrc_t rsL = __builtin_amdgcn_make_buffer_rsrc((void*)p.lse2, 0, 0x7fffffff, kBufferFlags);
-  const __amdgpu_buffer_rsrc_t rsD = __builtin_amdgcn_make_buffer_rsrc((void*)p.dlt, 0, 0x7fffffff, kBufferFlags);
-  const __amdgpu_buffer_rsrc_t rsQp = __builtin_amdgcn_make_buffer_rsrc((void*)p.qpos_pad, 0, 0x7fffffff, kBufferFlags);
-  const __amdgpu_buffer_rsrc_t rsQl = __builtin_amdgcn_make_buffer_rsrc((void*)p.qlo_pad, 0, 0x7fffffff, kBufferFlags);
-
-  // Copies query tile (head h, tile t) into buffer `buf`.
-  auto issue = [&](int buf, int e) __attribute__((always_inline)) {
-    const int hg = e / p.nqt, t = e - (e / p.nqt) * p.nqt;
+  // Copies query tile ex (t | hg << 16) into buffer buf: the columns of the Q
+  // and dO tiles split over the waves; waves 0..3 each copy one per-row array.
+  auto issue = [&](int buf, int ex) {
+    const int t = ex & 0xFFFF, hg = ex >> 16;
     const int h = kvh * g + hg;
     const int r0 = t * kQT;
     const int nval = min(kQT, p.sq - r0);
     const long long bh = (long long)b * p.Hq + h;
-    const __amdgpu_buffer_rsrc_t rsQ = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(p.q + ((long long)b * p.q_sb + (long long)h * p.q_sh + (long long)r0 * p.q_ss) * 2), 0,
-        (int)(nval * q_row_bytes), kBufferFlags);
-    const __amdgpu_buffer_rsrc_t rsO = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(p.dout + ((long long)b * p.q_sb + (long long)h * p.q_sh + (long long)r0 * p.q_ss) * 2), 0,
-        (int)(nval * q_row_bytes), kBufferFlags);
-    const __amdgpu_buffer_rsrc_t rsQT = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(p.qt + (bh * D * p.sq_pad + r0) * 2), 0, (int)(D * t_row_bytes), kBufferFlags);
-    const __amdgpu_buffer_rsrc_t rsOT = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(p.dot + (bh * D * p.sq_pad + r0) * 2), 0, (int)(D * t_row_bytes), kBufferFlags);
+    const long long qoff = ((long long)b * p.q_sb + (long long)h * p.q_sh + (long long)r0 * p.q_ss) * 2;
+    const __amdgpu_buffer_rsrc_t rsQ =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(p.q + qoff), 0, (int)(nval * q_row_bytes), kBufferFlags);
+    const __amdgpu_buffer_rsrc_t rsO =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(p.dout + qoff), 0, (int)(nval * q_row_bytes), kBufferFlags);
+    // 2*CHR column copies (Q then dO) over NW waves.
 #pragma unroll
-    for (int j = 0; j < C::RPW; ++j) {
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsQ, (lds_ptr_t)(&sQ[buf][0] + (wave + NW * j) * 1024), 16, voffR[j], 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsO, (lds_ptr_t)(&sDO[buf][0] + (wave + NW * j) * 1024), 16, voffR[j], 0, 0, 0);
+    for (int j = 0; j < (2 * C::CHR) / NW; ++j) {
+      const int i = wave + NW * j;
+      const int col = i % C::CHR;
+      if (i < C::CHR)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsQ, (lds_ptr_t)(&sQ[buf][0] + col * kColBytes), 16, voff, col * 16,
+                                                 0, 0);
+      else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsO, (lds_ptr_t)(&sO[buf][0] + col * kColBytes), 16, voff, col * 16,
+                                                 0, 0);
     }
-#pragma unroll
-    for (int j = 0; j < C::TPW; ++j) {
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsQT, (lds_ptr_t)(&sQT[buf][0] + (wave + NW * j) * 1024), 16, voffT[j], 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsOT, (lds_ptr_t)(&sDOT[buf][0] + (wave + NW * j) * 1024), 16, voffT[j], 0, 0, 0);
-    }
-    if (wave == 0) {
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsL, (lds_ptr_t)&sL[buf][0], 4, lane * 4, (int)((bh * p.sq_pad + r0) * 4), 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsD, (lds_ptr_t)&sDl[buf][0], 4, lane * 4, (int)((bh * p.sq_pad + r0) * 4), 0, 0);
-    } else if (wave == 1) {
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsQp, (lds_ptr_t)&sQp[buf][0], 4, lane * 4, r0 * 4, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsQl, (lds_ptr_t)&sQl[buf][0], 4, lane * 4, r0 * 4, 0, 0);
+    if (wave < 4) {
+      const void* arr = wave == 0 ? (const void*)p.nl2 : wave == 1 ? (const void*)p.dlt
+                      : wave == 2 ? (const void*)p.qlo_pad : (const void*)p.qspan_pad;
+      const int soff = (int)((wave < 2 ? bh * p.sq_pad + r0 : (long long)r0) * 4);
+      const __amdgpu_buffer_rsrc_t rsR = __builtin_amdgcn_make_buffer_rsrc((void*)arr, 0, 0x7fffffff, kBufferFlags);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsR, (lds_ptr_t)&sRow[buf][wave][0], 4, lane * 4, soff, 0, 0);
     }
   };
 
-  auto compute = [&](int buf, int cls) __attribute__((always_inline)) {
-    if (cls == kSkip) return;
-    const char* q_t = &sQ[buf][0];
-    const char* do_t = &sDO[buf][0];
-    const char* qt_t = &sQT[buf][0];
-    const char* dot_t = &sDOT[buf][0];
-#pragma unroll
-    for (int sub = 0; sub < 2; ++sub) {
-      // S = Q K^T and dP = dO V^T for 32 query rows (register r: row 32*sub + 16*(r/8) + 8*hi + r%8)
-      f32x16 s, dp;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        s[r] = 0.f;
-        dp[r] = 0.f;
-      }
-#pragma unroll
-      for (int kk = 0; kk < C::KREG; ++kk) {
-        const bf16x8 aq = *reinterpret_cast<const bf16x8*>(q_t + raddr[kk] + sub * 32 * C::ROW);
-        const bf16x8 ao = *reinterpret_cast<const bf16x8*>(do_t + raddr[kk] + sub * 32 * C::ROW);
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, kreg[kk], s, 0, 0, 0);
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ao, vreg[kk], dp, 0, 0, 0);
-      }
-      bf16x8 pb[2], db[2];
-#pragma unroll
-      for (int gg = 0; gg < 2; ++gg) {
-        const int q0 = 32 * sub + 16 * gg + 8 * hi;
-        const f32x4 l0 = *reinterpret_cast<const f32x4*>(&sL[buf][q0]);
-        const f32x4 l1 = *reinterpret_cast<const f32x4*>(&sL[buf][q0 + 4]);
-        const f32x4 d0 = *reinterpret_cast<const f32x4*>(&sDl[buf][q0]);
-        const f32x4 d1 = *reinterpret_cast<const f32x4*>(&sDl[buf][q0 + 4]);
-        const float lv[8] = {l0[0], l0[1], l0[2], l0[3], l1[0], l1[1], l1[2], l1[3]};
-        const float dl[8] = {d0[0], d0[1], d0[2], d0[3], d1[0], d1[1], d1[2], d1[3]};
-        bool ok[8];
-        if (cls == kPartial) {
-          const int4 p0 = *reinterpret_cast<const int4*>(&sQp[buf][q0]);
-          const int4 p1 = *reinterpret_cast<const int4*>(&sQp[buf][q0 + 4]);
-          const int4 o0 = *reinterpret_cast<const int4*>(&sQl[buf][q0]);
-          const int4 o1 = *reinterpret_cast<const int4*>(&sQl[buf][q0 + 4]);
-          const int qpv[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
-          const int qlv[8] = {o0.x, o0.y, o0.z, o0.w, o1.x, o1.y, o1.z, o1.w};
-#pragma unroll
-          for (int j = 0; j < 8; ++j) ok[j] = kp >= qlv[j] && kp <= qpv[j];
-        } else {
-#pragma unroll
-          for (int j = 0; j < 8; ++j) ok[j] = true;
-        }
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int r = 8 * gg + j;
-          const float pr = ok[j] ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], p.c2, -lv[j])) : 0.f;
-          const float ds = pr * (dp[r] - dl[j]);
-          pb[gg][j] = (__bf16)pr;
-          db[gg][j] = (__bf16)ds;
-        }
-      }
-      // dV^T += dO^T P and dK^T += Q^T dS over this sub-tile's 32 query rows
-#pragma unroll
-      for (int gg = 0; gg < 2; ++gg) {
-        const int kg = 2 * sub + gg;
-#pragma unroll
-        for (int t = 0; t < C::DT; ++t) {
-          const bf16x8 ao = *reinterpret_cast<const bf16x8*>(dot_t + taddr[kg] + t * 32 * C::TROW);
-          const bf16x8 aq = *reinterpret_cast<const bf16x8*>(qt_t + taddr[kg] + t * 32 * C::TROW);
-          dva[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ao, pb[gg], dva[t], 0, 0, 0);
-          dka[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, db[gg], dka[t], 0, 0, 0);
-        }
-      }
-    }
+  // Lane pointers pass through an empty asm where they are formed so that
+  // pointer + constant is not hoisted out of the loop as one register per
+  // read: every read is then one of these pointers plus a DS offset immediate.
+  auto launder = [](const lds_char* ptr) {
+    asm volatile("" : "+v"(ptr));
+    return ptr;
   };
 
+  // One half tile (sub) of the tile in buffer buf: S/dP, P/dS, dV/dK.  Key kp
+  // is allowed for a row iff kp - lo <= span as unsigned numbers (span = pos -
+  // lo; padding rows have zero Q and dO rows and add nothing).  The test runs
+  // on every tile: one code path keeps the accumulators in place, where a
+  // second (unmasked) copy of the MFMAs made the compiler shuttle them between
+  // register sets.
+  auto half = [&](int buf, int sub) {
+    const lds_char* qn = launder(to_lds(&sQ[0][0]) + buf * C::TILE + nbase + sub * 512);
+    const lds_char* on = launder(to_lds(&sO[0][0]) + buf * C::TILE + nbase + sub * 512);
+    const lds_char* vn = launder(to_lds(sV) + vbase);
+    // S = Q K^T, dP = dO V^T: register r is query row 32sub + 16(r/8) + 8hi + r%8.
+    f32x16 s, dp;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      s[r] = 0.f;
+      dp[r] = 0.f;
+    }
+    // Operands are read one d-slice ahead; the fences keep the compiler from
+    // hoisting every read of the half tile (and spilling).
+    bf16x8 aq[2], ao[2], bv[2];
+    aq[0] = lds_read8(qn);
+    ao[0] = lds_read8(on);
+    bv[0] = lds_read8(vn);
+#pragma unroll
+    for (int kk = 0; kk < C::KREG; ++kk) {
+      if (kk + 1 < C::KREG) {
+        aq[(kk + 1) & 1] = lds_read8(qn + (kk + 1) * 2 * kColBytes);
+        ao[(kk + 1) & 1] = lds_read8(on + (kk + 1) * 2 * kColBytes);
+        bv[(kk + 1) & 1] = lds_read8(vn + (kk + 1) * 2 * kVColBytes);
+      }
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq[kk & 1], kreg[kk], s, 0, 0, 0);
+      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ao[kk & 1], bv[kk & 1], dp, 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // P = exp2(c2 s - LSE log2 e) on allowed pairs, dS = P (dP - delta).
+    const lds_char* rowb = launder(to_lds(&sRow[0][0][0]) + (buf * 4 * kQT + 32 * sub + 8 * hi) * 4);
+    bf16x8 pb[2], db[2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {  // values 4i..4i+3: rows 16(i/2) + 4(i%2) + 0..3 of the lane's 8
+      const int ro = (16 * (i >> 1) + 4 * (i & 1)) * 4;
+      const f32x4 nl = *(const __attribute__((address_space(3))) f32x4*)(rowb + ro);
+      const f32x4 dl = *(const __attribute__((address_space(3))) f32x4*)(rowb + kQT * 4 + ro);
+      // Integer arrays are read as integer vectors: a bit_cast of one element
+      // of a float vector is avoided (clang has been seen to read element 0
+      // for it whatever the index).
+      const u32x4 lo = *(const __attribute__((address_space(3))) u32x4*)(rowb + 2 * kQT * 4 + ro);
+      const u32x4 sp = *(const __attribute__((address_space(3))) u32x4*)(rowb + 3 * kQT * 4 + ro);
+      float pr[4], ds[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int x = 4 * i + e;
+        pr[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[x], p.c2, nl[e]));
+        pr[e] = ((unsigned)kp - lo[e] <= sp[e]) ? pr[e] : 0.f;
+        ds[e] = pr[e] * (dp[x] - dl[e]);
+      }
+#pragma unroll
+      for (int e = 0; e < 4; e += 2) {
+        const bf16x2 pp = __builtin_convertvector((f32x2){pr[e], pr[e + 1]}, bf16x2);
+        const bf16x2 dd = __builtin_convertvector((f32x2){ds[e], ds[e + 1]}, bf16x2);
+        const int j = 4 * (i & 1) + e;
+        pb[i >> 1][j] = pp[0];
+        pb[i >> 1][j + 1] = pp[1];
+        db[i >> 1][j] = dd[0];
+        db[i >> 1][j + 1] = dd[1];
+      }
+    }
+    // dV^T += dO^T P, dK^T += Q^T dS over the half tile's 32 query rows.
+    const lds_char* qt = launder(to_lds(&sQ[0][0]) + buf * C::TILE + tbase + sub * 512);
+    const lds_char* ot = launder(to_lds(&sO[0][0]) + buf * C::TILE + tbase + sub * 512);
+    constexpr int NG = 2 * C::DT;  // (gg, t) pairs
+    auto toff = [](int m) { return (m % C::DT) * 4 * kColBytes + (m / C::DT) * 256; };
+    bf16x8 to[2], tq[2];
+    to[0] = lds_read_tr(ot, ot + 64);
+    tq[0] = lds_read_tr(qt, qt + 64);
+#pragma unroll
+    for (int m = 0; m < NG; ++m) {
+      if (m + 1 < NG) {
+        const int o = toff(m + 1);
+        to[(m + 1) & 1] = lds_read_tr(ot + o, ot + o + 64);
+        tq[(m + 1) & 1] = lds_read_tr(qt + o, qt + o + 64);
+      }
+      const int t = m % C::DT, gg = m / C::DT;
+      dva[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(to[m & 1], pb[gg], dva[t], 0, 0, 0);
+      dka[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tq[m & 1], db[gg], dka[t], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
   const int total = g * p.nqt;
   const int csh = 2 * wave;
   for (int u0 = 0; u0 < total; u0 += C::LIST) {
     const int cnt = build(u0, min(total, u0 + C::LIST));
     if (cnt == 0) continue;
-    issue(0, __builtin_amdgcn_readfirstlane(sList[0].x));
+    auto ent = [&](int j) {
+      int2 e;
+      e.x = __builtin_amdgcn_readfirstlane(sList[j].x);
+      e.y = __builtin_amdgcn_readfirstlane(sList[j].y);
+      return e;
+    };
+    issue(0, ent(0).x);
     wait_vmem();
     __syncthreads();
     for (int j = 0; j < cnt; ++j) {
-      const int cur = j & 1;
-      if (j + 1 < cnt) issue(cur ^ 1, __builtin_amdgcn_readfirstlane(sList[j + 1].x));
-      compute(cur, (int)(((unsigned)__builtin_amdgcn_readfirstlane(sList[j].y) >> csh) & 3));
+      const int buf = j & 1;
+      if (j + 1 < cnt) issue(buf ^ 1, ent(j + 1).x);
+      if ((((unsigned)ent(j).y >> csh) & 3) != kSkip) {
+#pragma nounroll
+        for (int sub = 0; sub < 2; ++sub) half(buf, sub);
+      }
       wait_vmem();
       __syncthreads();
     }
@@ -568,7 +586,7 @@ __global__ __launch_bounds__(512, 1) void dq_kernel(BParams p) {
   }
   const int qp = valid ? p.q_pos[row] : -1;
   const int ql = valid ? (p.q_lo ? p.q_lo[row] : 0) : INT_MAX;
-  const float lse2 = valid ? p.lse2[bh * p.sq_pad + row] : 0.f;
+  const float nl2 = valid ? p.nl2[bh * p.sq_pad + row] : 0.f;
   const float dl = valid ? p.dlt[bh * p.sq_pad + row] : 0.f;
   {
     const int a = wave_min(valid ? qp : INT_MAX), bb = wave_max(valid ? qp : INT_MIN);
@@ -681,7 +699,7 @@ __global__ __launch_bounds__(512, 1) void dq_kernel(BParams p) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           const int r = 8 * gg + j;
-          const float pr = ok[j] ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], p.c2, -lse2)) : 0.f;
+          const float pr = ok[j] ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], p.c2, nl2)) : 0.f;
           db[gg][j] = (__bf16)(pr * (dp[r] - dl));
         }
       }
@@ -748,12 +766,10 @@ hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
   p.kpos_pad = reinterpret_cast<const int*>(ws + w.kpos_off);
   p.kt = ws + w.kt_off;
   p.qbounds = reinterpret_cast<const int4*>(ws + w.qbounds_off);
-  p.qpos_pad = reinterpret_cast<const int*>(ws + w.qpos_off);
   p.qlo_pad = reinterpret_cast<const int*>(ws + w.qlo_off);
-  p.lse2 = reinterpret_cast<const float*>(ws + w.lse2_off);
+  p.qspan_pad = reinterpret_cast<const int*>(ws + w.qspan_off);
+  p.nl2 = reinterpret_cast<const float*>(ws + w.nl2_off);
   p.dlt = reinterpret_cast<const float*>(ws + w.dlt_off);
-  p.qt = ws + w.qt_off;
-  p.dot = ws + w.dot_off;
   p.dq = a.dq;
   p.dk = a.dk;
   p.dv = a.dv;
@@ -787,16 +803,15 @@ hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
                        reinterpret_cast<__bf16*>(ws + w.kt_off));
     if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((query_prep_kernel<D>), dim3(p.nqt, a.b * a.hq), dim3(256), 0, stream, p, a.lse, a.delta,
-                     reinterpret_cast<int4*>(ws + w.qbounds_off), reinterpret_cast<int*>(ws + w.qpos_off),
-                     reinterpret_cast<int*>(ws + w.qlo_off), reinterpret_cast<float*>(ws + w.lse2_off),
-                     reinterpret_cast<float*>(ws + w.dlt_off), reinterpret_cast<__bf16*>(ws + w.qt_off),
-                     reinterpret_cast<__bf16*>(ws + w.dot_off));
+  hipLaunchKernelGGL(query_prep_kernel, dim3(p.nqt, a.b * a.hq), dim3(64), 0, stream, p, a.lse, a.delta,
+                     reinterpret_cast<int4*>(ws + w.qbounds_off), reinterpret_cast<int*>(ws + w.qlo_off),
+                     reinterpret_cast<int*>(ws + w.qspan_off), reinterpret_cast<float*>(ws + w.nl2_off),
+                     reinterpret_cast<float*>(ws + w.dlt_off));
   if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
   if (ntiles == 0) return hipSuccess;
-  const int t128 = (a.rows_per_rank + 127) / 128;
-  const long long nkv = (long long)a.cp * t128 * a.hkv * a.b;
-  hipLaunchKernelGGL((dkdv_kernel<D>), dim3((unsigned)nkv), dim3(256), 0, stream, p);
+  const int tg = (a.rows_per_rank + kKeysPerWg - 1) / kKeysPerWg;
+  const long long nkv = (long long)a.cp * tg * a.hkv * a.b;
+  hipLaunchKernelGGL((dkdv_kernel<D>), dim3((unsigned)nkv), dim3(512), 0, stream, p);
   if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
   const int nqt256 = (a.sq + 255) / 256;
   const long long nq = (long long)nqt256 * a.hq * a.b;

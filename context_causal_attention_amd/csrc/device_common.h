@@ -35,6 +35,38 @@ __device__ __forceinline__ int swz(int row, int chunk) {
   else return chunk ^ ((row >> 1) & 7);
 }
 
+// Swizzle for tiles that are read both along rows (ds_read_b128 of 16 lanes
+// covering 16 consecutive rows at one chunk) and transposed (ds_read_b64_tr_b16:
+// each 16-lane group covers 4 consecutive rows x 4 consecutive chunks).  Rows
+// r..r+3 land in four different aligned groups of four chunks, and 16
+// consecutive rows at one chunk in 16 different chunks (C = 16) or in the two
+// 128-byte halves times 8 chunks (C = 8), so both patterns are conflict free.
+template <int C>
+__device__ __forceinline__ int swz_t(int row, int chunk) {
+  if constexpr (C >= 16) return chunk ^ (((row & 3) << 2) | ((row >> 2) & 3));
+  else return chunk ^ ((((row >> 1) & 1) << 2) | ((row >> 2) & 3));
+}
+
+// ds_read_b64_tr_b16: within each group of 16 lanes, lane l receives element
+// l % 4 of the 8-byte reads of lanes l / 4 + 4j, j = 0..3.  If lane s of the
+// group reads row k0 + s / 4 at column n0 + 4 (s % 4), lane l therefore gets
+// column n0 + l at rows k0..k0+3: the k-major layout of an MFMA operand read
+// from a row-major tile whose rows run along k.
+// Address arithmetic on LDS-space pointers lets the compiler fold constant
+// offsets into the DS instructions' offset field.
+typedef __attribute__((address_space(3))) char lds_char;
+typedef __bf16 bf16x4 __attribute__((__vector_size__(4 * sizeof(__bf16))));
+__device__ __forceinline__ lds_char* to_lds(void* p) { return (lds_char*)p; }
+__device__ __forceinline__ bf16x8 lds_read8(const lds_char* p) {
+  return *(const __attribute__((address_space(3))) bf16x8*)p;
+}
+__device__ __forceinline__ bf16x8 lds_read_tr(const lds_char* lo, const lds_char* hi) {
+  typedef __attribute__((address_space(3))) bf16x4* lp;
+  const bf16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lp)(lo));
+  const bf16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lp)(hi));
+  return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
 // Row order of a 32x32 MFMA operand that makes each lane's 8 consecutive
 // accumulator registers cover 8 consecutive rows: bits 2 and 3 of the row
 // index swapped.  With the 32x32 accumulator layout (register r of lane half h
