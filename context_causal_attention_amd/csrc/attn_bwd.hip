@@ -399,8 +399,7 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(BParams p) {
       s[r] = 0.f;
       dp[r] = 0.f;
     }
-    // Operands are read one d-slice ahead; the fences keep the compiler from
-    // hoisting every read of the half tile (and spilling).
+    // Operands are read one d-slice ahead.
     bf16x8 aq[2], ao[2], bv[2];
     aq[0] = lds_read8(qn);
     ao[0] = lds_read8(on);
@@ -414,7 +413,6 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(BParams p) {
       }
       s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq[kk & 1], kreg[kk], s, 0, 0, 0);
       dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ao[kk & 1], bv[kk & 1], dp, 0, 0, 0);
-      __builtin_amdgcn_sched_barrier(0);
     }
     // P = exp2(c2 s - LSE log2 e) on allowed pairs, dS = P (dP - delta).
     const lds_char* rowb = launder(to_lds(&sRow[0][0][0]) + (buf * 4 * kQT + 32 * sub + 8 * hi) * 4);
@@ -466,7 +464,6 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(BParams p) {
       const int t = m % C::DT, gg = m / C::DT;
       dva[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(to[m & 1], pb[gg], dva[t], 0, 0, 0);
       dka[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tq[m & 1], db[gg], dka[t], 0, 0, 0);
-      __builtin_amdgcn_sched_barrier(0);
     }
   };
   const int total = g * p.nqt;
