@@ -382,13 +382,11 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(BParams p) {
     return ptr;
   };
 
-  // One half tile (sub) of the tile in buffer buf: S/dP, P/dS, dV/dK.  Key kp
-  // is allowed for a row iff kp - lo <= span as unsigned numbers (span = pos -
-  // lo; padding rows have zero Q and dO rows and add nothing).  The test runs
-  // on every tile: one code path keeps the accumulators in place, where a
-  // second (unmasked) copy of the MFMAs made the compiler shuttle them between
-  // register sets.
-  auto half = [&](int buf, int sub) {
+  // One half tile (sub) of the tile in buffer buf: S/dP, P/dS, dV/dK.  On
+  // partial tiles key kp is allowed for a row iff kp - lo <= span as unsigned
+  // numbers (span = pos - lo; padding rows have zero Q and dO rows and add
+  // nothing); full tiles skip the test.
+  auto half = [&](int buf, int sub, bool full) {
     const lds_char* qn = launder(to_lds(&sQ[0][0]) + buf * C::TILE + nbase + sub * 512);
     const lds_char* on = launder(to_lds(&sO[0][0]) + buf * C::TILE + nbase + sub * 512);
     const lds_char* vn = launder(to_lds(sV) + vbase);
@@ -414,38 +412,48 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(BParams p) {
       s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq[kk & 1], kreg[kk], s, 0, 0, 0);
       dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ao[kk & 1], bv[kk & 1], dp, 0, 0, 0);
     }
-    // P = exp2(c2 s - LSE log2 e) on allowed pairs, dS = P (dP - delta).
+    // P = exp2(c2 s - LSE log2 e) on allowed pairs, dS = P (dP - delta).  Only
+    // this vector part differs between partial and full tiles; the MFMAs around
+    // it exist once, so their accumulators stay in place.
     const lds_char* rowb = launder(to_lds(&sRow[0][0][0]) + (buf * 4 * kQT + 32 * sub + 8 * hi) * 4);
     bf16x8 pb[2], db[2];
+    auto probs = [&](auto maskc) {
+      constexpr bool MASKED = decltype(maskc)::value;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {  // values 4i..4i+3: rows 16(i/2) + 4(i%2) + 0..3 of the lane's 8
-      const int ro = (16 * (i >> 1) + 4 * (i & 1)) * 4;
-      const f32x4 nl = *(const __attribute__((address_space(3))) f32x4*)(rowb + ro);
-      const f32x4 dl = *(const __attribute__((address_space(3))) f32x4*)(rowb + kQT * 4 + ro);
-      // Integer arrays are read as integer vectors: a bit_cast of one element
-      // of a float vector is avoided (clang has been seen to read element 0
-      // for it whatever the index).
-      const u32x4 lo = *(const __attribute__((address_space(3))) u32x4*)(rowb + 2 * kQT * 4 + ro);
-      const u32x4 sp = *(const __attribute__((address_space(3))) u32x4*)(rowb + 3 * kQT * 4 + ro);
-      float pr[4], ds[4];
+      for (int i = 0; i < 4; ++i) {  // values 4i..4i+3: rows 16(i/2) + 4(i%2) + 0..3 of the lane's 8
+        const int ro = (16 * (i >> 1) + 4 * (i & 1)) * 4;
+        const f32x4 nl = *(const __attribute__((address_space(3))) f32x4*)(rowb + ro);
+        const f32x4 dl = *(const __attribute__((address_space(3))) f32x4*)(rowb + kQT * 4 + ro);
+        // Integer arrays are read as integer vectors: a bit_cast of one element
+        // of a float vector is avoided (clang has been seen to read element 0
+        // for it whatever the index).
+        u32x4 lo = {0, 0, 0, 0}, sp = {0, 0, 0, 0};
+        if (MASKED) {
+          lo = *(const __attribute__((address_space(3))) u32x4*)(rowb + 2 * kQT * 4 + ro);
+          sp = *(const __attribute__((address_space(3))) u32x4*)(rowb + 3 * kQT * 4 + ro);
+        }
+        float pr[4], ds[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int x = 4 * i + e;
-        pr[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[x], p.c2, nl[e]));
-        pr[e] = ((unsigned)kp - lo[e] <= sp[e]) ? pr[e] : 0.f;
-        ds[e] = pr[e] * (dp[x] - dl[e]);
+        for (int e = 0; e < 4; ++e) {
+          const int x = 4 * i + e;
+          pr[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[x], p.c2, nl[e]));
+          if (MASKED) pr[e] = ((unsigned)kp - lo[e] <= sp[e]) ? pr[e] : 0.f;
+          ds[e] = pr[e] * (dp[x] - dl[e]);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; e += 2) {
+          const bf16x2 pp = __builtin_convertvector((f32x2){pr[e], pr[e + 1]}, bf16x2);
+          const bf16x2 dd = __builtin_convertvector((f32x2){ds[e], ds[e + 1]}, bf16x2);
+          const int j = 4 * (i & 1) + e;
+          pb[i >> 1][j] = pp[0];
+          pb[i >> 1][j + 1] = pp[1];
+          db[i >> 1][j] = dd[0];
+          db[i >> 1][j + 1] = dd[1];
+        }
       }
-#pragma unroll
-      for (int e = 0; e < 4; e += 2) {
-        const bf16x2 pp = __builtin_convertvector((f32x2){pr[e], pr[e + 1]}, bf16x2);
-        const bf16x2 dd = __builtin_convertvector((f32x2){ds[e], ds[e + 1]}, bf16x2);
-        const int j = 4 * (i & 1) + e;
-        pb[i >> 1][j] = pp[0];
-        pb[i >> 1][j + 1] = pp[1];
-        db[i >> 1][j] = dd[0];
-        db[i >> 1][j + 1] = dd[1];
-      }
-    }
+    };
+    if (full) probs(std::integral_constant<bool, false>{});
+    else probs(std::integral_constant<bool, true>{});
     // dV^T += dO^T P, dK^T += Q^T dS over the half tile's 32 query rows.
     const lds_char* qt = launder(to_lds(&sQ[0][0]) + buf * C::TILE + tbase + sub * 512);
     const lds_char* ot = launder(to_lds(&sO[0][0]) + buf * C::TILE + tbase + sub * 512);
@@ -483,9 +491,10 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(BParams p) {
     for (int j = 0; j < cnt; ++j) {
       const int buf = j & 1;
       if (j + 1 < cnt) issue(buf ^ 1, ent(j + 1).x);
-      if ((((unsigned)ent(j).y >> csh) & 3) != kSkip) {
+      const int cls = (int)(((unsigned)ent(j).y >> csh) & 3);
+      if (cls != kSkip) {
 #pragma nounroll
-        for (int sub = 0; sub < 2; ++sub) half(buf, sub);
+        for (int sub = 0; sub < 2; ++sub) half(buf, sub, cls == kFull);
       }
       wait_vmem();
       __syncthreads();
