@@ -89,6 +89,45 @@ def test_ring_bwd_32k_cp8_per_rank(rank):
         assert torch.isfinite(t).all()
 
 
+@pytest.mark.parametrize("rank", [0, 7])
+def test_ring_bwd_128k_cp8_sampled(rank):
+    """The backward at the bench workload's size (131072 tokens, cp=8, 32q/8kv
+    heads, d=128, bf16), in the launch configuration the bench times.
+    dQ: sampled rows of the rank, all heads, against the oracle's gradient of
+    those rows' loss terms (row i's dQ depends on its own term only).
+    dK, dV: the last 128 keys of the rank's second chunk are attended, among the
+    rank's rows, only by its last 128 rows, so the oracle restricted to those
+    rows gives their gradients exactly; checked for kv heads 0 and 7."""
+    w = si.WORKLOADS["llama8b_s128k_cp8"]
+    full = si.make_qkv(w.B, w.Hq, w.Hkv, w.S, w.d, "bf16", seed=w.seed, with_dout=True)
+    announce(f"ring bwd 128k cp8 rank {rank}")
+    R = Rank(w.B, w.Hq, w.Hkv, w.S, w.d, w.cp, rank, "bf16", full=full)
+    _, _, dq, dk, dv = R.ring_bwd()
+    torch.cuda.synchronize()
+    for t in (dq, dk, dv):
+        assert torch.isfinite(t).all()
+    q64, k64, v64, do64 = (t.double().numpy() for t in full)
+    n = w.S // w.cp
+    c = n // 2
+    rng = np.random.default_rng(2)
+    idx = np.unique(np.concatenate([[0, c - 1, c, n - 1], rng.integers(0, n, 6)]))
+    rows = R.pos[idx]
+    dq_ref, _, _ = orc.attention_bwd(q64, k64, v64, do64[:, :, rows], R.scale, rows=rows)
+    e = max_err(dq[:, :, idx], dq_ref)
+    assert e <= GTOL, f"dq on sampled rows: max-abs error {e:.3e}"
+    g = w.Hq // w.Hkv
+    last = R.pos[-128:]  # last 128 positions of the rank's second chunk
+    where = np.argsort(R.allp)[last]  # their rows in k_all
+    for kvh in (0, w.Hkv - 1):
+        hs = slice(kvh * g, (kvh + 1) * g)
+        _, dk_ref, dv_ref = orc.attention_bwd(q64[:, hs], k64[:, kvh:kvh + 1], v64[:, kvh:kvh + 1],
+                                              do64[:, hs][:, :, last], R.scale, rows=last)
+        for name, got, ref in (("dk", dk[:, kvh:kvh + 1, where], dk_ref[:, :, last]),
+                               ("dv", dv[:, kvh:kvh + 1, where], dv_ref[:, :, last])):
+            e = max_err(got, ref)
+            assert e <= GTOL, f"{name} of the last 128 keys, kv head {kvh}: max-abs error {e:.3e}"
+
+
 @pytest.mark.parametrize("mode", [cpa.CP_STREAM, cpa.CP_PER_DOC])
 def test_ring_bwd_varlen(mode):
     """Block-diagonal document masks: each rank's loss against the oracle with

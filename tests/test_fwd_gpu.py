@@ -152,6 +152,28 @@ def test_llama8b_s32k_cp8_all_ranks_sampled():
         assert_close(o[:, :, idx], lse[:, :, idx], O_ref, L_ref, "bf16", f"rank {rank}")
 
 
+def test_llama8b_s128k_cp8_all_ranks_sampled():
+    """The bench workload itself (131072 tokens, 32q/8kv heads, d=128, cp=8,
+    bf16), in the launch configuration the bench times: every rank's full ring,
+    checked on sampled rows (chunk ends plus random rows) against the oracle
+    computed row by row."""
+    w = si.WORKLOADS["llama8b_s128k_cp8"]
+    full = si.make_qkv(w.B, w.Hq, w.Hkv, w.S, w.d, w.dtype, seed=w.seed)
+    q64, k64, v64 = (t.double().numpy() for t in full)
+    rng = np.random.default_rng(1)
+    n = w.S // w.cp
+    c = n // 2
+    for rank in range(w.cp):
+        announce(f"llama8b 128k rank {rank}")
+        R = Rank(w.B, w.Hq, w.Hkv, w.S, w.d, w.cp, rank, w.dtype, full=full)
+        o, lse = R.ring_fwd()
+        idx = np.unique(np.concatenate([[0, c - 1, c, n - 1], rng.integers(0, n, 8)]))
+        O_ref, L_ref = orc.attention_fwd(q64, k64, v64, R.scale, rows=R.pos[idx])
+        assert_close(o[:, :, idx], lse[:, :, idx], O_ref, L_ref, "bf16", f"rank {rank}")
+        del R, o, lse
+        torch.cuda.empty_cache()
+
+
 def test_local_only_schedule_fails_parity():
     """Attending only the local shard (the silent no-communication pitfall) is
     rejected by the same tolerance."""
