@@ -172,13 +172,15 @@ __global__ __launch_bounds__(256) void delta_kernel(const char* __restrict__ dou
 // exponentials run while the other's MFMAs do, and LDS reads of two waves
 // are in flight at once.
 //
-// LDS layout of a tile (and of the workgroup's V rows): 16-byte chunk c of row
-// r at c * col + 16 r, one column per chunk, columns 64 bytes apart modulo 256.
-// 16 rows of one chunk are 256 contiguous bytes (row reads) and 4 rows x 4
-// chunks fall in 16 different bank groups (transposed reads), so neither
-// pattern has bank conflicts; a 64-row tile column is exactly what one
-// LDS-direct DMA instruction writes, and every address is a per-lane pointer
-// plus an immediate.
+// Q and dO tiles are row-major in LDS with 16-byte chunks permuted per row by
+// swz_t: one LDS-direct DMA instruction writes 4 (d = 128) or 8 (d = 64)
+// whole rows, read from global memory as contiguous row segments, and both the
+// row reads and the transposed reads are free of bank conflicts; a read's
+// address is a lane pointer plus (lane constant XOR a per-read constant).
+// The workgroup's V rows, copied once, use a column layout instead: chunk c of
+// row r at c * col + 16 r, columns 64 bytes apart modulo 256, so 16 rows of
+// one chunk are 256 contiguous bytes and every address is a lane pointer plus
+// an immediate.
 constexpr int kColBytes = kQT * 16 + 64;  // a column of a 64-row tile
 constexpr int kKeysPerWg = 256;
 constexpr int kVColBytes = kKeysPerWg * 16 + 64;
@@ -186,13 +188,19 @@ constexpr int kVColBytes = kKeysPerWg * 16 + 64;
 template <int D>
 struct KvCfg {
   static constexpr int NW = 8;
-  static constexpr int CHR = D / 8;              // 16-byte chunks (columns) per row
-  static constexpr int TILE = CHR * kColBytes;   // one Q or dO tile
+  static constexpr int CHR = D / 8;              // 16-byte chunks per row
+  static constexpr int ROW = D * 2;              // bytes per Q / dO row
+  static constexpr int TILE = kQT * ROW;         // one Q or dO tile (row-major)
+  static constexpr int NBLK = TILE / 1024;       // 1 KB DMA blocks per tile
+  static constexpr int RPB = 1024 / ROW;         // rows per DMA block
   static constexpr int VTILE = CHR * kVColBytes; // the workgroup's V rows
   static constexpr int KREG = D / 16;            // 16-wide d slices
   static constexpr int DT = D / 32;              // 32-row blocks of dK^T / dV^T
   static constexpr int LIST = 1024;
   static_assert(CHR % NW == 0 || NW % CHR == 0, "column split");
+  // The swizzle depends on row % 16; a wave's DMA blocks must all see the same
+  // pattern so that one lane offset serves all of them.
+  static_assert(NW % (16 / RPB) == 0 && NBLK % (16 / RPB) == 0 && (2 * NBLK) % NW == 0, "DMA split");
 };
 
 template <int D>
@@ -273,17 +281,32 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(BParams p) {
 
   // ---- per-lane constant offsets ----------------------------------------
   const long long q_row_bytes = p.q_ss * 2;
-  const int voff = (int)(lane * q_row_bytes);  // DMA: lane l copies row l of a tile column
-  // Row reads (A of S = Q K^T and dP = dO V^T): row key_perm(l32) (+32 sub) at
-  // chunk 2kk + hi: nbase + kk * 2 kColBytes + sub * 512.
-  const int nbase = hi * kColBytes + key_perm(l32) * 16;
+  // DMA: blocks wave, wave + NW, ... of the Q and dO tiles; lane l fills slot
+  // l % CHR of row l / CHR of its block.
+  const int voff = (int)((lane / C::CHR) * q_row_bytes) +
+                   16 * swz_t<C::CHR>(C::RPB * (wave % C::NBLK) + lane / C::CHR, lane % C::CHR);
+  // Row reads (A of S = Q K^T and dP = dO V^T): row key_perm(l32) (+32 sub),
+  // logical chunk 2kk + hi, at byte nrow*ROW + ((32 kk) ^ nY) of the tile.
+  const int nrow = key_perm(l32);
+  const int nY = 16 * (hi ^ swz_t<C::CHR>(nrow, 0));
   // V operand (B of dP): this lane's key at chunk 2kk + hi.
   const int vbase = hi * kVColBytes + kloc * 16;
   // Transposed reads (A of dV^T += dO^T P, dK^T += Q^T dS): lane s16 of its
   // 16-lane group reads row 8hi + 4h + s16/4 (+16gg + 32sub) at column 32t +
-  // 16*(bit 4 of lane) + 4*(s16%4): tbase + t * 4 kColBytes + h * 64 + gg * 256
-  // + sub * 512; the lane then holds column 32t + l32 at rows 8hi + 4h + 0..3.
-  const int tbase = (2 * ((lane >> 4) & 1) + ((s16 & 3) >> 1)) * kColBytes + (8 * hi + (s16 >> 2)) * 16 + 8 * (s16 & 1);
+  // 16*(bit 4 of lane) + 4*(s16%4); the lane then holds column 32t + l32 at
+  // rows 8hi + 4h + 0..3.  With the row's swizzle f, the logical chunk 4t + cl
+  // lands at 4 (t ^ (f >> 2)) + (cl ^ (f & 3)): byte tP[h] + ((64 t) ^ tA).
+  int tP[2], tA;
+  {
+    const int cl = 2 * ((lane >> 4) & 1) + ((s16 & 3) >> 1);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int r = 8 * hi + 4 * h + (s16 >> 2);
+      const int f = swz_t<C::CHR>(r, 0);
+      tP[h] = r * C::ROW + 16 * (cl ^ (f & 3)) + 8 * (s16 & 1);
+      tA = 64 * (f >> 2);  // the same for both h
+    }
+  }
 
   // ---- list of (query head, query tile) pairs this workgroup needs ---------
   // Entry .x = t | hg << 16 for tile t of query head kvh*g + hg; .y = class of
@@ -353,17 +376,16 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(BParams p) {
         __builtin_amdgcn_make_buffer_rsrc((void*)(p.q + qoff), 0, (int)(nval * q_row_bytes), kBufferFlags);
     const __amdgpu_buffer_rsrc_t rsO =
         __builtin_amdgcn_make_buffer_rsrc((void*)(p.dout + qoff), 0, (int)(nval * q_row_bytes), kBufferFlags);
-    // 2*CHR column copies (Q then dO) over NW waves.
+    // 2*NBLK block copies (Q then dO) over NW waves.
 #pragma unroll
-    for (int j = 0; j < (2 * C::CHR) / NW; ++j) {
+    for (int j = 0; j < (2 * C::NBLK) / NW; ++j) {
       const int i = wave + NW * j;
-      const int col = i % C::CHR;
-      if (i < C::CHR)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsQ, (lds_ptr_t)(&sQ[buf][0] + col * kColBytes), 16, voff, col * 16,
-                                                 0, 0);
+      const int ib = i % C::NBLK;
+      const int soff = (int)(C::RPB * ib * q_row_bytes);
+      if (i < C::NBLK)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsQ, (lds_ptr_t)(&sQ[buf][0] + ib * 1024), 16, voff, soff, 0, 0);
       else
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsO, (lds_ptr_t)(&sO[buf][0] + col * kColBytes), 16, voff, col * 16,
-                                                 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsO, (lds_ptr_t)(&sO[buf][0] + ib * 1024), 16, voff, soff, 0, 0);
     }
     if (wave < 4) {
       const void* arr = wave == 0 ? (const void*)p.nl2 : wave == 1 ? (const void*)p.dlt
@@ -387,8 +409,8 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(BParams p) {
   // numbers (span = pos - lo; padding rows have zero Q and dO rows and add
   // nothing); full tiles skip the test.
   auto half = [&](int buf, int sub, bool full) {
-    const lds_char* qn = launder(to_lds(&sQ[0][0]) + buf * C::TILE + nbase + sub * 512);
-    const lds_char* on = launder(to_lds(&sO[0][0]) + buf * C::TILE + nbase + sub * 512);
+    const lds_char* qn = launder(to_lds(&sQ[0][0]) + buf * C::TILE + nrow * C::ROW + sub * 32 * C::ROW);
+    const lds_char* on = launder(to_lds(&sO[0][0]) + buf * C::TILE + nrow * C::ROW + sub * 32 * C::ROW);
     const lds_char* vn = launder(to_lds(sV) + vbase);
     // S = Q K^T, dP = dO V^T: register r is query row 32sub + 16(r/8) + 8hi + r%8.
     f32x16 s, dp;
@@ -399,14 +421,14 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(BParams p) {
     }
     // Operands are read one d-slice ahead.
     bf16x8 aq[2], ao[2], bv[2];
-    aq[0] = lds_read8(qn);
-    ao[0] = lds_read8(on);
+    aq[0] = lds_read8(qn + nY);
+    ao[0] = lds_read8(on + nY);
     bv[0] = lds_read8(vn);
 #pragma unroll
     for (int kk = 0; kk < C::KREG; ++kk) {
       if (kk + 1 < C::KREG) {
-        aq[(kk + 1) & 1] = lds_read8(qn + (kk + 1) * 2 * kColBytes);
-        ao[(kk + 1) & 1] = lds_read8(on + (kk + 1) * 2 * kColBytes);
+        aq[(kk + 1) & 1] = lds_read8(qn + (nY ^ (32 * (kk + 1))));
+        ao[(kk + 1) & 1] = lds_read8(on + (nY ^ (32 * (kk + 1))));
         bv[(kk + 1) & 1] = lds_read8(vn + (kk + 1) * 2 * kVColBytes);
       }
       s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq[kk & 1], kreg[kk], s, 0, 0, 0);
@@ -455,19 +477,22 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(BParams p) {
     if (full) probs(std::integral_constant<bool, false>{});
     else probs(std::integral_constant<bool, true>{});
     // dV^T += dO^T P, dK^T += Q^T dS over the half tile's 32 query rows.
-    const lds_char* qt = launder(to_lds(&sQ[0][0]) + buf * C::TILE + tbase + sub * 512);
-    const lds_char* ot = launder(to_lds(&sO[0][0]) + buf * C::TILE + tbase + sub * 512);
+    const lds_char* qt0 = launder(to_lds(&sQ[0][0]) + buf * C::TILE + tP[0] + sub * 32 * C::ROW);
+    const lds_char* qt1 = launder(to_lds(&sQ[0][0]) + buf * C::TILE + tP[1] + sub * 32 * C::ROW);
+    const lds_char* ot0 = launder(to_lds(&sO[0][0]) + buf * C::TILE + tP[0] + sub * 32 * C::ROW);
+    const lds_char* ot1 = launder(to_lds(&sO[0][0]) + buf * C::TILE + tP[1] + sub * 32 * C::ROW);
     constexpr int NG = 2 * C::DT;  // (gg, t) pairs
-    auto toff = [](int m) { return (m % C::DT) * 4 * kColBytes + (m / C::DT) * 256; };
+    // Byte offset of pair m = DT*gg + t: rows +16gg, chunk group t.
+    auto toff = [&](int m) { return (m / C::DT) * 16 * C::ROW + ((64 * (m % C::DT)) ^ tA); };
     bf16x8 to[2], tq[2];
-    to[0] = lds_read_tr(ot, ot + 64);
-    tq[0] = lds_read_tr(qt, qt + 64);
+    to[0] = lds_read_tr(ot0 + toff(0), ot1 + toff(0));
+    tq[0] = lds_read_tr(qt0 + toff(0), qt1 + toff(0));
 #pragma unroll
     for (int m = 0; m < NG; ++m) {
       if (m + 1 < NG) {
         const int o = toff(m + 1);
-        to[(m + 1) & 1] = lds_read_tr(ot + o, ot + o + 64);
-        tq[(m + 1) & 1] = lds_read_tr(qt + o, qt + o + 64);
+        to[(m + 1) & 1] = lds_read_tr(ot0 + o, ot1 + o);
+        tq[(m + 1) & 1] = lds_read_tr(qt0 + o, qt1 + o);
       }
       const int t = m % C::DT, gg = m / C::DT;
       dva[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(to[m & 1], pb[gg], dva[t], 0, 0, 0);
