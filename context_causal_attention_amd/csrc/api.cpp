@@ -135,7 +135,6 @@ BwdWorkspace bwd_workspace_layout(int32_t b, int32_t hq, int32_t hkv, int32_t d,
   };
   w.kbounds_off = take((size_t)nkt * 16);
   w.kpos_off = take((size_t)w.kt_row * 4);
-  w.kt_off = take((size_t)b * hkv * d * (size_t)w.kt_row * 2);
   w.qbounds_off = take((size_t)nqt * 16);
   w.qlo_off = take((size_t)w.sq_pad * 4);
   w.qspan_off = take((size_t)w.sq_pad * 4);
@@ -294,10 +293,11 @@ int run_bwd(const cp_shape* s, int32_t cp, int32_t rank, const void* q, const vo
     return fail(CP_EINVAL, "%lld query rows or %d query heads per kv head are too many for the backward",
                 (long long)s->sq, s->hq / s->hkv);
   const BwdWorkspace w = bwd_workspace_layout(s->b, s->hq, s->hkv, s->d, s->sq, s->sk, cp);
-  // The kernels address the transposed copies and the padded per-row arrays
-  // with 32-bit buffer offsets.
-  if ((double)s->d * (double)w.kt_row * 2.0 >= 2147483648.0 ||
-      (double)s->b * s->hq * (double)w.sq_pad * 4.0 >= 2147483648.0)
+  // The kernels address the padded per-row and per-key arrays, and one tile's
+  // rows of Q, dO, K or V, with 32-bit buffer offsets.
+  if ((double)w.kt_row * 4.0 >= 2147483648.0 || (double)s->b * s->hq * (double)w.sq_pad * 4.0 >= 2147483648.0 ||
+      64.0 * (double)s->q_str[2] * 2.0 >= 2147483648.0 || 64.0 * (double)s->k_str[2] * 2.0 >= 2147483648.0 ||
+      64.0 * (double)s->v_str[2] * 2.0 >= 2147483648.0)
     return fail(CP_EINVAL, "sequence too long for 32-bit buffer offsets (sq=%lld, sk=%lld)", (long long)s->sq,
                 (long long)s->sk);
   if (!ws) return fail(CP_EWORKSPACE, "workspace is null (%zu bytes needed)", w.total);

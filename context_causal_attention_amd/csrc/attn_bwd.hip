@@ -20,7 +20,7 @@
 //     walks the ring's key tiles like the forward; S^T = K Q^T, dP^T = V dO^T,
 //     dQ^T += K^T dS^T, with Q and dO of the wave's rows resident.
 // Operand tiles are copied HBM -> LDS by buffer loads with the LDS-direct bit;
-// K^T comes from a preparation pass.
+// a small preparation pass tabulates tile bounds and per-row constants.
 #include <hip/hip_runtime.h>
 
 #include <climits>
@@ -48,7 +48,6 @@ struct BParams {
   // workspace
   const int4* kbounds;   // per 64-key tile {min pos, max pos, valid rows, 0}
   const int* kpos_pad;   // per key slot, padding = kInvalidKey
-  const char* kt;        // bf16 K^T [b][hkv][d][kt_row]
   const int4* qbounds;   // per 64-row query tile {min pos, max pos, min lo, max lo}
   const int* qlo_pad;    // per query slot [sq_pad]: document start (padding INT_MIN)
   const int* qspan_pad;  // position - document start (padding 0)
@@ -58,7 +57,6 @@ struct BParams {
   float* dk;             // fp32 [b, hkv, sk, d] contiguous, accumulated
   float* dv;
   long long q_sb, q_sh, q_ss, k_sb, k_sh, k_ss, v_sb, v_sh, v_ss;
-  long long kt_row;      // elements per K^T row
   int sq_pad;            // query rows per (b, head), padded to kQT
   int B, Hq, Hkv, sq, sk, cp, rank, R, tpr, nqt;
   float c2;              // scale * log2(e)
@@ -68,44 +66,22 @@ struct BParams {
 // ============================================================================
 // Preparation
 // ============================================================================
-// Key side, per 64-key tile of a rank's shard: position bounds, padded key
-// positions and K^T.
-template <int D>
-__global__ __launch_bounds__(256) void key_prep_kernel(BParams p, int4* __restrict__ kbounds, int* __restrict__ kpos_pad,
-                                                       __bf16* __restrict__ kt) {
+// Key side, per 64-key tile of a rank's shard: position bounds and padded key
+// positions.
+__global__ __launch_bounds__(64) void key_prep_kernel(BParams p, int4* __restrict__ kbounds,
+                                                      int* __restrict__ kpos_pad) {
   const int tile = blockIdx.x;
   const int src = tile / p.tpr;
   const int i = tile - src * p.tpr;
   const int r0 = src * p.R + i * kKT;
   const int nval = min(kKT, p.R - i * kKT);
   const int tid = threadIdx.x;
-  if (blockIdx.y == 0 && tid < 64) {
-    const bool ok = tid < nval;
-    const int kp = ok ? p.k_pos[r0 + tid] : 0;
-    const int mn = wave_min(ok ? kp : INT_MAX);
-    const int mx = wave_max(ok ? kp : INT_MIN);
-    if (tid == 0) kbounds[tile] = int4{mn, mx, nval, 0};
-    kpos_pad[tile * kKT + tid] = ok ? kp : kInvalidKey;
-  }
-  __shared__ __bf16 s[kKT][D + 8];
-  const int b = blockIdx.y / p.Hkv, kvh = blockIdx.y % p.Hkv;
-  const char* kb = p.k + ((long long)b * p.k_sb + (long long)kvh * p.k_sh) * 2;
-  constexpr int CH = D / 8;
-  for (int c = tid; c < kKT * CH; c += 256) {
-    const int r = c / CH, ch = c % CH;
-    const u32x4 raw = r < nval ? *reinterpret_cast<const u32x4*>(kb + ((long long)(r0 + r) * p.k_ss + ch * 8) * 2)
-                               : u32x4{0, 0, 0, 0};
-    *reinterpret_cast<u32x4*>(&s[r][ch * 8]) = raw;
-  }
-  __syncthreads();
-  __bf16* out = kt + ((long long)blockIdx.y * D) * p.kt_row + (long long)tile * kKT;
-  for (int c = tid; c < D * (kKT / 8); c += 256) {
-    const int dd = c / (kKT / 8), kc = c % (kKT / 8);
-    bf16x8 w;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) w[j] = s[kc * 8 + j][dd];
-    *reinterpret_cast<bf16x8*>(out + (long long)dd * p.kt_row + kc * 8) = w;
-  }
+  const bool ok = tid < nval;
+  const int kp = ok ? p.k_pos[r0 + tid] : 0;
+  const int mn = wave_min(ok ? kp : INT_MAX);
+  const int mx = wave_max(ok ? kp : INT_MIN);
+  if (tid == 0) kbounds[tile] = int4{mn, mx, nval, 0};
+  kpos_pad[tile * kKT + tid] = ok ? kp : kInvalidKey;
 }
 
 // Query side, per 64-row tile of one (batch, query head): -LSE in base 2 and
@@ -208,11 +184,18 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(BParams p) {
 #if defined(__HIP_DEVICE_COMPILE__)
   using C = KvCfg<D>;
   constexpr int NW = C::NW;
-  __shared__ __attribute__((aligned(1024))) char sQ[2][C::TILE];
-  __shared__ __attribute__((aligned(1024))) char sO[2][C::TILE];
+  // Two buffers per tile kind, as separate arrays with roles fixed at compile
+  // time: the compiler can then tell a tile's LDS reads from the DMA writes
+  // into the other buffer, and does not wait for the copy in flight before
+  // reading.
+  __shared__ __attribute__((aligned(1024))) char sQ0[C::TILE];
+  __shared__ __attribute__((aligned(1024))) char sQ1[C::TILE];
+  __shared__ __attribute__((aligned(1024))) char sO0[C::TILE];
+  __shared__ __attribute__((aligned(1024))) char sO1[C::TILE];
   __shared__ __attribute__((aligned(1024))) char sV[C::VTILE];
   // Per row of each buffered tile: -LSE*log2(e), delta, document start, span.
-  __shared__ __attribute__((aligned(16))) float sRow[2][4][kQT];
+  __shared__ __attribute__((aligned(16))) float sR0[4][kQT];
+  __shared__ __attribute__((aligned(16))) float sR1[4][kQT];
   __shared__ int2 sList[C::LIST];
   __shared__ int sCnt[NW];
   __shared__ int sKb[NW][3];  // per wave: min key pos, max key pos, all keys valid
@@ -363,9 +346,14 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(BParams p) {
       dka[t][r] = 0.f;
     }
 
-  // Copies query tile ex (t | hg << 16) into buffer buf: the columns of the Q
-  // and dO tiles split over the waves; waves 0..3 each copy one per-row array.
-  auto issue = [&](int buf, int ex) {
+  // Buffers of compile-time index B.
+  auto qbuf = [&](auto bc) -> char* { if constexpr (decltype(bc)::value) return sQ1; else return sQ0; };
+  auto obuf = [&](auto bc) -> char* { if constexpr (decltype(bc)::value) return sO1; else return sO0; };
+  auto rbuf = [&](auto bc) -> float* { if constexpr (decltype(bc)::value) return &sR1[0][0]; else return &sR0[0][0]; };
+
+  // Copies query tile ex (t | hg << 16) into buffer B: the blocks of the Q and
+  // dO tiles split over the waves; waves 0..3 each copy one per-row array.
+  auto issue = [&](auto bc, int ex) {
     const int t = ex & 0xFFFF, hg = ex >> 16;
     const int h = kvh * g + hg;
     const int r0 = t * kQT;
@@ -383,35 +371,37 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(BParams p) {
       const int ib = i % C::NBLK;
       const int soff = (int)(C::RPB * ib * q_row_bytes);
       if (i < C::NBLK)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsQ, (lds_ptr_t)(&sQ[buf][0] + ib * 1024), 16, voff, soff, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsQ, (lds_ptr_t)(qbuf(bc) + ib * 1024), 16, voff, soff, 0, 0);
       else
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsO, (lds_ptr_t)(&sO[buf][0] + ib * 1024), 16, voff, soff, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsO, (lds_ptr_t)(obuf(bc) + ib * 1024), 16, voff, soff, 0, 0);
     }
     if (wave < 4) {
       const void* arr = wave == 0 ? (const void*)p.nl2 : wave == 1 ? (const void*)p.dlt
                       : wave == 2 ? (const void*)p.qlo_pad : (const void*)p.qspan_pad;
       const int soff = (int)((wave < 2 ? bh * p.sq_pad + r0 : (long long)r0) * 4);
       const __amdgpu_buffer_rsrc_t rsR = __builtin_amdgcn_make_buffer_rsrc((void*)arr, 0, 0x7fffffff, kBufferFlags);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsR, (lds_ptr_t)&sRow[buf][wave][0], 4, lane * 4, soff, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsR, (lds_ptr_t)(rbuf(bc) + wave * kQT), 4, lane * 4, soff, 0, 0);
     }
   };
 
-  // Lane pointers pass through an empty asm where they are formed so that
-  // pointer + constant is not hoisted out of the loop as one register per
-  // read: every read is then one of these pointers plus a DS offset immediate.
-  auto launder = [](const lds_char* ptr) {
-    asm volatile("" : "+v"(ptr));
-    return ptr;
+  // Lane offsets pass through an empty asm where they are used so that lane
+  // offset + constant is not hoisted out of the loop as one register per read:
+  // every read is then buffer + lane offset + a DS offset immediate, and the
+  // buffer it reads stays visible to the compiler.
+  auto launder = [](int off) {
+    asm volatile("" : "+v"(off));
+    return off;
   };
 
   // One half tile (sub) of the tile in buffer buf: S/dP, P/dS, dV/dK.  On
   // partial tiles key kp is allowed for a row iff kp - lo <= span as unsigned
   // numbers (span = pos - lo; padding rows have zero Q and dO rows and add
   // nothing); full tiles skip the test.
-  auto half = [&](int buf, int sub, bool full) {
-    const lds_char* qn = launder(to_lds(&sQ[0][0]) + buf * C::TILE + nrow * C::ROW + sub * 32 * C::ROW);
-    const lds_char* on = launder(to_lds(&sO[0][0]) + buf * C::TILE + nrow * C::ROW + sub * 32 * C::ROW);
-    const lds_char* vn = launder(to_lds(sV) + vbase);
+  auto half = [&](auto bc, int sub, bool full) {
+    const int no = launder(nrow * C::ROW + sub * 32 * C::ROW);
+    const lds_char* qn = to_lds(qbuf(bc)) + no;
+    const lds_char* on = to_lds(obuf(bc)) + no;
+    const lds_char* vn = to_lds(sV) + launder(vbase);
     // S = Q K^T, dP = dO V^T: register r is query row 32sub + 16(r/8) + 8hi + r%8.
     f32x16 s, dp;
 #pragma unroll
@@ -437,7 +427,7 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(BParams p) {
     // P = exp2(c2 s - LSE log2 e) on allowed pairs, dS = P (dP - delta).  Only
     // this vector part differs between partial and full tiles; the MFMAs around
     // it exist once, so their accumulators stay in place.
-    const lds_char* rowb = launder(to_lds(&sRow[0][0][0]) + (buf * 4 * kQT + 32 * sub + 8 * hi) * 4);
+    const lds_char* rowb = to_lds(rbuf(bc)) + launder((32 * sub + 8 * hi) * 4);
     bf16x8 pb[2], db[2];
     auto probs = [&](auto maskc) {
       constexpr bool MASKED = decltype(maskc)::value;
@@ -477,10 +467,11 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(BParams p) {
     if (full) probs(std::integral_constant<bool, false>{});
     else probs(std::integral_constant<bool, true>{});
     // dV^T += dO^T P, dK^T += Q^T dS over the half tile's 32 query rows.
-    const lds_char* qt0 = launder(to_lds(&sQ[0][0]) + buf * C::TILE + tP[0] + sub * 32 * C::ROW);
-    const lds_char* qt1 = launder(to_lds(&sQ[0][0]) + buf * C::TILE + tP[1] + sub * 32 * C::ROW);
-    const lds_char* ot0 = launder(to_lds(&sO[0][0]) + buf * C::TILE + tP[0] + sub * 32 * C::ROW);
-    const lds_char* ot1 = launder(to_lds(&sO[0][0]) + buf * C::TILE + tP[1] + sub * 32 * C::ROW);
+    const int t0 = launder(tP[0] + sub * 32 * C::ROW), t1 = launder(tP[1] + sub * 32 * C::ROW);
+    const lds_char* qt0 = to_lds(qbuf(bc)) + t0;
+    const lds_char* qt1 = to_lds(qbuf(bc)) + t1;
+    const lds_char* ot0 = to_lds(obuf(bc)) + t0;
+    const lds_char* ot1 = to_lds(obuf(bc)) + t1;
     constexpr int NG = 2 * C::DT;  // (gg, t) pairs
     // Byte offset of pair m = DT*gg + t: rows +16gg, chunk group t.
     auto toff = [&](int m) { return (m / C::DT) * 16 * C::ROW + ((64 * (m % C::DT)) ^ tA); };
@@ -510,19 +501,25 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(BParams p) {
       e.y = __builtin_amdgcn_readfirstlane(sList[j].y);
       return e;
     };
-    issue(0, ent(0).x);
+    const std::integral_constant<int, 0> b0{};
+    const std::integral_constant<int, 1> b1{};
+    issue(b0, ent(0).x);
     wait_vmem();
     __syncthreads();
-    for (int j = 0; j < cnt; ++j) {
-      const int buf = j & 1;
-      if (j + 1 < cnt) issue(buf ^ 1, ent(j + 1).x);
+    // Tile j from buffer B while tile j+1 is copied into the other buffer.
+    auto tile = [&](auto bc, int j) {
+      if (j + 1 < cnt) issue(std::integral_constant<int, 1 - decltype(bc)::value>{}, ent(j + 1).x);
       const int cls = (int)(((unsigned)ent(j).y >> csh) & 3);
       if (cls != kSkip) {
 #pragma nounroll
-        for (int sub = 0; sub < 2; ++sub) half(buf, sub, cls == kFull);
+        for (int sub = 0; sub < 2; ++sub) half(bc, sub, cls == kFull);
       }
       wait_vmem();
       __syncthreads();
+    };
+    for (int j = 0; j < cnt; j += 2) {
+      tile(b0, j);
+      if (j + 1 < cnt) tile(b1, j + 1);
     }
   }
 
@@ -552,21 +549,28 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(BParams p) {
 // ============================================================================
 // dQ
 // ============================================================================
+// A workgroup of 8 waves owns 256 query rows (32 a wave) of one query head and
+// walks the ring's 64-key tiles like the forward: per 32-key half tile,
+// S^T = K Q^T and dP^T = V dO^T (the wave's rows as MFMA columns, Q and dO in
+// registers), then dS^T, then dQ^T += K^T dS^T with K^T read from the K tile
+// by transposing LDS reads.  K and V tiles are row-major with the swz_t chunk
+// permutation (whole rows per DMA instruction, conflict-free row and
+// transposed reads) and double-buffered in separate arrays with roles fixed at
+// compile time, so the compiler sees that a tile's reads and the copy into
+// the other buffer do not overlap.
 template <int D>
 struct QCfg {
   static constexpr int NW = 8;
-  static constexpr int ROW = D * 2;           // bytes per K / V row in LDS
+  static constexpr int ROW = D * 2;             // bytes per K / V row
   static constexpr int CHR = D / 8;
-  static constexpr int TROW = kKT * 2;        // bytes per K^T row in LDS (128)
-  static constexpr int TCHR = kKT / 8;
-  static constexpr int RBYTES = kKT * ROW;
-  static constexpr int TBYTES = D * TROW;
-  static constexpr int RPW = RBYTES / 1024 / NW;
-  static constexpr int TPW = TBYTES / 1024 / NW;
+  static constexpr int TILE = kKT * ROW;        // one K or V tile (row-major)
+  static constexpr int NBLK = TILE / 1024;      // 1 KB DMA blocks per tile
+  static constexpr int RPB = 1024 / ROW;        // rows per DMA block
   static constexpr int QREG = D / 16;
   static constexpr int DT = D / 32;
   static constexpr int LIST = 2048;
-  static_assert(RPW >= 1 && TPW >= 1, "tile too small for the DMA split");
+  static constexpr int LOADS = (2 * NBLK) / NW;  // DMA instructions per wave per tile (wave 0: one more)
+  static_assert(NW % (16 / RPB) == 0 && NBLK % (16 / RPB) == 0 && (2 * NBLK) % NW == 0, "DMA split");
 };
 
 template <int D>
@@ -574,10 +578,12 @@ __global__ __launch_bounds__(512, 1) void dq_kernel(BParams p) {
 #if defined(__HIP_DEVICE_COMPILE__)
   using C = QCfg<D>;
   constexpr int NW = C::NW;
-  __shared__ __attribute__((aligned(1024))) char sK[2][C::RBYTES];
-  __shared__ __attribute__((aligned(1024))) char sV[2][C::RBYTES];
-  __shared__ __attribute__((aligned(1024))) char sKT[2][C::TBYTES];
-  __shared__ __attribute__((aligned(16))) int sP[2][kKT];
+  __shared__ __attribute__((aligned(1024))) char sK0[C::TILE];
+  __shared__ __attribute__((aligned(1024))) char sK1[C::TILE];
+  __shared__ __attribute__((aligned(1024))) char sV0[C::TILE];
+  __shared__ __attribute__((aligned(1024))) char sV1[C::TILE];
+  __shared__ __attribute__((aligned(16))) int sP0[kKT];
+  __shared__ __attribute__((aligned(16))) int sP1[kKT];
   __shared__ int2 sList[C::LIST];
   __shared__ int sCnt[NW];
   __shared__ int sWb[NW][4];
@@ -587,6 +593,7 @@ __global__ __launch_bounds__(512, 1) void dq_kernel(BParams p) {
   const int lane = tid & 63;
   const int l32 = lane & 31;
   const int hi = lane >> 5;
+  const int s16 = lane & 15;
   const int g = p.Hq / p.Hkv;
   const int nqt = (p.sq + NW * 32 - 1) / (NW * 32);
 
@@ -633,37 +640,43 @@ __global__ __launch_bounds__(512, 1) void dq_kernel(BParams p) {
 
   const long long k_row_bytes = p.k_ss * 2;
   const long long v_row_bytes = p.v_ss * 2;
-  const long long t_row_bytes = p.kt_row * 2;
-  int voffK[C::RPW], voffV[C::RPW], voffT[C::TPW];
+  // DMA: blocks wave, wave + NW, ... of the K and V tiles; lane l fills slot
+  // l % CHR of row l / CHR of its block (all of a wave's blocks share one
+  // swizzle pattern).
+  const int lrow = lane / C::CHR;
+  const int lslot = 16 * swz_t<C::CHR>(C::RPB * (wave % C::NBLK) + lrow, lane % C::CHR);
+  const int voffK = (int)(lrow * k_row_bytes) + lslot;
+  const int voffV = (int)(lrow * v_row_bytes) + lslot;
+  // Row reads (A of S^T = K Q^T and dP^T = V dO^T): key key_perm(l32) (+32
+  // sub), logical chunk 2kk + hi, at byte nrow*ROW + ((32 kk) ^ nY).
+  const int nrow = key_perm(l32);
+  const int nY = 16 * (hi ^ swz_t<C::CHR>(nrow, 0));
+  // Transposed reads of K (A of dQ^T += K^T dS^T): lane s16 of its 16-lane
+  // group reads key 8hi + 4h + s16/4 (+16gg + 32sub) at column 32t +
+  // 16*(bit 4 of lane) + 4*(s16%4): byte tP[h] + ((64 t) ^ tA).
+  int tP[2], tA;
+  {
+    const int cl = 2 * ((lane >> 4) & 1) + ((s16 & 3) >> 1);
 #pragma unroll
-  for (int j = 0; j < C::RPW; ++j) {
-    const int c = (wave + NW * j) * 64 + lane;
-    const int r = c / C::CHR, ph = c % C::CHR;
-    voffK[j] = (int)(r * k_row_bytes) + 16 * swz<C::CHR>(r, ph);
-    voffV[j] = (int)(r * v_row_bytes) + 16 * swz<C::CHR>(r, ph);
+    for (int hh = 0; hh < 2; ++hh) {
+      const int r = 8 * hi + 4 * hh + (s16 >> 2);
+      const int f = swz_t<C::CHR>(r, 0);
+      tP[hh] = r * C::ROW + 16 * (cl ^ (f & 3)) + 8 * (s16 & 1);
+      tA = 64 * (f >> 2);
+    }
   }
-#pragma unroll
-  for (int j = 0; j < C::TPW; ++j) {
-    const int c = (wave + NW * j) * 64 + lane;
-    const int r = c / C::TCHR, ph = c % C::TCHR;
-    voffT[j] = (int)(r * t_row_bytes) + 16 * swz<C::TCHR>(r, ph);
-  }
-  const int krow = key_perm(l32);
-  int raddr[C::QREG];
-#pragma unroll
-  for (int kk = 0; kk < C::QREG; ++kk) raddr[kk] = krow * C::ROW + 16 * swz<C::CHR>(krow, 2 * kk + hi);
-  int taddr[4];
-#pragma unroll
-  for (int kg = 0; kg < 4; ++kg) taddr[kg] = l32 * C::TROW + 16 * swz<C::TCHR>(l32, 2 * kg + hi);
 
   const char* kbase = p.k + ((long long)b * p.k_sb + (long long)kvh * p.k_sh) * 2;
   const char* vbase = p.v + ((long long)b * p.v_sb + (long long)kvh * p.v_sh) * 2;
-  const char* ktbase = p.kt + (((long long)b * p.Hkv + kvh) * D) * p.kt_row * 2;
-  const __amdgpu_buffer_rsrc_t rsT =
-      __builtin_amdgcn_make_buffer_rsrc((void*)ktbase, 0, (int)(D * t_row_bytes), kBufferFlags);
   const __amdgpu_buffer_rsrc_t rsP = __builtin_amdgcn_make_buffer_rsrc((void*)p.kpos_pad, 0, 0x7fffffff, kBufferFlags);
 
-  auto issue = [&](int buf, int e) __attribute__((always_inline)) {
+  auto kbuf = [&](auto bc) -> char* { if constexpr (decltype(bc)::value) return sK1; else return sK0; };
+  auto vbuf = [&](auto bc) -> char* { if constexpr (decltype(bc)::value) return sV1; else return sV0; };
+  auto pbuf = [&](auto bc) -> int* { if constexpr (decltype(bc)::value) return sP1; else return sP0; };
+
+  // Copies key tile e (src | i << 8) into buffer B: LOADS blocks per wave, and
+  // the padded key positions (wave 0).
+  auto issue = [&](auto bc, int e) {
     const int src = e & 0xFF, i = (e >> 8) & 0xFFFF;
     const int tile = src * p.tpr + i;
     const int r0 = src * p.R + i * kKT;
@@ -673,16 +686,25 @@ __global__ __launch_bounds__(512, 1) void dq_kernel(BParams p) {
     const __amdgpu_buffer_rsrc_t rsV = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(vbase + (long long)r0 * v_row_bytes), 0, (int)(nval * v_row_bytes), kBufferFlags);
 #pragma unroll
-    for (int j = 0; j < C::RPW; ++j) {
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsK, (lds_ptr_t)(&sK[buf][0] + (wave + NW * j) * 1024), 16, voffK[j], 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsV, (lds_ptr_t)(&sV[buf][0] + (wave + NW * j) * 1024), 16, voffV[j], 0, 0, 0);
+    for (int j = 0; j < C::LOADS; ++j) {
+      const int bi = wave + NW * j;
+      const int ib = bi % C::NBLK;
+      if (bi < C::NBLK)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsK, (lds_ptr_t)(kbuf(bc) + ib * 1024), 16, voffK,
+                                                 (int)(C::RPB * ib * k_row_bytes), 0, 0);
+      else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsV, (lds_ptr_t)(vbuf(bc) + ib * 1024), 16, voffV,
+                                                 (int)(C::RPB * ib * v_row_bytes), 0, 0);
     }
-#pragma unroll
-    for (int j = 0; j < C::TPW; ++j)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsT, (lds_ptr_t)(&sKT[buf][0] + (wave + NW * j) * 1024), 16, voffT[j],
-                                               tile * kKT * 2, 0, 0);
     if (wave == 0)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsP, (lds_ptr_t)&sP[buf][0], 4, lane * 4, tile * kKT * 4, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsP, (lds_ptr_t)pbuf(bc), 4, lane * 4, tile * kKT * 4, 0, 0);
+  };
+
+  // Lane offsets pass through an empty asm where they are used (see the dK/dV
+  // kernel): reads are buffer + lane offset + a DS offset immediate.
+  auto launder = [](int off) {
+    asm volatile("" : "+v"(off));
+    return off;
   };
 
   f32x16 dqa[C::DT];
@@ -691,60 +713,68 @@ __global__ __launch_bounds__(512, 1) void dq_kernel(BParams p) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) dqa[t][r] = 0.f;
 
-  auto compute = [&](int buf, int cls) __attribute__((always_inline)) {
-    if (cls == kSkip) return;
-    const char* k_t = &sK[buf][0];
-    const char* v_t = &sV[buf][0];
-    const char* kt_t = &sKT[buf][0];
+  // One half tile (sub: keys 32sub..32sub+31) of the tile in buffer buf.
+  auto half = [&](auto bc, int sub, bool full) {
+    const int no = launder(nrow * C::ROW + sub * 32 * C::ROW);
+    const lds_char* kn = to_lds(kbuf(bc)) + no;
+    const lds_char* vn = to_lds(vbuf(bc)) + no;
+    // S^T, dP^T: register r is key 32sub + 16(r/8) + 8hi + r%8.
+    f32x16 s, dp;
 #pragma unroll
-    for (int sub = 0; sub < 2; ++sub) {
-      // S^T = K Q^T, dP^T = V dO^T for 32 keys (register r: key 32*sub + 16*(r/8) + 8*hi + r%8)
-      f32x16 s, dp;
+    for (int r = 0; r < 16; ++r) {
+      s[r] = 0.f;
+      dp[r] = 0.f;
+    }
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        s[r] = 0.f;
-        dp[r] = 0.f;
-      }
-#pragma unroll
-      for (int kk = 0; kk < C::QREG; ++kk) {
-        const bf16x8 ak = *reinterpret_cast<const bf16x8*>(k_t + raddr[kk] + sub * 32 * C::ROW);
-        const bf16x8 av = *reinterpret_cast<const bf16x8*>(v_t + raddr[kk] + sub * 32 * C::ROW);
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, qreg[kk], s, 0, 0, 0);
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, oreg[kk], dp, 0, 0, 0);
-      }
-      bf16x8 db[2];
+    for (int kk = 0; kk < C::QREG; ++kk) {
+      const bf16x8 ak = lds_read8(kn + (nY ^ (32 * kk)));
+      const bf16x8 av = lds_read8(vn + (nY ^ (32 * kk)));
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, qreg[kk], s, 0, 0, 0);
+      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, oreg[kk], dp, 0, 0, 0);
+    }
+    // dS^T = P^T (dP^T - delta), P^T = exp2(c2 s - LSE log2 e) on allowed keys.
+    bf16x8 db[2];
+    auto probs = [&](auto maskc) {
+      constexpr bool MASKED = decltype(maskc)::value;
 #pragma unroll
       for (int gg = 0; gg < 2; ++gg) {
-        bool ok[8];
-        if (cls == kPartial) {
-          const int* kpp = &sP[buf][32 * sub + 16 * gg + 8 * hi];
+        int kv[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+        if (MASKED) {
+          const int* kpp = pbuf(bc) + 32 * sub + 16 * gg + 8 * hi;
           const int4 k0 = *reinterpret_cast<const int4*>(kpp);
           const int4 k1 = *reinterpret_cast<const int4*>(kpp + 4);
-          const int kv[8] = {k0.x, k0.y, k0.z, k0.w, k1.x, k1.y, k1.z, k1.w};
-#pragma unroll
-          for (int j = 0; j < 8; ++j) ok[j] = kv[j] >= ql && kv[j] <= qp;
-        } else {
-#pragma unroll
-          for (int j = 0; j < 8; ++j) ok[j] = true;
+          kv[0] = k0.x; kv[1] = k0.y; kv[2] = k0.z; kv[3] = k0.w;
+          kv[4] = k1.x; kv[5] = k1.y; kv[6] = k1.z; kv[7] = k1.w;
         }
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int r = 8 * gg + j;
-          const float pr = ok[j] ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], p.c2, nl2)) : 0.f;
-          db[gg][j] = (__bf16)(pr * (dp[r] - dl));
-        }
-      }
-      // dQ^T += K^T dS^T
+        for (int j = 0; j < 8; j += 2) {
+          float pr[2], ds[2];
 #pragma unroll
-      for (int gg = 0; gg < 2; ++gg) {
-        const int kg = 2 * sub + gg;
-#pragma unroll
-        for (int t = 0; t < C::DT; ++t) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(kt_t + taddr[kg] + t * 32 * C::TROW);
-          dqa[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, db[gg], dqa[t], 0, 0, 0);
+          for (int e = 0; e < 2; ++e) {
+            const int r = 8 * gg + j + e;
+            pr[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], p.c2, nl2));
+            if (MASKED) pr[e] = (kv[j + e] >= ql && kv[j + e] <= qp) ? pr[e] : 0.f;
+            ds[e] = pr[e] * (dp[r] - dl);
+          }
+          const bf16x2 dd = __builtin_convertvector((f32x2){ds[0], ds[1]}, bf16x2);
+          db[gg][j] = dd[0];
+          db[gg][j + 1] = dd[1];
         }
       }
-    }
+    };
+    if (full) probs(std::integral_constant<bool, false>{});
+    else probs(std::integral_constant<bool, true>{});
+    // dQ^T += K^T dS^T over the half tile's 32 keys.
+    const lds_char* kt0 = to_lds(kbuf(bc)) + launder(tP[0] + sub * 32 * C::ROW);
+    const lds_char* kt1 = to_lds(kbuf(bc)) + launder(tP[1] + sub * 32 * C::ROW);
+#pragma unroll
+    for (int gg = 0; gg < 2; ++gg)
+#pragma unroll
+      for (int t = 0; t < C::DT; ++t) {
+        const int o = gg * 16 * C::ROW + ((64 * t) ^ tA);
+        const bf16x8 a = lds_read_tr(kt0 + o, kt1 + o);
+        dqa[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, db[gg], dqa[t], 0, 0, 0);
+      }
   };
 
   const int total = p.cp * p.tpr;
@@ -753,15 +783,31 @@ __global__ __launch_bounds__(512, 1) void dq_kernel(BParams p) {
     const int cnt = build_key_list<kKT, NW>(p.kbounds, p.tpr, p.rank, p.cp, u0, min(total, u0 + C::LIST), tid, wave,
                                             lane, sWb, sList, sCnt);
     if (cnt == 0) continue;
-    issue(0, __builtin_amdgcn_readfirstlane(sList[0].x));
+    auto ent = [&](int j) {
+      int2 e;
+      e.x = __builtin_amdgcn_readfirstlane(sList[j].x);
+      e.y = __builtin_amdgcn_readfirstlane(sList[j].y);
+      return e;
+    };
+    const std::integral_constant<int, 0> b0{};
+    const std::integral_constant<int, 1> b1{};
+    issue(b0, ent(0).x);
     wait_vmem();
     __syncthreads();
-    for (int j = 0; j < cnt; ++j) {
-      const int cur = j & 1;
-      if (j + 1 < cnt) issue(cur ^ 1, __builtin_amdgcn_readfirstlane(sList[j + 1].x));
-      compute(cur, (int)(((unsigned)__builtin_amdgcn_readfirstlane(sList[j].y) >> csh) & 3));
+    // Tile j from buffer B while tile j+1 is copied into the other buffer.
+    auto tile = [&](auto bc, int j) {
+      if (j + 1 < cnt) issue(std::integral_constant<int, 1 - decltype(bc)::value>{}, ent(j + 1).x);
+      const int cls = (int)(((unsigned)ent(j).y >> csh) & 3);
+      if (cls != kSkip) {
+#pragma nounroll
+        for (int sub = 0; sub < 2; ++sub) half(bc, sub, cls == kFull);
+      }
       wait_vmem();
       __syncthreads();
+    };
+    for (int j = 0; j < cnt; j += 2) {
+      tile(b0, j);
+      if (j + 1 < cnt) tile(b1, j + 1);
     }
   }
 
@@ -795,7 +841,6 @@ hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
   p.k_pos = a.k_pos;
   p.kbounds = reinterpret_cast<const int4*>(ws + w.kbounds_off);
   p.kpos_pad = reinterpret_cast<const int*>(ws + w.kpos_off);
-  p.kt = ws + w.kt_off;
   p.qbounds = reinterpret_cast<const int4*>(ws + w.qbounds_off);
   p.qlo_pad = reinterpret_cast<const int*>(ws + w.qlo_off);
   p.qspan_pad = reinterpret_cast<const int*>(ws + w.qspan_off);
@@ -813,7 +858,6 @@ hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
   p.v_sb = a.v_str[0];
   p.v_sh = a.v_str[1];
   p.v_ss = a.v_str[2];
-  p.kt_row = w.kt_row;
   p.sq_pad = (int)w.sq_pad;
   p.B = a.b;
   p.Hq = a.hq;
@@ -829,9 +873,8 @@ hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
   p.scale = a.scale;
   const int ntiles = a.cp * p.tpr;
   if (ntiles > 0) {
-    hipLaunchKernelGGL((key_prep_kernel<D>), dim3(ntiles, a.b * a.hkv), dim3(256), 0, stream, p,
-                       reinterpret_cast<int4*>(ws + w.kbounds_off), reinterpret_cast<int*>(ws + w.kpos_off),
-                       reinterpret_cast<__bf16*>(ws + w.kt_off));
+    hipLaunchKernelGGL(key_prep_kernel, dim3(ntiles), dim3(64), 0, stream, p,
+                       reinterpret_cast<int4*>(ws + w.kbounds_off), reinterpret_cast<int*>(ws + w.kpos_off));
     if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
   }
   hipLaunchKernelGGL(query_prep_kernel, dim3(p.nqt, a.b * a.hq), dim3(64), 0, stream, p, a.lse, a.delta,

@@ -88,14 +88,13 @@ constexpr int kBwdTile = 64;
 struct BwdWorkspace {
   size_t kbounds_off;  // int4 per key tile: {min pos, max pos, valid rows, 0}
   size_t kpos_off;     // int32 per key slot, padding = INT32_MAX
-  size_t kt_off;       // bf16 K^T [b][hkv][d][kt_row]
   size_t qbounds_off;  // int4 per query tile: {min pos, max pos, min lo, max lo}
   size_t qlo_off;      // int32 [sq_pad]: document start, padding = INT32_MIN
   size_t qspan_off;    // int32 [sq_pad]: position - document start, padding = 0
   size_t nl2_off;      // fp32 [b][hq][sq_pad]: -LSE * log2(e)
   size_t dlt_off;      // fp32 [b][hq][sq_pad]: delta
   size_t total;
-  int64_t kt_row;      // cp * ceil((sk / cp) / 64) * 64
+  int64_t kt_row;      // key slots: cp * ceil((sk / cp) / 64) * 64
   int64_t sq_pad;      // ceil(sq / 64) * 64
 };
 

@@ -261,9 +261,11 @@ def test_ring_bwd_rejects_bad_args():
 def test_bwd_workspace_query():
     s = _shape(sk=131072, sq=16384, hq=32, hkv=8)
     n = cpa.lib().cp_attn_bwd_workspace(ctypes.byref(s), 8)
-    # K^T (8 kv heads) in bf16, plus per-row tables
-    kt = 8 * 128 * 131072 * 2
-    assert kt <= n < kt + (8 << 20)
+    # per-row tables (-LSE log2 e and delta for 32 heads x 16384 rows, document
+    # start and span) and per-key tables (bounds, padded positions)
+    rows = 2 * 32 * 16384 * 4 + 2 * 16384 * 4
+    keys = 131072 * 4
+    assert rows + keys <= n < rows + keys + (1 << 20)
     assert cpa.lib().cp_attn_bwd_workspace(ctypes.byref(_shape(d=96)), 8) == 0
 
 
