@@ -52,7 +52,7 @@ struct BParams {
   const int* qlo_pad;    // per query slot [sq_pad]: document start (padding INT_MIN)
   const int* qspan_pad;  // position - document start (padding 0)
   const float* nl2;      // [b][hq][sq_pad]: -LSE * log2(e), 0 in padding
-  const float* dlt;      // [b][hq][sq_pad]: delta, 0 in padding
+  const float* dlt;      // [b][hq][sq_pad]: -delta, 0 in padding
   float* dq;             // fp32 [b, hq, sq, d] contiguous, accumulated
   float* dk;             // fp32 [b, hkv, sk, d] contiguous, accumulated
   float* dv;
@@ -109,7 +109,7 @@ __global__ __launch_bounds__(64) void query_prep_kernel(BParams p, const float* 
   }
   const long long idx = (long long)bh * p.sq + r0 + tid;
   nl2[(long long)bh * p.sq_pad + r0 + tid] = ok ? -lse[idx] * kLog2e : 0.f;
-  dlt[(long long)bh * p.sq_pad + r0 + tid] = ok ? delta[idx] : 0.f;
+  dlt[(long long)bh * p.sq_pad + r0 + tid] = ok ? -delta[idx] : 0.f;
 }
 
 // delta_q = sum_d dO[q, d] * O[q, d]; one half-wave (32 lanes) per row.
@@ -192,8 +192,10 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(BParams p) {
   __shared__ __attribute__((aligned(1024))) char sQ1[C::TILE];
   __shared__ __attribute__((aligned(1024))) char sO0[C::TILE];
   __shared__ __attribute__((aligned(1024))) char sO1[C::TILE];
-  __shared__ __attribute__((aligned(1024))) char sV[C::VTILE];
-  // Per row of each buffered tile: -LSE*log2(e), delta, document start, span.
+  // The smaller alignment places V after the four tiles, which then lie in the
+  // first 64 KiB, where a tile read's constant part fits the DS offset field.
+  __shared__ __attribute__((aligned(16))) char sV[C::VTILE];
+  // Per row of each buffered tile: -LSE*log2(e), -delta, document start, span.
   __shared__ __attribute__((aligned(16))) float sR0[4][kQT];
   __shared__ __attribute__((aligned(16))) float sR1[4][kQT];
   __shared__ int2 sList[C::LIST];
@@ -290,6 +292,27 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(BParams p) {
       tA = 64 * (f >> 2);  // the same for both h
     }
   }
+  // A row read of the loop is a per-lane offset yo[kk] plus a constant
+  // (buffer address, half-tile and dO offsets) that the DS offset field holds;
+  // a transposed read adds (64 t) ^ tA to tP[h] first.  These offsets pass
+  // through an empty asm, in place, at the start of each half tile, so that
+  // the compiler does not hoist offset + constant out of the loop as one
+  // register per read.  V and the per-row arrays lie above 64 KiB: their
+  // offsets carry the expected array address, which a constant in the read
+  // subtracts again (another placement only costs an add per read).
+  int yo[C::KREG];   // row reads: nrow*ROW + ((32 kk) ^ nY)
+#pragma unroll
+  for (int kk = 0; kk < C::KREG; ++kk) yo[kk] = nrow * C::ROW + ((32 * kk) ^ nY);
+  constexpr int kVAt = 4 * C::TILE;            // expected address of sV
+  constexpr int kRAt = 4 * C::TILE + C::VTILE;  // expected address of sR0
+  int vo = vbase + kVAt;
+  int ro8 = 32 * hi + kRAt;  // rows 8hi.. of the per-row arrays
+  auto refresh = [&]() {
+#pragma unroll
+    for (int kk = 0; kk < C::KREG; ++kk) asm volatile("" : "+v"(yo[kk]));
+    asm volatile("" : "+v"(tP[0]), "+v"(tP[1]), "+v"(tA));
+    asm volatile("" : "+v"(vo), "+v"(ro8));
+  };
 
   // ---- list of (query head, query tile) pairs this workgroup needs ---------
   // Entry .x = t | hg << 16 for tile t of query head kvh*g + hg; .y = class of
@@ -384,41 +407,38 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(BParams p) {
     }
   };
 
-  // Lane offsets pass through an empty asm where they are used so that lane
-  // offset + constant is not hoisted out of the loop as one register per read:
-  // every read is then buffer + lane offset + a DS offset immediate, and the
-  // buffer it reads stays visible to the compiler.
-  auto launder = [](int off) {
-    asm volatile("" : "+v"(off));
-    return off;
-  };
-
   // One half tile (sub) of the tile in buffer buf: S/dP, P/dS, dV/dK.  On
   // partial tiles key kp is allowed for a row iff kp - lo <= span as unsigned
   // numbers (span = pos - lo; padding rows have zero Q and dO rows and add
   // nothing); full tiles skip the test.
   auto half = [&](auto bc, int sub, bool full) {
-    const int no = launder(nrow * C::ROW + sub * 32 * C::ROW);
-    const lds_char* qn = to_lds(qbuf(bc)) + no;
-    const lds_char* on = to_lds(obuf(bc)) + no;
-    const lds_char* vn = to_lds(sV) + launder(vbase);
+    refresh();
+    const lds_char* qn = to_lds(qbuf(bc)) + sub * 32 * C::ROW;
+    const lds_char* on = to_lds(obuf(bc)) + sub * 32 * C::ROW;
+    const lds_char* vn = to_lds(sV) + (vo - kVAt);
+    const lds_char* rowb = to_lds(rbuf(bc)) + (ro8 - kRAt) + 32 * sub * 4;
     // S = Q K^T, dP = dO V^T: register r is query row 32sub + 16(r/8) + 8hi + r%8.
+    // dP starts from -delta of its row, so that it ends as dP - delta.
     f32x16 s, dp;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      s[r] = 0.f;
-      dp[r] = 0.f;
+    for (int r = 0; r < 16; ++r) s[r] = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {  // registers 4i..4i+3: rows 16(i/2) + 4(i%2) + 0..3 of the lane's 8
+      const f32x4 v = *(const __attribute__((address_space(3))) f32x4*)(rowb + kQT * 4 +
+                                                                         (16 * (i >> 1) + 4 * (i & 1)) * 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dp[4 * i + e] = v[e];
     }
     // Operands are read one d-slice ahead.
     bf16x8 aq[2], ao[2], bv[2];
-    aq[0] = lds_read8(qn + nY);
-    ao[0] = lds_read8(on + nY);
+    aq[0] = lds_read8(qn + yo[0]);
+    ao[0] = lds_read8(on + yo[0]);
     bv[0] = lds_read8(vn);
 #pragma unroll
     for (int kk = 0; kk < C::KREG; ++kk) {
       if (kk + 1 < C::KREG) {
-        aq[(kk + 1) & 1] = lds_read8(qn + (nY ^ (32 * (kk + 1))));
-        ao[(kk + 1) & 1] = lds_read8(on + (nY ^ (32 * (kk + 1))));
+        aq[(kk + 1) & 1] = lds_read8(qn + yo[kk + 1]);
+        ao[(kk + 1) & 1] = lds_read8(on + yo[kk + 1]);
         bv[(kk + 1) & 1] = lds_read8(vn + (kk + 1) * 2 * kVColBytes);
       }
       s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq[kk & 1], kreg[kk], s, 0, 0, 0);
@@ -427,7 +447,6 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(BParams p) {
     // P = exp2(c2 s - LSE log2 e) on allowed pairs, dS = P (dP - delta).  Only
     // this vector part differs between partial and full tiles; the MFMAs around
     // it exist once, so their accumulators stay in place.
-    const lds_char* rowb = to_lds(rbuf(bc)) + launder((32 * sub + 8 * hi) * 4);
     bf16x8 pb[2], db[2];
     auto probs = [&](auto maskc) {
       constexpr bool MASKED = decltype(maskc)::value;
@@ -435,7 +454,6 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(BParams p) {
       for (int i = 0; i < 4; ++i) {  // values 4i..4i+3: rows 16(i/2) + 4(i%2) + 0..3 of the lane's 8
         const int ro = (16 * (i >> 1) + 4 * (i & 1)) * 4;
         const f32x4 nl = *(const __attribute__((address_space(3))) f32x4*)(rowb + ro);
-        const f32x4 dl = *(const __attribute__((address_space(3))) f32x4*)(rowb + kQT * 4 + ro);
         // Integer arrays are read as integer vectors: a bit_cast of one element
         // of a float vector is avoided (clang has been seen to read element 0
         // for it whatever the index).
@@ -450,7 +468,7 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(BParams p) {
           const int x = 4 * i + e;
           pr[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[x], p.c2, nl[e]));
           if (MASKED) pr[e] = ((unsigned)kp - lo[e] <= sp[e]) ? pr[e] : 0.f;
-          ds[e] = pr[e] * (dp[x] - dl[e]);
+          ds[e] = pr[e] * dp[x];
         }
 #pragma unroll
         for (int e = 0; e < 4; e += 2) {
@@ -467,23 +485,21 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(BParams p) {
     if (full) probs(std::integral_constant<bool, false>{});
     else probs(std::integral_constant<bool, true>{});
     // dV^T += dO^T P, dK^T += Q^T dS over the half tile's 32 query rows.
-    const int t0 = launder(tP[0] + sub * 32 * C::ROW), t1 = launder(tP[1] + sub * 32 * C::ROW);
-    const lds_char* qt0 = to_lds(qbuf(bc)) + t0;
-    const lds_char* qt1 = to_lds(qbuf(bc)) + t1;
-    const lds_char* ot0 = to_lds(obuf(bc)) + t0;
-    const lds_char* ot1 = to_lds(obuf(bc)) + t1;
     constexpr int NG = 2 * C::DT;  // (gg, t) pairs
-    // Byte offset of pair m = DT*gg + t: rows +16gg, chunk group t.
-    auto toff = [&](int m) { return (m / C::DT) * 16 * C::ROW + ((64 * (m % C::DT)) ^ tA); };
+    // Pair m = DT*gg + t: rows +16gg, chunk group t.
+    auto trd = [&](auto buf, int m) {
+      const lds_char* b = to_lds(buf) + sub * 32 * C::ROW + (m / C::DT) * 16 * C::ROW;
+      const int xa = (64 * (m % C::DT)) ^ tA;
+      return lds_read_tr(b + (tP[0] + xa), b + (tP[1] + xa));
+    };
     bf16x8 to[2], tq[2];
-    to[0] = lds_read_tr(ot0 + toff(0), ot1 + toff(0));
-    tq[0] = lds_read_tr(qt0 + toff(0), qt1 + toff(0));
+    to[0] = trd(obuf(bc), 0);
+    tq[0] = trd(qbuf(bc), 0);
 #pragma unroll
     for (int m = 0; m < NG; ++m) {
       if (m + 1 < NG) {
-        const int o = toff(m + 1);
-        to[(m + 1) & 1] = lds_read_tr(ot0 + o, ot1 + o);
-        tq[(m + 1) & 1] = lds_read_tr(qt0 + o, qt1 + o);
+        to[(m + 1) & 1] = trd(obuf(bc), m + 1);
+        tq[(m + 1) & 1] = trd(qbuf(bc), m + 1);
       }
       const int t = m % C::DT, gg = m / C::DT;
       dva[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(to[m & 1], pb[gg], dva[t], 0, 0, 0);
@@ -511,8 +527,8 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(BParams p) {
       if (j + 1 < cnt) issue(std::integral_constant<int, 1 - decltype(bc)::value>{}, ent(j + 1).x);
       const int cls = (int)(((unsigned)ent(j).y >> csh) & 3);
       if (cls != kSkip) {
-#pragma nounroll
-        for (int sub = 0; sub < 2; ++sub) half(bc, sub, cls == kFull);
+        half(bc, 0, cls == kFull);
+        half(bc, 1, cls == kFull);
       }
       wait_vmem();
       __syncthreads();
@@ -625,7 +641,7 @@ __global__ __launch_bounds__(512, 1) void dq_kernel(BParams p) {
   const int qp = valid ? p.q_pos[row] : -1;
   const int ql = valid ? (p.q_lo ? p.q_lo[row] : 0) : INT_MAX;
   const float nl2 = valid ? p.nl2[bh * p.sq_pad + row] : 0.f;
-  const float dl = valid ? p.dlt[bh * p.sq_pad + row] : 0.f;
+  const float ndl = valid ? p.dlt[bh * p.sq_pad + row] : 0.f;
   {
     const int a = wave_min(valid ? qp : INT_MAX), bb = wave_max(valid ? qp : INT_MIN);
     const int c = wave_min(valid ? ql : INT_MAX), d = wave_max(valid ? ql : INT_MIN);
@@ -754,7 +770,7 @@ __global__ __launch_bounds__(512, 1) void dq_kernel(BParams p) {
             const int r = 8 * gg + j + e;
             pr[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], p.c2, nl2));
             if (MASKED) pr[e] = (kv[j + e] >= ql && kv[j + e] <= qp) ? pr[e] : 0.f;
-            ds[e] = pr[e] * (dp[r] - dl);
+            ds[e] = pr[e] * (dp[r] + ndl);
           }
           const bf16x2 dd = __builtin_convertvector((f32x2){ds[0], ds[1]}, bf16x2);
           db[gg][j] = dd[0];
