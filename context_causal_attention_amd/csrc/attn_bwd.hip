@@ -51,7 +51,7 @@ struct BParams {
   const int4* qbounds;   // per 64-row query tile {min pos, max pos, min lo, max lo}
   const int* qlo_pad;    // per query slot [sq_pad]: document start (padding INT_MIN)
   const int* qspan_pad;  // position - document start (padding 0)
-  const float* nl2;      // [b][hq][sq_pad]: -LSE * log2(e), 0 in padding
+  const float* nl2;      // [b][hq][sq_pad]: -LSE * log2(e), 0 in padding and where LSE = -inf
   const float* dlt;      // [b][hq][sq_pad]: -delta, 0 in padding
   float* dq;             // fp32 [b, hq, sq, d] contiguous, accumulated
   float* dk;             // fp32 [b, hkv, sk, d] contiguous, accumulated
@@ -108,7 +108,10 @@ __global__ __launch_bounds__(64) void query_prep_kernel(BParams p, const float* 
     qspan_pad[r0 + tid] = ok ? (int)((unsigned)qp - (unsigned)ql) : 0;
   }
   const long long idx = (long long)bh * p.sq + r0 + tid;
-  nl2[(long long)bh * p.sq_pad + r0 + tid] = ok ? -lse[idx] * kLog2e : 0.f;
+  // A row without any allowed key (LSE = -inf) gets 0 rather than +inf: the
+  // score kernels mask with a -inf score, and -inf * c + inf would be NaN.
+  const float l = ok ? lse[idx] : 0.f;
+  nl2[(long long)bh * p.sq_pad + r0 + tid] = (ok && l != -__builtin_inff()) ? -l * kLog2e : 0.f;
   dlt[(long long)bh * p.sq_pad + r0 + tid] = ok ? -delta[idx] : 0.f;
 }
 
@@ -407,10 +410,7 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(BParams p) {
     }
   };
 
-  // One half tile (sub) of the tile in buffer buf: S/dP, P/dS, dV/dK.  On
-  // partial tiles key kp is allowed for a row iff kp - lo <= span as unsigned
-  // numbers (span = pos - lo; padding rows have zero Q and dO rows and add
-  // nothing); full tiles skip the test.
+  // One half tile (sub) of the tile in buffer buf: S/dP, P/dS, dV/dK.
   auto half = [&](auto bc, int sub, bool full) {
     refresh();
     const lds_char* qn = to_lds(qbuf(bc)) + sub * 32 * C::ROW;
@@ -418,10 +418,28 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(BParams p) {
     const lds_char* vn = to_lds(sV) + (vo - kVAt);
     const lds_char* rowb = to_lds(rbuf(bc)) + (ro8 - kRAt) + 32 * sub * 4;
     // S = Q K^T, dP = dO V^T: register r is query row 32sub + 16(r/8) + 8hi + r%8.
-    // dP starts from -delta of its row, so that it ends as dP - delta.
+    // dP starts from -delta of its row, so that it ends as dP - delta.  S
+    // starts at 0, or on partial tiles at -inf for the pairs the mask removes
+    // (key kp is allowed for a row iff kp - lo <= span as unsigned numbers,
+    // span = pos - lo), which makes P = 0 there: the vector part after the
+    // MFMAs is the same for every tile and shares a basic block with them.
+    // Padding rows (span 0, lo INT_MIN) are masked; integer arrays are read
+    // as integer vectors (a bit_cast of one element of a float vector has been
+    // seen to read element 0 whatever the index).
     f32x16 s, dp;
+    if (full) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) s[r] = 0.f;
+      for (int r = 0; r < 16; ++r) s[r] = 0.f;
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int ro = (16 * (i >> 1) + 4 * (i & 1)) * 4;
+        const u32x4 lo = *(const __attribute__((address_space(3))) u32x4*)(rowb + 2 * kQT * 4 + ro);
+        const u32x4 sp = *(const __attribute__((address_space(3))) u32x4*)(rowb + 3 * kQT * 4 + ro);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) s[4 * i + e] = ((unsigned)kp - lo[e] <= sp[e]) ? 0.f : -__builtin_inff();
+      }
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {  // registers 4i..4i+3: rows 16(i/2) + 4(i%2) + 0..3 of the lane's 8
       const f32x4 v = *(const __attribute__((address_space(3))) f32x4*)(rowb + kQT * 4 +
@@ -444,46 +462,30 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(BParams p) {
       s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq[kk & 1], kreg[kk], s, 0, 0, 0);
       dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ao[kk & 1], bv[kk & 1], dp, 0, 0, 0);
     }
-    // P = exp2(c2 s - LSE log2 e) on allowed pairs, dS = P (dP - delta).  Only
-    // this vector part differs between partial and full tiles; the MFMAs around
-    // it exist once, so their accumulators stay in place.
+    // P = exp2(c2 s - LSE log2 e), dS = P (dP - delta).
     bf16x8 pb[2], db[2];
-    auto probs = [&](auto maskc) {
-      constexpr bool MASKED = decltype(maskc)::value;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {  // values 4i..4i+3: rows 16(i/2) + 4(i%2) + 0..3 of the lane's 8
-        const int ro = (16 * (i >> 1) + 4 * (i & 1)) * 4;
-        const f32x4 nl = *(const __attribute__((address_space(3))) f32x4*)(rowb + ro);
-        // Integer arrays are read as integer vectors: a bit_cast of one element
-        // of a float vector is avoided (clang has been seen to read element 0
-        // for it whatever the index).
-        u32x4 lo = {0, 0, 0, 0}, sp = {0, 0, 0, 0};
-        if (MASKED) {
-          lo = *(const __attribute__((address_space(3))) u32x4*)(rowb + 2 * kQT * 4 + ro);
-          sp = *(const __attribute__((address_space(3))) u32x4*)(rowb + 3 * kQT * 4 + ro);
-        }
-        float pr[4], ds[4];
+    for (int i = 0; i < 4; ++i) {  // values 4i..4i+3: rows 16(i/2) + 4(i%2) + 0..3 of the lane's 8
+      const int ro = (16 * (i >> 1) + 4 * (i & 1)) * 4;
+      const f32x4 nl = *(const __attribute__((address_space(3))) f32x4*)(rowb + ro);
+      float pr[4], ds[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int x = 4 * i + e;
-          pr[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[x], p.c2, nl[e]));
-          if (MASKED) pr[e] = ((unsigned)kp - lo[e] <= sp[e]) ? pr[e] : 0.f;
-          ds[e] = pr[e] * dp[x];
-        }
-#pragma unroll
-        for (int e = 0; e < 4; e += 2) {
-          const bf16x2 pp = __builtin_convertvector((f32x2){pr[e], pr[e + 1]}, bf16x2);
-          const bf16x2 dd = __builtin_convertvector((f32x2){ds[e], ds[e + 1]}, bf16x2);
-          const int j = 4 * (i & 1) + e;
-          pb[i >> 1][j] = pp[0];
-          pb[i >> 1][j + 1] = pp[1];
-          db[i >> 1][j] = dd[0];
-          db[i >> 1][j + 1] = dd[1];
-        }
+      for (int e = 0; e < 4; ++e) {
+        const int x = 4 * i + e;
+        pr[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[x], p.c2, nl[e]));
+        ds[e] = pr[e] * dp[x];
       }
-    };
-    if (full) probs(std::integral_constant<bool, false>{});
-    else probs(std::integral_constant<bool, true>{});
+#pragma unroll
+      for (int e = 0; e < 4; e += 2) {
+        const bf16x2 pp = __builtin_convertvector((f32x2){pr[e], pr[e + 1]}, bf16x2);
+        const bf16x2 dd = __builtin_convertvector((f32x2){ds[e], ds[e + 1]}, bf16x2);
+        const int j = 4 * (i & 1) + e;
+        pb[i >> 1][j] = pp[0];
+        pb[i >> 1][j + 1] = pp[1];
+        db[i >> 1][j] = dd[0];
+        db[i >> 1][j + 1] = dd[1];
+      }
+    }
     // dV^T += dO^T P, dK^T += Q^T dS over the half tile's 32 query rows.
     constexpr int NG = 2 * C::DT;  // (gg, t) pairs
     // Pair m = DT*gg + t: rows +16gg, chunk group t.
