@@ -736,12 +736,26 @@ __global__ __launch_bounds__(512, 1) void dq_kernel(BParams p) {
     const int no = launder(nrow * C::ROW + sub * 32 * C::ROW);
     const lds_char* kn = to_lds(kbuf(bc)) + no;
     const lds_char* vn = to_lds(vbuf(bc)) + no;
-    // S^T, dP^T: register r is key 32sub + 16(r/8) + 8hi + r%8.
+    // S^T, dP^T: register r is key 32sub + 16(r/8) + 8hi + r%8.  S^T starts
+    // at 0, or on partial tiles at -inf for the keys outside [q_lo, q_pos] of
+    // the lane's row, which makes P = 0 there: the vector part after the MFMAs
+    // is the same for every tile and shares a basic block with them.
     f32x16 s, dp;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      s[r] = 0.f;
-      dp[r] = 0.f;
+    for (int r = 0; r < 16; ++r) dp[r] = 0.f;
+    if (full) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[r] = 0.f;
+    } else {
+#pragma unroll
+      for (int gg = 0; gg < 2; ++gg) {
+        const int* kpp = pbuf(bc) + 32 * sub + 16 * gg + 8 * hi;
+        const int4 k0 = *reinterpret_cast<const int4*>(kpp);
+        const int4 k1 = *reinterpret_cast<const int4*>(kpp + 4);
+        const int kv[8] = {k0.x, k0.y, k0.z, k0.w, k1.x, k1.y, k1.z, k1.w};
+#pragma unroll
+        for (int j = 0; j < 8; ++j) s[8 * gg + j] = (kv[j] >= ql && kv[j] <= qp) ? 0.f : -__builtin_inff();
+      }
     }
 #pragma unroll
     for (int kk = 0; kk < C::QREG; ++kk) {
@@ -750,38 +764,23 @@ __global__ __launch_bounds__(512, 1) void dq_kernel(BParams p) {
       s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, qreg[kk], s, 0, 0, 0);
       dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, oreg[kk], dp, 0, 0, 0);
     }
-    // dS^T = P^T (dP^T - delta), P^T = exp2(c2 s - LSE log2 e) on allowed keys.
+    // dS^T = P^T (dP^T - delta), P^T = exp2(c2 s - LSE log2 e).
     bf16x8 db[2];
-    auto probs = [&](auto maskc) {
-      constexpr bool MASKED = decltype(maskc)::value;
 #pragma unroll
-      for (int gg = 0; gg < 2; ++gg) {
-        int kv[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-        if (MASKED) {
-          const int* kpp = pbuf(bc) + 32 * sub + 16 * gg + 8 * hi;
-          const int4 k0 = *reinterpret_cast<const int4*>(kpp);
-          const int4 k1 = *reinterpret_cast<const int4*>(kpp + 4);
-          kv[0] = k0.x; kv[1] = k0.y; kv[2] = k0.z; kv[3] = k0.w;
-          kv[4] = k1.x; kv[5] = k1.y; kv[6] = k1.z; kv[7] = k1.w;
+    for (int gg = 0; gg < 2; ++gg) {
+#pragma unroll
+      for (int j = 0; j < 8; j += 2) {
+        float ds[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const int r = 8 * gg + j + e;
+          ds[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], p.c2, nl2)) * (dp[r] + ndl);
         }
-#pragma unroll
-        for (int j = 0; j < 8; j += 2) {
-          float pr[2], ds[2];
-#pragma unroll
-          for (int e = 0; e < 2; ++e) {
-            const int r = 8 * gg + j + e;
-            pr[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], p.c2, nl2));
-            if (MASKED) pr[e] = (kv[j + e] >= ql && kv[j + e] <= qp) ? pr[e] : 0.f;
-            ds[e] = pr[e] * (dp[r] + ndl);
-          }
-          const bf16x2 dd = __builtin_convertvector((f32x2){ds[0], ds[1]}, bf16x2);
-          db[gg][j] = dd[0];
-          db[gg][j + 1] = dd[1];
-        }
+        const bf16x2 dd = __builtin_convertvector((f32x2){ds[0], ds[1]}, bf16x2);
+        db[gg][j] = dd[0];
+        db[gg][j + 1] = dd[1];
       }
-    };
-    if (full) probs(std::integral_constant<bool, false>{});
-    else probs(std::integral_constant<bool, true>{});
+    }
     // dQ^T += K^T dS^T over the half tile's 32 keys.
     const lds_char* kt0 = to_lds(kbuf(bc)) + launder(tP[0] + sub * 32 * C::ROW);
     const lds_char* kt1 = to_lds(kbuf(bc)) + launder(tP[1] + sub * 32 * C::ROW);

@@ -51,6 +51,7 @@ __all__ = [
     "lse_merge",
     "bwd_delta",
     "attention_bwd",
+    "partial_attention_bwd",
     "ring_partials_fwd",
     "attention_matrix_bytes",
 ]
@@ -301,6 +302,42 @@ def attention_bwd(q, k, v, dout, scale, cu_seqlens=None, rows=None, row_block=51
                 dS = P * (dP - delta[b, h, s0:s0 + len(r)][:, None])
                 dq[b, h, s0:s0 + len(r)] = scale * (dS @ k[b, kvh, kmin:kmax])
                 dk[b, kvh, kmin:kmax] += scale * (dS.T @ q[b, h, r])
+    return dq, dk, dv
+
+
+def partial_attention_bwd(q_rows, k_rows, v_rows, dout, lse, delta, scale, q_pos, q_lo, k_pos):
+    """One ring step's share of the gradients, given each row's LSE and delta
+    (those of the merged output when the steps of a ring are summed, or those
+    of this step's own output for the gradient of one step alone).
+
+    P_ij = exp(s_ij - LSE_i) on allowed pairs, 0 elsewhere (a row whose LSE is
+    -inf has no allowed key and gets P = 0); dV_j = sum_i P_ij dO_i ;
+    dS_ij = P_ij (dO_i . v_j - delta_i) ; dQ_i = scale sum_j dS_ij k_j ;
+    dK_j = scale sum_i dS_ij q_i ; dK and dV of a key/value head sum over the
+    query heads that read it.
+
+    q_rows, dout: [B, Hq, nq, d]; k_rows, v_rows: [B, Hkv, nk, d]; lse, delta:
+    [B, Hq, nq].  Returns dq [B, Hq, nq, d] and dk, dv [B, Hkv, nk, d].
+    """
+    q, k, v, do = _as64(q_rows), _as64(k_rows), _as64(v_rows), _as64(dout)
+    L, dl = _as64(lse), _as64(delta)
+    B, Hq, nq, d = q.shape
+    Hkv = k.shape[1]
+    g = Hq // Hkv
+    ok = allowed_mask(q_pos, q_lo, k_pos)
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    for b in range(B):
+        for h in range(Hq):
+            kvh = h // g
+            s = scale * (q[b, h] @ k[b, kvh].T)
+            use = ok & np.isfinite(L[b, h])[:, None]
+            P = np.where(use, np.exp(np.where(use, s - L[b, h][:, None], 0.0)), 0.0)
+            dv[b, kvh] += P.T @ do[b, h]
+            dS = P * (do[b, h] @ v[b, kvh].T - dl[b, h][:, None])
+            dq[b, h] = scale * (dS @ k[b, kvh])
+            dk[b, kvh] += scale * (dS.T @ q[b, h])
     return dq, dk, dv
 
 

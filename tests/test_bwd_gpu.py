@@ -168,6 +168,38 @@ def test_partial_bwd_steps_match_ring():
         _check_grads((dq, dk, dv), R.oracle_grads(), f"partial steps rank {rank}")
 
 
+def test_partial_bwd_rows_without_keys():
+    """One ring step alone, with the step's own LSE and delta: rank 0 of cp=2
+    (positions 0..255 and 768..1023 of 1024) against keys at positions
+    100..611.  Rows 0..99 have no allowed key (LSE -inf), rows 100..255 some,
+    and query tiles mix both kinds; the gradients must be finite, zero in dQ
+    for the rows without keys, and match the oracle's per-step backward."""
+    B, Hq, Hkv, S, d, cp = 1, 4, 2, 1024, 128, 2
+    q, k, v, do = si.make_qkv(B, Hq, Hkv, S, d, "bf16", seed=9, with_dout=True)
+    rows = orc.zigzag_positions(S, cp, 0)
+    keys = np.arange(100, 612)
+    scale = 1.0 / math.sqrt(d)
+    announce("partial bwd, rows without keys")
+    ri, ki = torch.from_numpy(rows.astype(np.int64)), torch.from_numpy(keys)
+    qg, dog = q.index_select(2, ri).cuda(), do.index_select(2, ri).cuda()
+    kg, vg = k.index_select(2, ki).cuda(), v.index_select(2, ki).cuda()
+    o, lse = cpa.cp_attn_partial_fwd(qg, kg, vg, rows, None, keys, scale=scale)
+    none = rows < 100
+    assert torch.isneginf(lse[:, :, torch.from_numpy(none).cuda()]).all()
+    delta = cpa.cp_attn_bwd_delta(dog, o)
+    dq, dk, dv = cpa.cp_attn_partial_bwd(qg, kg, vg, dog, lse, delta, rows, None, keys, scale=scale)
+    torch.cuda.synchronize()
+    for t in (dq, dk, dv):
+        assert torch.isfinite(t).all()
+    assert torch.all(dq[:, :, torch.from_numpy(none).cuda()] == 0)
+    q64, k64, v64, do64 = (x.double().numpy() for x in (q, k, v, do))
+    O_ref, L_ref = orc.partial_attention_fwd(q64[:, :, rows], k64[:, :, keys], v64[:, :, keys], scale, rows,
+                                             np.zeros_like(rows), keys)
+    ref = orc.partial_attention_bwd(q64[:, :, rows], k64[:, :, keys], v64[:, :, keys], do64[:, :, rows], L_ref,
+                                    orc.bwd_delta(do64[:, :, rows], O_ref), scale, rows, np.zeros_like(rows), keys)
+    _check_grads((dq, dk, dv), ref, "partial bwd rows without keys")
+
+
 def test_bwd_accumulates_and_is_deterministic():
     """Calls add into the gradient buffers: a second identical call doubles
     them exactly, and two fresh runs agree bit for bit."""

@@ -236,6 +236,84 @@ def test_delta_is_rowwise_dot():
         assert abs(dl[idx] - math.fsum(do[idx] * o[idx])) < 1e-14
 
 
+def test_partial_bwd_single_step_over_all_keys_is_attention_bwd():
+    """One step holding every key, with the full attention's LSE and delta,
+    is the whole causal backward (documents included)."""
+    B, Hq, Hkv, S, d = 1, 4, 2, 30, 5
+    cu = [0, 11, 30]
+    q, k, v, do = (_rand((B, Hq, S, d), 50), _rand((B, Hkv, S, d), 51),
+                   _rand((B, Hkv, S, d), 52), _rand((B, Hq, S, d), 53))
+    scale = 0.45
+    pos = np.arange(S)
+    lo = orc.doc_start_of(pos, cu)
+    O, L = orc.attention_fwd(q, k, v, scale, cu_seqlens=cu)
+    got = orc.partial_attention_bwd(q, k, v, do, L, orc.bwd_delta(do, O), scale, pos, lo, pos)
+    ref = orc.attention_bwd(q, k, v, do, scale, cu_seqlens=cu)
+    for a, b_ in zip(got, ref):
+        assert np.abs(a - b_).max() < 1e-12
+
+
+def test_partial_bwd_ring_steps_sum_to_attention_bwd():
+    """Per rank and ring step, with the merged LSE and delta: dQ of a rank is
+    the sum over its steps, dK/dV the sum over every rank and step."""
+    B, Hq, Hkv, S, d, cp = 1, 2, 1, 24, 4, 3
+    q, k, v, do = (_rand((B, Hq, S, d), 54), _rand((B, Hkv, S, d), 55),
+                   _rand((B, Hkv, S, d), 56), _rand((B, Hq, S, d), 57))
+    scale = 0.6
+    O, L = orc.attention_fwd(q, k, v, scale)
+    dl = orc.bwd_delta(do, O)
+    dq_ref, dk_ref, dv_ref = orc.attention_bwd(q, k, v, do, scale)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    for rank in range(cp):
+        rows = orc.zigzag_positions(S, cp, rank)
+        dq = np.zeros((B, Hq, len(rows), d))
+        for src in range(cp):
+            keys = orc.zigzag_positions(S, cp, src)
+            a, b_, c = orc.partial_attention_bwd(q[:, :, rows], k[:, :, keys], v[:, :, keys], do[:, :, rows],
+                                                 L[:, :, rows], dl[:, :, rows], scale, rows, np.zeros_like(rows),
+                                                 keys)
+            dq += a
+            dk[:, :, keys] += b_
+            dv[:, :, keys] += c
+        assert np.abs(dq - dq_ref[:, :, rows]).max() < 1e-12
+    assert np.abs(dk - dk_ref).max() < 1e-12
+    assert np.abs(dv - dv_ref).max() < 1e-12
+
+
+def test_partial_bwd_own_step_matches_central_differences():
+    """With the step's own LSE and delta the result is the gradient of that
+    step's attention output alone, rows without any allowed key included
+    (their output is the constant 0)."""
+    B, Hq, Hkv, d = 1, 2, 1, 3
+    q_pos = np.array([2, 9, 10, 15, 4])      # rows 0 and 4 see no key of the step
+    q_lo = np.array([0, 0, 8, 8, 0])
+    k_pos = np.array([8, 9, 10, 11, 12, 13])
+    nq, nk = len(q_pos), len(k_pos)
+    q, k, v, do = (_rand((B, Hq, nq, d), 58), _rand((B, Hkv, nk, d), 59),
+                   _rand((B, Hkv, nk, d), 60), _rand((B, Hq, nq, d), 61))
+    scale = 0.7
+    O, L = orc.partial_attention_fwd(q, k, v, scale, q_pos, q_lo, k_pos)
+    assert np.isneginf(L[0, :, 0]).all() and np.isneginf(L[0, :, 4]).all()
+    dq, dk, dv = orc.partial_attention_bwd(q, k, v, do, L, orc.bwd_delta(do, O), scale, q_pos, q_lo, k_pos)
+    assert np.all(dq[0, :, 0] == 0) and np.all(dq[0, :, 4] == 0)
+
+    def f(q_, k_, v_):
+        O_, _ = orc.partial_attention_fwd(q_, k_, v_, scale, q_pos, q_lo, k_pos)
+        return float((O_ * do).sum())
+
+    h = 1e-6
+    for which, grad in ((0, dq), (1, dk), (2, dv)):
+        dirn = _rand(grad.shape, 62 + which)
+        args_p = [q, k, v]
+        args_m = [q, k, v]
+        args_p[which] = args_p[which] + h * dirn
+        args_m[which] = args_m[which] - h * dirn
+        fd = (f(*args_p) - f(*args_m)) / (2 * h)
+        an = float((grad * dirn).sum())
+        assert abs(fd - an) <= 1e-7 * max(1.0, abs(an))
+
+
 # ---------------------------------------------------------------- sharding, merge
 def test_zigzag_positions_are_a_permutation_and_cp1_is_identity():
     for S, cp in [(1024, 2), (64, 8), (48, 3), (32768, 8)]:
