@@ -78,6 +78,8 @@ def parse():
     ap.add_argument("--workload", default="llama8b_s128k_cp8")
     ap.add_argument("--ranks", default="all", help="'all' or a comma list of virtual ranks")
     ap.add_argument("--pass", dest="mode", choices=["fwd", "fwdbwd"], default="fwdbwd")
+    ap.add_argument("--varlen-mode", choices=["stream", "per_doc"], default="stream",
+                    help="how a varlen workload's packed stream is dealt to ranks")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time for the cpu_baseline sample")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -124,15 +126,22 @@ def main():
     t0 = time.time()
     full = si.make_qkv(w.B, w.Hq, w.Hkv, w.S, w.d, w.dtype, seed=w.seed, with_dout=bwd)
     q, k, v = full[:3]
-    cu = si.cu_seqlens_from_lengths(si.doc_lengths(total=w.S, seed=w.seed)) if w.varlen else None
+    cu = si.workload_cu_seqlens(w)
     ranks = list(range(w.cp)) if args.ranks == "all" else [int(x) for x in args.ranks.split(",")]
 
+    balance = None
     if cu is None:
         allp = cpa.cp_unshard_zigzag(w.S, w.cp)
         idx = {r: (cpa.cp_shard_zigzag(w.S, w.cp, r), None) for r in ranks}
     else:
-        allp = np.concatenate([cpa.cp_varlen_index(cu, w.cp, r)[0] for r in range(w.cp)])
-        idx = {r: cpa.cp_varlen_index(cu, w.cp, r) for r in ranks}
+        vmode = cpa.CP_PER_DOC if args.varlen_mode == "per_doc" else cpa.CP_STREAM
+        every = [cpa.cp_varlen_index(cu, w.cp, r, vmode) for r in range(w.cp)]
+        allp = np.concatenate([e[0] for e in every])
+        idx = {r: every[r] for r in ranks}
+        # Causal work per rank under this deal: exact unmasked pairs per head.
+        rp = [cpa.cp_pairs(e[0], e[1], allp) for e in every]
+        balance = {"deal": args.varlen_mode, "pairs_per_rank": rp,
+                   "max_over_mean": round(max(rp) / (sum(rp) / len(rp)), 4)}
     ai = torch.from_numpy(allp.astype(np.int64))
     k_all = k.index_select(2, ai).to(dev)
     v_all = v.index_select(2, ai).to(dev)
@@ -239,6 +248,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "pass": "fwd+bwd" if bwd else "fwd", "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv,
                    "d": w.d, "S": w.S, "cp": w.cp, "ranks": ranks, "varlen": w.varlen,
+                   **({"varlen_deal": args.varlen_mode, "docs": len(cu) - 1} if cu is not None else {}),
                    "step": ("per rank: ring forward, delta, ring backward (fp32 dQ/dK/dV zeroed once a step)"
                             if bwd else "ring forward of each listed virtual rank") +
                            ", ranks sequential, K/V resident"},
@@ -248,6 +258,8 @@ def main():
         "roofline_by_pass": rooflines,
         "cpu_baseline": cpu,
     }
+    if balance is not None:
+        out["balance"] = balance
     print(json.dumps(out), flush=True)
 
 

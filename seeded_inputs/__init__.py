@@ -23,7 +23,8 @@ from dataclasses import dataclass, field
 import numpy as np
 import torch
 
-__all__ = ["Workload", "WORKLOADS", "make_qkv", "doc_lengths", "cu_seqlens_from_lengths"]
+__all__ = ["Workload", "WORKLOADS", "make_qkv", "doc_lengths", "round_doc_lengths", "cu_seqlens_from_lengths",
+           "workload_cu_seqlens"]
 
 
 @dataclass(frozen=True)
@@ -38,6 +39,7 @@ class Workload:
     dtype: str          # "f32" or "bf16"
     varlen: bool = False
     backward: bool = False
+    doc_multiple: int = 0  # varlen: document lengths rounded down to a multiple of this (0: as drawn)
     seed: int = 0
     note: str = field(default="", compare=False)
 
@@ -63,6 +65,9 @@ WORKLOADS = {
                                   note="32q/8kv heads, d=128, S=131072, cp=8, bf16"),
     "varlen_s64k_cp4": Workload("varlen_s64k_cp4", 1, 32, 8, 128, 65536, 4, "bf16", varlen=True,
                                 note="packed lognormal documents, 65536 tokens, cp=4"),
+    "varlen8_s64k_cp4": Workload("varlen8_s64k_cp4", 1, 32, 8, 128, 65536, 4, "bf16", varlen=True, doc_multiple=8,
+                                 note="the 65536-token documents with lengths rounded down to multiples of 2cp = 8, "
+                                      "so both the stream and the per-document deal apply"),
     "bwd_s32k_cp8": Workload("bwd_s32k_cp8", 1, 32, 8, 128, 32768, 8, "bf16", backward=True,
                              note="backward on the 32768-token shapes, dO ~ N(0,1) bf16"),
 }
@@ -101,6 +106,27 @@ def doc_lengths(total: int = 65536, mean: float = 2048.0, sigma: float = 1.0,
         out.append(n)
         acc += n
     return np.asarray(out, dtype=np.int64)
+
+
+def round_doc_lengths(lengths, multiple: int) -> np.ndarray:
+    """Each length rounded down to a multiple of ``multiple``; the tokens cut
+    off form one last document (a multiple too when the total is), and empty
+    documents are dropped."""
+    lengths = np.asarray(lengths, dtype=np.int64)
+    total = int(lengths.sum())
+    out = (lengths // multiple) * multiple
+    out = np.append(out, total - out.sum())
+    return out[out > 0]
+
+
+def workload_cu_seqlens(w: "Workload"):
+    """Document boundaries of a varlen workload (None for dense ones)."""
+    if not w.varlen:
+        return None
+    L = doc_lengths(total=w.S, seed=w.seed)
+    if w.doc_multiple:
+        L = round_doc_lengths(L, w.doc_multiple)
+    return cu_seqlens_from_lengths(L)
 
 
 def cu_seqlens_from_lengths(lengths) -> np.ndarray:

@@ -126,6 +126,27 @@ def test_varlen_per_doc_index():
         cpa.cp_varlen_index([0, 6, 16], 2, 0, cpa.CP_PER_DOC)
 
 
+def test_varlen_deals_balance_at_workload_size():
+    """The 65536-token documents rounded to multiples of 2cp: the per-document
+    deal gives every rank the same causal work, the stream deal does not; the
+    library's pair counts equal the oracle's for both."""
+    w = si.WORKLOADS["varlen8_s64k_cp4"]
+    cu = si.workload_cu_seqlens(w)
+    assert np.all(np.diff(cu) % (2 * w.cp) == 0)
+    counts = {}
+    for mode in (cpa.CP_STREAM, cpa.CP_PER_DOC):
+        every = [cpa.cp_varlen_index(cu, w.cp, r, mode) for r in range(w.cp)]
+        allp = np.concatenate([e[0] for e in every])
+        assert np.array_equal(np.sort(allp), np.arange(w.S))
+        got = [cpa.cp_pairs(p, l, allp) for p, l in every]
+        ref = [orc.pair_count(p, orc.doc_start_of(p, cu), np.arange(w.S)) for p, _ in every]
+        assert got == ref
+        counts[mode] = got
+    assert len(set(counts[cpa.CP_PER_DOC])) == 1
+    assert sum(counts[cpa.CP_PER_DOC]) == sum(counts[cpa.CP_STREAM])
+    assert max(counts[cpa.CP_STREAM]) > 1.2 * min(counts[cpa.CP_PER_DOC])
+
+
 def test_varlen_errors():
     with pytest.raises(ValueError, match="must be 0"):
         cpa.cp_varlen_index([1, 8], 2, 0)
