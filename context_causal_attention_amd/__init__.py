@@ -26,7 +26,8 @@ __all__ = [
     "CP_F32", "CP_BF16", "CP_STREAM", "CP_PER_DOC", "CpShape", "CpError", "LIB_PATH",
     "lib", "cp_version", "cp_last_error", "cp_shard_zigzag", "cp_unshard_zigzag",
     "cp_varlen_index", "cp_ring_source", "cp_pairs", "cp_attn_fwd_workspace",
-    "cp_attn_partial_fwd", "cp_attn_merge", "cp_attn_ring_fwd", "RingFwdPlan",
+    "cp_attn_partial_fwd", "cp_attn_merge", "cp_attn_ring_fwd", "RingFwdPlan", "cp_attn_ring_fwd_stepwise",
+    "RingFwdStepwisePlan",
     "cp_attn_bwd_workspace", "cp_attn_bwd_delta", "cp_attn_partial_bwd", "cp_attn_ring_bwd", "RingBwdPlan",
 ]
 
@@ -81,6 +82,12 @@ def lib() -> ctypes.CDLL:
         L.cp_attn_merge.argtypes = [c_int64, c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]
         L.cp_attn_ring_fwd.argtypes = [POINTER(CpShape), c_int32, c_int32] + [c_void_p] * 6 + \
             [c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]
+        L.cp_attn_ring_fwd_stepwise_workspace.argtypes = [POINTER(CpShape), c_int32]
+        L.cp_attn_ring_fwd_stepwise_workspace.restype = c_size_t
+        L.cp_attn_ring_stage_bytes.argtypes = [POINTER(CpShape), c_int32]
+        L.cp_attn_ring_stage_bytes.restype = c_size_t
+        L.cp_attn_ring_fwd_stepwise.argtypes = [POINTER(CpShape), c_int32, c_int32] + [c_void_p] * 6 + \
+            [c_void_p, c_void_p, c_void_p, c_size_t, c_void_p, c_size_t, c_void_p, c_void_p]
         L.cp_attn_bwd_workspace.argtypes = [POINTER(CpShape), c_int32]
         L.cp_attn_bwd_workspace.restype = c_size_t
         L.cp_attn_bwd_delta.argtypes = [POINTER(CpShape), c_void_p, c_void_p, c_void_p, c_void_p]
@@ -88,7 +95,8 @@ def lib() -> ctypes.CDLL:
         L.cp_attn_ring_bwd.argtypes = [POINTER(CpShape), c_int32, c_int32] + [c_void_p] * 12 + \
             [c_void_p, c_size_t, c_void_p]
         for name in ("cp_shard_zigzag", "cp_unshard_zigzag", "cp_varlen_index", "cp_ring_source",
-                     "cp_attn_partial_fwd", "cp_attn_merge", "cp_attn_ring_fwd", "cp_attn_bwd_delta",
+                     "cp_attn_partial_fwd", "cp_attn_merge", "cp_attn_ring_fwd", "cp_attn_ring_fwd_stepwise",
+                     "cp_attn_bwd_delta",
                      "cp_attn_partial_bwd", "cp_attn_ring_bwd"):
             getattr(L, name).restype = c_int32
         _lib_handle = L
@@ -286,6 +294,54 @@ def cp_attn_ring_fwd(q_loc, k_all, v_all, cp, rank, q_pos, q_lo, k_pos_all, scal
     """A virtual rank's whole ring with every K/V shard resident: final (O, LSE)."""
     return RingFwdPlan(q_loc, k_all, v_all, cp, rank, q_pos, q_lo, k_pos_all, scale, out_dtype, out, lse,
                        workspace).run()
+
+
+class RingFwdStepwisePlan:
+    """A validated cp_attn_ring_fwd_stepwise call: one partial forward and one
+    merge per ring step.  staged=True copies each step's K/V shard into a
+    two-slot staging buffer on copy_stream (a torch.cuda.Stream, or None for a
+    new one) first, overlapped with the previous step, as a rotation ring
+    receives the shards; staged=False reads every shard in place.  O is fp32."""
+
+    def __init__(self, q_loc, k_all, v_all, cp, rank, q_pos, q_lo, k_pos_all, scale=None, staged=True,
+                 copy_stream=None, out=None, lse=None, workspace=None, stage=None):
+        dev = q_loc.device
+        B, Hq, Sq, D = q_loc.shape
+        self.out = torch.empty(B, Hq, Sq, D, dtype=torch.float32, device=dev) if out is None else out
+        self.lse = torch.empty(B, Hq, Sq, dtype=torch.float32, device=dev) if lse is None else lse
+        self.shape = _shape(q_loc, k_all, v_all, _strides(self.out), scale, torch.float32)
+        self.qp = _dev_i32(q_pos, dev)
+        self.ql = None if q_lo is None else _dev_i32(q_lo, dev)
+        self.kp = _dev_i32(k_pos_all, dev)
+        nws = int(lib().cp_attn_ring_fwd_stepwise_workspace(ctypes.byref(self.shape), cp))
+        self.ws = _workspace(nws or 256, dev, workspace)
+        self.stage = None
+        self.copy_stream = None
+        if staged:
+            nst = int(lib().cp_attn_ring_stage_bytes(ctypes.byref(self.shape), cp))
+            self.stage = _workspace(nst or 256, dev, stage)
+            self.copy_stream = torch.cuda.Stream(device=dev) if copy_stream is None else copy_stream
+        self.keep = (q_loc, k_all, v_all)
+        self.args = (ctypes.byref(self.shape), cp, rank, q_loc.data_ptr(), k_all.data_ptr(), v_all.data_ptr(),
+                     self.qp.data_ptr(), None if self.ql is None else self.ql.data_ptr(), self.kp.data_ptr(),
+                     self.out.data_ptr(), self.lse.data_ptr(), self.ws.data_ptr(), self.ws.numel(),
+                     None if self.stage is None else self.stage.data_ptr(),
+                     0 if self.stage is None else self.stage.numel())
+        self.device = dev
+
+    def run(self, stream=None):
+        st = _stream(self.device) if stream is None else stream
+        cst = st if self.copy_stream is None else self.copy_stream.cuda_stream
+        _check(lib().cp_attn_ring_fwd_stepwise(*self.args, st, cst))
+        return self.out, self.lse
+
+
+def cp_attn_ring_fwd_stepwise(q_loc, k_all, v_all, cp, rank, q_pos, q_lo, k_pos_all, scale=None, staged=True,
+                              copy_stream=None, out=None, lse=None, workspace=None, stage=None):
+    """A virtual rank's ring as separate steps (partial forward + merge per
+    step), optionally with rotating K/V copies: final fp32 (O, LSE)."""
+    return RingFwdStepwisePlan(q_loc, k_all, v_all, cp, rank, q_pos, q_lo, k_pos_all, scale, staged,
+                               copy_stream, out, lse, workspace, stage).run()
 
 
 # ------------------------------------------------------------------ backward

@@ -5,6 +5,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <string>
+#include <vector>
 
 #include "internal.h"
 
@@ -159,10 +160,10 @@ extern "C" size_t cp_attn_fwd_workspace(const cp_shape* s, int32_t cp) {
 
 namespace {
 
-int run_fwd(const cp_shape* s, int32_t cp, int32_t rank, const void* q, const void* k, const void* v,
-            const int32_t* q_pos, const int32_t* q_lo, const int32_t* k_pos, void* o, int32_t o_dtype,
-            float* lse, void* ws, size_t ws_bytes, hipStream_t stream) {
-  if (s->sq == 0) return CP_OK;  // no query rows: nothing to read or write
+// Validates one forward launch and fills its kernel arguments; launches nothing.
+int prep_fwd(const cp_shape* s, int32_t cp, int32_t rank, const void* q, const void* k, const void* v,
+             const int32_t* q_pos, const int32_t* q_lo, const int32_t* k_pos, void* o, int32_t o_dtype,
+             float* lse, void* ws, size_t ws_bytes, FwdArgs* out) {
   if (int rc = check_ptrs16({{q, "q"}, {o, "o"}, {lse, "lse"}})) return rc;
   if (!q_pos) return fail(CP_EINVAL, "q_pos is null");
   if (s->sk > 0) {
@@ -201,6 +202,16 @@ int run_fwd(const cp_shape* s, int32_t cp, int32_t rank, const void* q, const vo
   a.tiles_per_rank = (a.rows_per_rank + tk - 1) / tk;
   a.out_dtype = o_dtype;
   a.ws = ws;
+  *out = a;
+  return CP_OK;
+}
+
+int run_fwd(const cp_shape* s, int32_t cp, int32_t rank, const void* q, const void* k, const void* v,
+            const int32_t* q_pos, const int32_t* q_lo, const int32_t* k_pos, void* o, int32_t o_dtype,
+            float* lse, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (s->sq == 0) return CP_OK;  // no query rows: nothing to read or write
+  FwdArgs a;
+  if (int rc = prep_fwd(s, cp, rank, q, k, v, q_pos, q_lo, k_pos, o, o_dtype, lse, ws, ws_bytes, &a)) return rc;
   return hip_status(launch_fwd(a, stream), "forward launch");
 }
 
@@ -238,6 +249,187 @@ extern "C" int cp_attn_merge(int64_t rows, int32_t d, float* o_acc, float* lse_a
   if (!lse_acc || !lse_p) return fail(CP_EINVAL, "lse pointer is null");
   if (rows == 0) return CP_OK;
   return hip_status(launch_merge(rows, d, o_acc, lse_acc, o_p, lse_p, stream), "merge launch");
+}
+
+namespace {
+
+// Workspace of the stepwise ring: the step's partial O and LSE, then the
+// tables of the step kernel (cp = 1 over one shard).
+struct StepwiseLayout {
+  size_t opart_off, lpart_off, kern_off, kern_bytes, total;
+};
+
+StepwiseLayout stepwise_layout(const cp_shape* s, int32_t cp) {
+  StepwiseLayout w{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off += align_up(bytes, 256);
+    return at;
+  };
+  const size_t rows = (size_t)s->b * s->hq * (size_t)s->sq;
+  w.opart_off = take(rows * s->d * 4);
+  w.lpart_off = take(rows * 4);
+  w.kern_bytes = fwd_workspace_layout(s->b, s->hkv, s->d, s->sk / cp, 1, s->in_dtype).total;
+  w.kern_off = take(w.kern_bytes);
+  w.total = off;
+  return w;
+}
+
+// One staged shard of K or V: [b][hkv][sk/cp][d] packed, 256-byte aligned.
+size_t stage_slot_bytes(const cp_shape* s, int32_t cp) {
+  return align_up((size_t)s->b * s->hkv * (size_t)(s->sk / cp) * s->d * esize(s->in_dtype), 256);
+}
+
+// Copies rows [src*R, (src+1)*R) of every (batch, kv head) of x (element
+// strides st, rows contiguous) into dst, packed as [b][hkv][R][d].
+hipError_t copy_shard(char* dst, const void* x, const int64_t* st, const cp_shape* s, int64_t R, int32_t src,
+                      hipStream_t stream) {
+  const size_t e = esize(s->in_dtype);
+  const size_t width = (size_t)R * s->d * e;
+  if (width == 0) return hipSuccess;
+  for (int32_t b = 0; b < s->b; ++b) {
+    const char* from = static_cast<const char*>(x) + ((size_t)b * st[0] + (size_t)src * R * st[2]) * e;
+    char* to = dst + (size_t)b * s->hkv * width;
+    const hipError_t err =
+        hipMemcpy2DAsync(to, width, from, (size_t)st[1] * e, width, s->hkv, hipMemcpyDeviceToDevice, stream);
+    if (err != hipSuccess) return err;
+  }
+  return hipSuccess;
+}
+
+// Events of one call, released when the call returns (a recorded event that
+// has not completed yet is released by the runtime once it completes).
+struct CallEvents {
+  std::vector<hipEvent_t> ev;
+  hipError_t make(hipEvent_t* out) {
+    const hipError_t e = hipEventCreateWithFlags(out, hipEventDisableTiming);
+    if (e == hipSuccess) ev.push_back(*out);
+    return e;
+  }
+  ~CallEvents() {
+    for (hipEvent_t e : ev) (void)hipEventDestroy(e);
+  }
+};
+
+}  // namespace
+
+extern "C" size_t cp_attn_ring_fwd_stepwise_workspace(const cp_shape* s, int32_t cp) {
+  if (check_shape(s) != CP_OK || cp < 1) return 0;
+  return stepwise_layout(s, cp).total;
+}
+
+extern "C" size_t cp_attn_ring_stage_bytes(const cp_shape* s, int32_t cp) {
+  if (check_shape(s) != CP_OK || cp < 1) return 0;
+  const size_t n = 4 * stage_slot_bytes(s, cp);  // two slots of K and V
+  return n < 256 ? 256 : n;
+}
+
+extern "C" int cp_attn_ring_fwd_stepwise(const cp_shape* s, int32_t cp, int32_t rank, const void* q_loc,
+                                         const void* k_all, const void* v_all, const int32_t* q_pos,
+                                         const int32_t* q_lo, const int32_t* k_pos_all, float* o, float* lse,
+                                         void* ws, size_t ws_bytes, void* stage, size_t stage_bytes,
+                                         hipStream_t stream, hipStream_t copy_stream) {
+  clear_error();
+  if (int rc = check_shape(s)) return rc;
+  if (cp < 1) return fail(CP_EINVAL, "cp must be >= 1 (got %d)", cp);
+  if (rank < 0 || rank >= cp) return fail(CP_EINVAL, "rank %d outside [0, %d)", rank, cp);
+  if (s->sk % (2 * (int64_t)cp) != 0)
+    return fail(CP_ESHAPE, "key rows %lld are not a multiple of 2*cp = %lld", (long long)s->sk,
+                2 * (long long)cp);
+  if (s->out_dtype != CP_F32) return fail(CP_EDTYPE, "the stepwise ring writes an fp32 O (out_dtype must be CP_F32)");
+  if (s->o_str[2] != s->d || s->o_str[1] != s->sq * s->d || s->o_str[0] != s->hq * s->sq * s->d)
+    return fail(CP_EINVAL, "o must be contiguous [b, hq, sq, d] for the merge");
+  if (s->sq == 0) return CP_OK;
+  const int64_t R = s->sk / cp;
+  const StepwiseLayout w = stepwise_layout(s, cp);
+  if (!ws) return fail(CP_EWORKSPACE, "workspace is null (%zu bytes needed)", w.total);
+  if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0) return fail(CP_EWORKSPACE, "workspace is not 256-byte aligned");
+  if (ws_bytes < w.total) return fail(CP_EWORKSPACE, "workspace too small: %zu < %zu bytes", ws_bytes, w.total);
+  const size_t slot = stage_slot_bytes(s, cp);
+  if (stage) {
+    if ((reinterpret_cast<uintptr_t>(stage) & 255u) != 0)
+      return fail(CP_EWORKSPACE, "stage is not 256-byte aligned");
+    if (stage_bytes < 4 * slot) return fail(CP_EWORKSPACE, "stage too small: %zu < %zu bytes", stage_bytes, 4 * slot);
+    if (s->k_str[2] != s->d || s->v_str[2] != s->d || s->k_str[1] < s->sk * s->d || s->v_str[1] < s->sk * s->d)
+      return fail(CP_EINVAL, "staging copies need k_all and v_all with contiguous rows and heads of sk rows");
+  }
+  char* wsb = static_cast<char*>(ws);
+  float* o_part = reinterpret_cast<float*>(wsb + w.opart_off);
+  float* l_part = reinterpret_cast<float*>(wsb + w.lpart_off);
+  void* kws = wsb + w.kern_off;
+  const size_t e = esize(s->in_dtype);
+  char* st = static_cast<char*>(stage);
+
+  // Every step's launch is validated before anything is enqueued.
+  std::vector<FwdArgs> steps(cp);
+  for (int32_t t = 0; t < cp; ++t) {
+    int32_t src = rank - t;
+    if (src < 0) src += cp;
+    cp_shape ss = *s;
+    ss.sk = R;
+    const void* k = static_cast<const char*>(k_all) + (size_t)src * R * s->k_str[2] * e;
+    const void* v = static_cast<const char*>(v_all) + (size_t)src * R * s->v_str[2] * e;
+    if (stage && t > 0) {
+      char* kb = st + (size_t)(t & 1) * 2 * slot;
+      k = kb;
+      v = kb + slot;
+      const int64_t packed[3] = {(int64_t)s->hkv * R * s->d, R * s->d, s->d};
+      for (int i = 0; i < 3; ++i) ss.k_str[i] = ss.v_str[i] = packed[i];
+    }
+    float* ot = t == 0 ? o : o_part;
+    float* lt = t == 0 ? lse : l_part;
+    if (int rc = prep_fwd(&ss, 1, 0, q_loc, k, v, q_pos, q_lo, k_pos_all + (size_t)src * R, ot, CP_F32, lt, kws,
+                          w.kern_bytes, &steps[t]))
+      return rc;
+  }
+
+  const int64_t rows = (int64_t)s->b * s->hq * s->sq;
+  const bool staged = stage != nullptr && cp > 1;
+  CallEvents ev;
+  std::vector<hipEvent_t> copied(cp, nullptr);
+  hipEvent_t slot_free[2] = {nullptr, nullptr}, start = nullptr, joined = nullptr;
+  if (staged) {
+    if (int rc = hip_status(ev.make(&start), "event")) return rc;
+    if (int rc = hip_status(ev.make(&joined), "event")) return rc;
+    for (int i = 0; i < 2; ++i)
+      if (int rc = hip_status(ev.make(&slot_free[i]), "event")) return rc;
+    for (int32_t t = 1; t < cp; ++t)
+      if (int rc = hip_status(ev.make(&copied[t]), "event")) return rc;
+    // The shards are read only after the work already queued on stream.
+    if (int rc = hip_status(hipEventRecord(start, stream), "event record")) return rc;
+    if (int rc = hip_status(hipStreamWaitEvent(copy_stream, start, 0), "stream wait")) return rc;
+  }
+  // Copy of step t's shard into slot t % 2, after step t - 2 (the slot's last
+  // reader) has finished.
+  auto enqueue_copy = [&](int32_t t) -> int {
+    int32_t src = rank - t;
+    if (src < 0) src += cp;
+    char* kb = st + (size_t)(t & 1) * 2 * slot;
+    if (t >= 3)
+      if (int rc = hip_status(hipStreamWaitEvent(copy_stream, slot_free[t & 1], 0), "stream wait")) return rc;
+    if (int rc = hip_status(copy_shard(kb, k_all, s->k_str, s, R, src, copy_stream), "K copy")) return rc;
+    if (int rc = hip_status(copy_shard(kb + slot, v_all, s->v_str, s, R, src, copy_stream), "V copy")) return rc;
+    return hip_status(hipEventRecord(copied[t], copy_stream), "event record");
+  };
+  if (staged)
+    if (int rc = enqueue_copy(1)) return rc;
+  for (int32_t t = 0; t < cp; ++t) {
+    if (staged && t + 1 < cp && t + 1 >= 2)
+      if (int rc = enqueue_copy(t + 1)) return rc;
+    if (staged && t > 0)
+      if (int rc = hip_status(hipStreamWaitEvent(stream, copied[t], 0), "stream wait")) return rc;
+    if (int rc = hip_status(launch_fwd(steps[t], stream), "forward launch")) return rc;
+    if (staged && t > 0)
+      if (int rc = hip_status(hipEventRecord(slot_free[t & 1], stream), "event record")) return rc;
+    if (t > 0)
+      if (int rc = hip_status(launch_merge(rows, s->d, o, lse, o_part, l_part, stream), "merge launch")) return rc;
+  }
+  if (staged) {
+    if (int rc = hip_status(hipEventRecord(joined, copy_stream), "event record")) return rc;
+    if (int rc = hip_status(hipStreamWaitEvent(stream, joined, 0), "stream wait")) return rc;
+  }
+  return CP_OK;
 }
 
 extern "C" size_t cp_attn_bwd_workspace(const cp_shape* s, int32_t cp) {

@@ -166,6 +166,42 @@ int cp_attn_ring_fwd(const cp_shape* s, int32_t cp, int32_t rank, const void* q_
                      const int32_t* q_lo, const int32_t* k_pos_all, void* o, float* lse,
                      void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* ---------------------------------------------------------------- stepwise ring
+ * The ring forward computed the way a ring of separate steps computes it
+ * (Accelerate concept guide, "So how does it work?": attend the local queries
+ * to one K/V shard, then combine, once per shard; the rotation of the shards
+ * is the "all-to-all" method of "How to choose the right rotation method?").
+ * Step t = 0..cp-1 attends q_loc to the shard of rank (rank - t) mod cp with
+ * the kernel of cp_attn_partial_fwd and merges the partial into (o, lse) with
+ * the kernel of cp_attn_merge; step 0 writes (o, lse) directly.
+ *
+ * stage == NULL: every step reads its shard where it lies in k_all / v_all.
+ * stage != NULL: the shards of steps 1..cp-1 are first copied into stage, two
+ * slots used in turn, on copy_stream, the way a rotation ring receives them
+ * from its neighbour.  The copy of a later step's shard overlaps the current
+ * step's attention; a step waits only for its own shard, and a slot is
+ * refilled only after the step that read it has finished.  copy_stream may be
+ * stream itself (copies then run in line with the steps).  Everything the call
+ * enqueues on copy_stream is joined back into stream before it returns, so
+ * work queued later on stream sees o and lse complete.  k_all and v_all must
+ * have contiguous rows (row stride d) when staging.
+ *
+ * Arguments as for cp_attn_ring_fwd, except: o (device fp32, contiguous
+ * [b,hq,sq,d], o_str = {hq*sq*d, sq*d, d}) and s->out_dtype must be CP_F32
+ * (the merge works on fp32; CP_EDTYPE otherwise).  ws (device) of at least
+ * cp_attn_ring_fwd_stepwise_workspace(s, cp) bytes holds the per-step partial
+ * (O, LSE) and the step kernel's tables; stage (device) of at least
+ * cp_attn_ring_stage_bytes(s, cp) bytes.  Both 256-byte aligned.  Both are
+ * owned by the caller and must stay untouched until stream has passed the call.
+ * CP_ESHAPE unless sk % (2cp) == 0. */
+size_t cp_attn_ring_fwd_stepwise_workspace(const cp_shape* s, int32_t cp);
+size_t cp_attn_ring_stage_bytes(const cp_shape* s, int32_t cp);
+int cp_attn_ring_fwd_stepwise(const cp_shape* s, int32_t cp, int32_t rank, const void* q_loc,
+                              const void* k_all, const void* v_all, const int32_t* q_pos,
+                              const int32_t* q_lo, const int32_t* k_pos_all, float* o, float* lse,
+                              void* ws, size_t ws_bytes, void* stage, size_t stage_bytes,
+                              hipStream_t stream, hipStream_t copy_stream);
+
 /* ---------------------------------------------------------------- backward
  * Gradients of the ring forward above with respect to q, k and v.  The pages
  * train through context-parallel attention (the Accelerate guide wraps the

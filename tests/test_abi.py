@@ -215,6 +215,40 @@ def test_ring_fwd_rejects_bad_args():
     assert _ring(s, ws_bytes=need - 1) == cpa.CP_EWORKSPACE
 
 
+def _stepwise(s, cp=2, rank=0, ws=FAKE, ws_bytes=1 << 40, stage=None, stage_bytes=0, o=FAKE):
+    return cpa.lib().cp_attn_ring_fwd_stepwise(ctypes.byref(s), cp, rank, FAKE, FAKE, FAKE, FAKE, None, FAKE, o,
+                                               FAKE, ws, ws_bytes, stage, stage_bytes, None, None)
+
+
+def test_ring_fwd_stepwise_validation():
+    L = cpa.lib()
+    s = _shape()
+    need = L.cp_attn_ring_fwd_stepwise_workspace(ctypes.byref(s), 2)
+    # partial O (1 x 4 heads x 256 rows x 128 fp32) + partial LSE + the step kernel's tables
+    assert need >= 4 * 256 * 128 * 4 + 4 * 256 * 4
+    # two slots of K and V, one shard each: 2 kv heads x 256 rows x 128 x bf16
+    assert L.cp_attn_ring_stage_bytes(ctypes.byref(s), 2) == 4 * 2 * 256 * 128 * 2
+    assert L.cp_attn_ring_fwd_stepwise_workspace(ctypes.byref(_shape(d=96)), 2) == 0
+    assert _stepwise(_shape(out_dtype=cpa.CP_BF16)) == cpa.CP_EDTYPE
+    t = _shape()
+    t.o_str = (ctypes.c_int64 * 3)(4 * 256 * 256, 256 * 256, 256)  # rows padded: not contiguous
+    assert _stepwise(t) == cpa.CP_EINVAL
+    assert _stepwise(_shape(sk=510)) == cpa.CP_ESHAPE
+    assert _stepwise(s, rank=2) == cpa.CP_EINVAL
+    assert _stepwise(s, cp=0) == cpa.CP_EINVAL
+    assert _stepwise(s, ws=0) == cpa.CP_EWORKSPACE
+    assert _stepwise(s, ws=FAKE + 16) == cpa.CP_EWORKSPACE
+    assert _stepwise(s, ws_bytes=need - 1) == cpa.CP_EWORKSPACE
+    st = L.cp_attn_ring_stage_bytes(ctypes.byref(s), 2)
+    assert _stepwise(s, ws_bytes=need, stage=FAKE, stage_bytes=st - 1) == cpa.CP_EWORKSPACE
+    assert _stepwise(s, ws_bytes=need, stage=FAKE + 16, stage_bytes=st) == cpa.CP_EWORKSPACE
+    u = _shape()
+    u.k_str = (ctypes.c_int64 * 3)(2 * 512 * 256, 512 * 256, 256)  # K rows strided: cannot be staged by rows
+    assert _stepwise(u, ws_bytes=need, stage=FAKE, stage_bytes=st) == cpa.CP_EINVAL
+    assert _stepwise(s, o=FAKE + 8) == cpa.CP_EINVAL
+    assert _stepwise(_shape(sq=0)) == cpa.CP_OK  # no query rows: nothing to do, nothing launched
+
+
 def test_workspace_query():
     s = _shape(sk=131072, sq=16384, hq=32, hkv=8)
     n = cpa.lib().cp_attn_fwd_workspace(ctypes.byref(s), 8)

@@ -220,3 +220,48 @@ def test_strided_row_views():
     o, lse = cpa.cp_attn_ring_fwd(qv, R.k_all, R.v_all, cp, 0, R.pos, None, R.allp, scale=R.scale, out=ov)
     assert_close(o, lse, *R.oracle(), "bf16", "views")
     assert torch.all(obig[:, :, :4] == 0) and torch.all(obig[:, :, 4 + S // cp:] == 0)
+
+
+# ------------------------------------------------------------------ the ring as separate steps
+@pytest.mark.parametrize("dtype,cp,S", [("bf16", 4, 2048), ("f32", 2, 1024), ("bf16", 8, 4096)])
+def test_ring_fwd_stepwise_matches_oracle(dtype, cp, S):
+    """Partial forward + merge per ring step, shards read in place, copied
+    step by step into the two-slot stage on a second stream, or copied on the
+    compute stream itself: all three match the oracle, and the staged runs are
+    bit-identical to the in-place run (the same kernels read the same values,
+    so a slot refilled too early would show)."""
+    B, Hq, Hkv, d = 1, 8, 2, 128
+    full = si.make_qkv(B, Hq, Hkv, S, d, dtype, seed=11)
+    for rank in range(cp):
+        announce(f"stepwise ring {dtype} cp={cp} S={S} rank {rank}")
+        R = Rank(B, Hq, Hkv, S, d, cp, rank, dtype, full=full)
+        args = (R.q_loc, R.k_all, R.v_all, cp, rank, R.pos, R.lo, R.allp)
+        o0, l0 = cpa.cp_attn_ring_fwd_stepwise(*args, scale=R.scale, staged=False)
+        o1, l1 = cpa.cp_attn_ring_fwd_stepwise(*args, scale=R.scale, staged=True)
+        o2, l2 = cpa.cp_attn_ring_fwd_stepwise(*args, scale=R.scale, staged=True,
+                                               copy_stream=torch.cuda.current_stream())
+        torch.cuda.synchronize()
+        assert torch.equal(o1, o0) and torch.equal(l1, l0)
+        assert torch.equal(o2, o0) and torch.equal(l2, l0)
+        assert_close(o0, l0, *R.oracle(), dtype, f"stepwise rank {rank}")
+
+
+def test_ring_fwd_stepwise_varlen_and_replay():
+    """Packed documents (stream deal), and one plan replayed: every replay of
+    the staged plan equals the first run bit for bit and the oracle."""
+    cp = 4
+    L = si.doc_lengths(total=4096, mean=400, sigma=1.0, lo=16, hi=3000, seed=12)
+    cu = si.cu_seqlens_from_lengths(L)
+    S = int(cu[-1])
+    full = si.make_qkv(1, 4, 2, S, 64, "bf16", seed=13)
+    for rank in (0, 3):
+        announce(f"stepwise ring varlen rank {rank} ({len(L)} docs), replays")
+        R = Rank(1, 4, 2, S, 64, cp, rank, "bf16", full=full, cu=cu)
+        plan = cpa.RingFwdStepwisePlan(R.q_loc, R.k_all, R.v_all, cp, rank, R.pos, R.lo, R.allp, scale=R.scale)
+        o, lse = plan.run()
+        o_first, l_first = o.clone(), lse.clone()
+        for _ in range(3):
+            plan.run()
+        torch.cuda.synchronize()
+        assert torch.equal(plan.out, o_first) and torch.equal(plan.lse, l_first)
+        assert_close(o_first, l_first, *R.oracle(), "bf16", f"stepwise varlen rank {rank}")
