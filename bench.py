@@ -6,7 +6,14 @@ shard already resident in HBM (index maps are built once, in set-up):
   --pass fwdbwd (default): zero the fp32 gradient buffers, then per rank the
       ring forward (final O, LSE), delta = rowsum(dO * O) and the ring backward
       (dQ of the rank's rows, dK/dV of every shard accumulated in place);
-  --pass fwd: the ring forward of each rank only.
+  --pass fwd: the ring forward of each rank only;
+  --pass rotate: the ring forward of each rank as separate steps (partial
+      forward + merge per step, cp_attn_ring_fwd_stepwise), four ways: the
+      fused resident ring, steps reading the shards in place, steps whose
+      shards are copied into a two-slot stage on a second stream (a rotation
+      ring's receive, overlapped), and the same copies on the compute stream.
+      ``value`` is the staged, overlapped rate; ``rotate`` gives all four and
+      the copies alone.
 ``value`` is the algorithmic work of a step divided by the time of the timed
 steps, in TFLOP/s: 4*d*Hq flops per allowed (query, key) pair for the forward
 (Q K^T and P V) and 10*d*Hq for the backward (Q K^T, dO V^T, P^T dO, dS K and
@@ -77,7 +84,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="llama8b_s128k_cp8")
     ap.add_argument("--ranks", default="all", help="'all' or a comma list of virtual ranks")
-    ap.add_argument("--pass", dest="mode", choices=["fwd", "fwdbwd"], default="fwdbwd")
+    ap.add_argument("--pass", dest="mode", choices=["fwd", "fwdbwd", "rotate"], default="fwdbwd")
     ap.add_argument("--varlen-mode", choices=["stream", "per_doc"], default="stream",
                     help="how a varlen workload's packed stream is dealt to ranks")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -118,6 +125,9 @@ def main():
     import seeded_inputs as si
 
     w = si.WORKLOADS[args.workload]
+    if args.mode == "rotate":
+        rotate_bench(args, w)
+        return
     bwd = args.mode == "fwdbwd"
     if bwd and w.dtype != "bf16":
         print(f"the backward takes bf16 inputs; {w.name} is {w.dtype} (use --pass fwd)", file=sys.stderr)
@@ -260,6 +270,140 @@ def main():
     }
     if balance is not None:
         out["balance"] = balance
+    print(json.dumps(out), flush=True)
+
+
+def rotate_bench(args, w):
+    """--pass rotate (see the module docstring)."""
+    import numpy as np
+    import torch
+
+    import context_causal_attention_amd as cpa
+    import seeded_inputs as si
+
+    dev = torch.device("cuda:0")
+    full = si.make_qkv(w.B, w.Hq, w.Hkv, w.S, w.d, w.dtype, seed=w.seed)
+    q, k, v = full
+    cu = si.workload_cu_seqlens(w)
+    ranks = list(range(w.cp)) if args.ranks == "all" else [int(x) for x in args.ranks.split(",")]
+    if cu is None:
+        allp = cpa.cp_unshard_zigzag(w.S, w.cp)
+        idx = {r: (cpa.cp_shard_zigzag(w.S, w.cp, r), None) for r in ranks}
+    else:
+        vmode = cpa.CP_PER_DOC if args.varlen_mode == "per_doc" else cpa.CP_STREAM
+        every = [cpa.cp_varlen_index(cu, w.cp, r, vmode) for r in range(w.cp)]
+        allp = np.concatenate([e[0] for e in every])
+        idx = {r: every[r] for r in ranks}
+    ai = torch.from_numpy(allp.astype(np.int64))
+    k_all = k.index_select(2, ai).to(dev)
+    v_all = v.index_select(2, ai).to(dev)
+    copy_stream = torch.cuda.Stream(device=dev)
+    kinds = ["fused", "steps_in_place", "steps_staged", "steps_staged_in_line"]
+    plans, pairs = {}, {}
+    for r in ranks:
+        pos, lo = idx[r]
+        q_loc = q.index_select(2, torch.from_numpy(pos.astype(np.int64))).to(dev)
+        a = (q_loc, k_all, v_all, w.cp, r, pos, lo, allp)
+        plans[r] = {
+            "fused": cpa.RingFwdPlan(*a, scale=w.scale),
+            "steps_in_place": cpa.RingFwdStepwisePlan(*a, scale=w.scale, staged=False),
+            "steps_staged": cpa.RingFwdStepwisePlan(*a, scale=w.scale, staged=True, copy_stream=copy_stream),
+            "steps_staged_in_line": cpa.RingFwdStepwisePlan(*a, scale=w.scale, staged=True,
+                                                            copy_stream=torch.cuda.current_stream(dev)),
+        }
+        pairs[r] = cpa.cp_pairs(pos, lo, allp)
+    # The copies alone: the (cp - 1) shards of K and V a rank receives, as
+    # plain device copies of the same bytes on the copy stream.
+    R = w.S // w.cp
+    src_k = [k_all[:, :, s * R:(s + 1) * R] for s in range(w.cp)]
+    src_v = [v_all[:, :, s * R:(s + 1) * R] for s in range(w.cp)]
+    slot = [torch.empty_like(src_k[0]) for _ in range(4)]
+    stream = torch.cuda.current_stream(dev)
+
+    def copies():
+        copy_stream.wait_stream(stream)
+        with torch.cuda.stream(copy_stream):
+            for t in range(1, w.cp):
+                slot[2 * (t & 1)].copy_(src_k[t])
+                slot[2 * (t & 1) + 1].copy_(src_v[t])
+        stream.wait_stream(copy_stream)
+
+    def step(ev=None):
+        for r in ranks:
+            for kd in kinds + ["copies"]:
+                if ev is not None:
+                    ev[kd][r][0].record(stream)
+                if kd == "copies":
+                    copies()
+                else:
+                    plans[r][kd].run()
+                if ev is not None:
+                    ev[kd][r][1].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [{kd: {r: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for r in ranks}
+            for kd in kinds + ["copies"]} for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for s_ in range(args.steps):
+        step(evs[s_])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = {kd: {r: float(np.mean([evs[s_][kd][r][0].elapsed_time(evs[s_][kd][r][1]) for s_ in range(args.steps)]))
+               for r in ranks} for kd in kinds + ["copies"]}
+    fl = {r: FLOPS_PER_PAIR_HEAD_DIM["fwd"] * w.d * w.Hq * w.B * pairs[r] for r in ranks}
+    tot = sum(fl.values())
+
+    def rate(kd):
+        return round(tot / (sum(ms[kd].values()) * 1e-3) / 1e12, 3)
+
+    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
+    staged = sum(ms["steps_staged"].values())
+    inplace = sum(ms["steps_in_place"].values())
+    shard_bytes = 2 * w.B * w.Hkv * R * w.d * (2 if w.dtype == "bf16" else 4)
+    copy_ms = sum(ms["copies"].values()) / len(ranks)
+    for kd in kinds + ["copies"]:
+        print(f"[bench] {kd} per-rank ms: " + ", ".join(f"{r}:{ms[kd][r]:.3f}" for r in ranks),
+              file=sys.stderr, flush=True)
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, full, idx[ranks[0]], allp, cu, args.cpu_seconds, ranks[0], False)
+    ach = tot / (staged * 1e-3) / 1e12
+    out = {
+        "metric": "ring forward as separate steps with rotating K/V copies: TFLOP/s per virtual rank",
+        "value": rate("steps_staged"),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "pass": "rotate", "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "d": w.d, "S": w.S,
+                   "cp": w.cp, "ranks": ranks,
+                   "step": "per rank, one after another: the fused ring, the steps in place, the steps with "
+                           "staged copies on a second stream, the same in line, and the copies alone; "
+                           "value is the staged, overlapped rate"},
+        "pct_peak": round(100 * rate("steps_staged") / peak, 2),
+        "rotate": {
+            "TFLOP/s": {kd: rate(kd) for kd in kinds},
+            "per_rank_ms": {kd: {str(r): round(x, 4) for r, x in ms[kd].items()} for kd in kinds + ["copies"]},
+            "copy_bytes_per_rank": shard_bytes * (w.cp - 1),
+            "copies_alone_GB/s": round(shard_bytes * (w.cp - 1) / (copy_ms * 1e-3) / 1e9, 1),
+            "staged_over_in_place": round(staged / inplace, 4),
+            "exposed_copy_ms_per_rank": round((staged - inplace) / len(ranks), 4),
+        },
+        "roofline": {"bound": "mfma", "achieved": round(ach, 3), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(ach / peak, 4), "traffic": None,
+                     "kernel": "cp_attn_ring_fwd_stepwise launch with staging (per step fwd_bf16_kernel over one "
+                               "shard + merge_kernel, copies on a second stream); achieved = algorithmic flops per "
+                               "launch / mean launch time from HIP events on the launch stream"},
+        "cpu_baseline": cpu,
+    }
     print(json.dumps(out), flush=True)
 
 
