@@ -52,6 +52,11 @@ __all__ = [
     "bwd_delta",
     "attention_bwd",
     "partial_attention_bwd",
+    "a2a_pack",
+    "a2a_unpack_pack",
+    "a2a_exchange",
+    "a2a_unpack",
+    "a2a_pack_unpack",
     "ring_partials_fwd",
     "attention_matrix_bytes",
 ]
@@ -339,6 +344,66 @@ def partial_attention_bwd(q_rows, k_rows, v_rows, dout, lse, delta, scale, q_pos
             dq[b, h] = scale * (dS @ k[b, kvh])
             dk[b, kvh] += scale * (dS.T @ q[b, h])
     return dq, dk, dv
+
+
+# --------------------------------------------------------------------------
+# All-to-all level of hierarchical context parallelism: the head exchange
+# --------------------------------------------------------------------------
+# NeMo Megatron-Bridge "Hierarchical Context Parallel Skill": with cp_comm_type
+# "a2a+p2p" the first level is a group of g ranks that communicate all-to-all.
+# The page gives no layout; the reading here is the head exchange: before it a
+# rank holds all heads of its rows, after it all rows of the group for H/g of
+# the heads.  These functions move data only; every value is copied exactly.
+def a2a_pack(x, g):
+    """Send buffer of one rank before the exchange.  x: [rows, H, d], the rank's
+    sequence shard, token-major.  Returns [g, H/g, rows, d]: block j holds
+    heads j*H/g .. (j+1)*H/g - 1 of every row, head-major, the part rank j
+    receives: send[j, hh, t] = x[t, j*H/g + hh]."""
+    rows, H, d = x.shape
+    Hg = H // g
+    send = np.empty((g, Hg, rows, d), dtype=x.dtype)
+    for j in range(g):
+        for hh in range(Hg):
+            send[j, hh] = x[:, j * Hg + hh]
+    return send
+
+
+def a2a_unpack_pack(send):
+    """Inverse of a2a_pack: x[t, j*H/g + hh] = send[j, hh, t]."""
+    g, Hg, rows, d = send.shape
+    x = np.empty((rows, g * Hg, d), dtype=send.dtype)
+    for j in range(g):
+        for hh in range(Hg):
+            x[:, j * Hg + hh] = send[j, hh]
+    return x
+
+
+def a2a_exchange(sends):
+    """The all-to-all itself: rank j receives block j of every rank's send
+    buffer, in source-rank order (recv_j[i] = send_i[j])."""
+    g = len(sends)
+    return [np.stack([sends[i][j] for i in range(g)]) for j in range(g)]
+
+
+def a2a_unpack(recv):
+    """Layout after the exchange.  recv: [g, H/g, rows, d], block i from rank i.
+    Returns [H/g, g*rows, d]: the rank's heads over all g*rows rows of the
+    group, rows in source-rank order: y[hh, i*rows + t] = recv[i, hh, t]."""
+    g, Hg, rows, d = recv.shape
+    y = np.empty((Hg, g * rows, d), dtype=recv.dtype)
+    for i in range(g):
+        y[:, i * rows:(i + 1) * rows] = recv[i]
+    return y
+
+
+def a2a_pack_unpack(y, g):
+    """Inverse of a2a_unpack: recv[i, hh, t] = y[hh, i*rows + t]."""
+    Hg, n, d = y.shape
+    rows = n // g
+    recv = np.empty((g, Hg, rows, d), dtype=y.dtype)
+    for i in range(g):
+        recv[i] = y[:, i * rows:(i + 1) * rows]
+    return recv
 
 
 # --------------------------------------------------------------------------

@@ -314,6 +314,46 @@ def test_partial_bwd_own_step_matches_central_differences():
         assert abs(fd - an) <= 1e-7 * max(1.0, abs(an))
 
 
+# ---------------------------------------------------------------- all-to-all head exchange
+def test_a2a_small_example_by_hand():
+    """rows = 2, H = 4, d = 1, g = 2, x[t, h] = 10 t + h."""
+    x = np.array([[[0], [1], [2], [3]], [[10], [11], [12], [13]]])
+    send = orc.a2a_pack(x, 2)
+    assert send[:, :, :, 0].tolist() == [[[0, 10], [1, 11]], [[2, 12], [3, 13]]]
+    y = orc.a2a_unpack(send)
+    assert y[:, :, 0].tolist() == [[0, 10, 2, 12], [1, 11, 3, 13]]
+
+
+@pytest.mark.parametrize("g,H,rows,d", [(2, 4, 3, 2), (4, 8, 5, 3), (1, 3, 4, 2), (8, 32, 2, 4)])
+def test_a2a_exchange_is_a_global_transpose(g, H, rows, d):
+    """The sequence-sharded tensor X [S, H, d] (rank i holds rows i*rows..),
+    packed, exchanged and unpacked, leaves on rank j exactly heads j*H/g.. of
+    X for all S rows, head-major: the block of numpy's transpose of X."""
+    rng = np.random.default_rng(70 + g)
+    S = g * rows
+    X = rng.integers(-1000, 1000, (S, H, d))
+    sends = [orc.a2a_pack(X[i * rows:(i + 1) * rows], g) for i in range(g)]
+    recvs = orc.a2a_exchange(sends)
+    Hg = H // g
+    XT = np.transpose(X, (1, 0, 2))
+    for j in range(g):
+        y = orc.a2a_unpack(recvs[j])
+        assert np.array_equal(y, XT[j * Hg:(j + 1) * Hg])
+        # the reverse direction restores each rank's shard
+        back = orc.a2a_exchange([orc.a2a_pack_unpack(orc.a2a_unpack(recvs[jj]), g) for jj in range(g)])
+        for i in range(g):
+            assert np.array_equal(orc.a2a_unpack_pack(back[i]), X[i * rows:(i + 1) * rows])
+
+
+def test_a2a_inverses_round_trip():
+    rng = np.random.default_rng(71)
+    x = rng.standard_normal((7, 12, 5))
+    for g in (1, 2, 3, 4, 6, 12):
+        assert np.array_equal(orc.a2a_unpack_pack(orc.a2a_pack(x, g)), x)
+        r = rng.standard_normal((g, 12 // g, 7, 5))
+        assert np.array_equal(orc.a2a_pack_unpack(orc.a2a_unpack(r), g), r)
+
+
 # ---------------------------------------------------------------- sharding, merge
 def test_zigzag_positions_are_a_permutation_and_cp1_is_identity():
     for S, cp in [(1024, 2), (64, 8), (48, 3), (32768, 8)]:
