@@ -13,7 +13,11 @@ shard already resident in HBM (index maps are built once, in set-up):
       shards are copied into a two-slot stage on a second stream (a rotation
       ring's receive, overlapped), and the same copies on the compute stream.
       ``value`` is the staged, overlapped rate; ``rotate`` gives all four and
-      the copies alone.
+      the copies alone;
+  --pass a2a: the head exchange layout calls of hierarchical CP's all-to-all
+      level (cp_a2a_pack, cp_a2a_unpack and their inverses) on one rank's
+      shard of the workload's queries ([S/cp, Hq, d]), for a2a group sizes
+      --a2a-groups; ``value`` is their HBM rate in GB/s (bytes read + written).
 ``value`` is the algorithmic work of a step divided by the time of the timed
 steps, in TFLOP/s: 4*d*Hq flops per allowed (query, key) pair for the forward
 (Q K^T and P V) and 10*d*Hq for the backward (Q K^T, dO V^T, P^T dO, dS K and
@@ -42,6 +46,7 @@ PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = {
     "fwd": ["context_causal_attention_amd/csrc/attn_fwd.hip", "context_causal_attention_amd/csrc/device_common.h"],
     "bwd": ["context_causal_attention_amd/csrc/attn_bwd.hip", "context_causal_attention_amd/csrc/device_common.h"],
+    "a2a": ["context_causal_attention_amd/csrc/a2a.hip", "context_causal_attention_amd/csrc/device_common.h"],
 }
 FLOPS_PER_PAIR_HEAD_DIM = {"fwd": 4.0, "bwd": 10.0}
 
@@ -84,7 +89,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="llama8b_s128k_cp8")
     ap.add_argument("--ranks", default="all", help="'all' or a comma list of virtual ranks")
-    ap.add_argument("--pass", dest="mode", choices=["fwd", "fwdbwd", "rotate"], default="fwdbwd")
+    ap.add_argument("--pass", dest="mode", choices=["fwd", "fwdbwd", "rotate", "a2a"], default="fwdbwd")
+    ap.add_argument("--a2a-groups", default="2,8", help="--pass a2a: comma list of all-to-all group sizes")
     ap.add_argument("--varlen-mode", choices=["stream", "per_doc"], default="stream",
                     help="how a varlen workload's packed stream is dealt to ranks")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -127,6 +133,9 @@ def main():
     w = si.WORKLOADS[args.workload]
     if args.mode == "rotate":
         rotate_bench(args, w)
+        return
+    if args.mode == "a2a":
+        a2a_bench(args, w)
         return
     bwd = args.mode == "fwdbwd"
     if bwd and w.dtype != "bf16":
@@ -270,6 +279,79 @@ def main():
     }
     if balance is not None:
         out["balance"] = balance
+    print(json.dumps(out), flush=True)
+
+
+def a2a_bench(args, w):
+    """--pass a2a (see the module docstring)."""
+    import numpy as np
+    import torch
+
+    import context_causal_attention_amd as cpa
+
+    dev = torch.device("cuda:0")
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    rows = w.S // w.cp
+    g_ = torch.Generator(device="cpu")
+    g_.manual_seed(w.seed)
+    x = torch.randn(rows, w.Hq, w.d, generator=g_, dtype=torch.float32).to(dt).to(dev)
+    nbytes = x.numel() * x.element_size()
+    groups = [int(t) for t in args.a2a_groups.split(",")]
+    stream = torch.cuda.current_stream(dev)
+    res = {}
+    for g in groups:
+        send = cpa.cp_a2a_pack(x, g)
+        y = cpa.cp_a2a_unpack(send)
+        back = torch.empty_like(x)
+        calls = {"pack": lambda: cpa.cp_a2a_pack(x, g, send),
+                 "unpack": lambda: cpa.cp_a2a_unpack(send, y),
+                 "unpack_inverse": lambda: cpa.cp_a2a_unpack_inverse(y, g, send),
+                 "pack_inverse": lambda: cpa.cp_a2a_pack_inverse(send, back)}
+        for name, fn in calls.items():
+            for _ in range(args.warmup):
+                fn()
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                  for _ in range(args.steps)]
+            torch.cuda.synchronize()
+            for a, b in ev:
+                a.record(stream)
+                fn()
+                b.record(stream)
+            torch.cuda.synchronize()
+            ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+            res[f"g{g}_{name}"] = {"ms": round(ms, 5), "GB/s": round(2 * nbytes / (ms * 1e-3) / 1e9, 1)}
+            print(f"[bench] a2a g={g} {name}: {ms * 1e3:.1f} us, {2 * nbytes / (ms * 1e-3) / 1e9:.0f} GB/s",
+                  file=sys.stderr, flush=True)
+    rates = [v["GB/s"] for v in res.values()]
+    value = float(np.mean(rates))
+    dominant = min(res, key=lambda k: res[k]["GB/s"])
+    ms_dom = res[dominant]["ms"]
+    out = {
+        "metric": "head exchange layout (all-to-all level of hierarchical CP): GB/s read + written per call",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(float(np.mean([v["ms"] for v in res.values()])), 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "pass": "a2a", "rows": rows, "heads": w.Hq, "d": w.d, "groups": groups,
+                   "step": "one call on one rank's query shard [S/cp, Hq, d]"},
+        "a2a": res,
+        "roofline": {"bound": "hbm", "achieved": round(2 * nbytes / (ms_dom * 1e-3) / 1e9, 1),
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(2 * nbytes / (ms_dom * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                     "traffic": stored_traffic("a2a", w.name),
+                     "kernel": f"rows_kernel of the slowest call ({dominant}); achieved = algorithmic bytes "
+                               f"(the shard read once and written once, {2 * nbytes} B) / mean call time from HIP "
+                               "events on the launch stream; traffic = calibrated FETCH_SIZE + WRITE_SIZE bytes "
+                               "per dispatch, mean over the calls"},
+        "cpu_baseline": None,
+    }
     print(json.dumps(out), flush=True)
 
 

@@ -27,7 +27,7 @@ __all__ = [
     "lib", "cp_version", "cp_last_error", "cp_shard_zigzag", "cp_unshard_zigzag",
     "cp_varlen_index", "cp_ring_source", "cp_pairs", "cp_attn_fwd_workspace",
     "cp_attn_partial_fwd", "cp_attn_merge", "cp_attn_ring_fwd", "RingFwdPlan", "cp_attn_ring_fwd_stepwise",
-    "RingFwdStepwisePlan",
+    "RingFwdStepwisePlan", "cp_a2a_pack", "cp_a2a_pack_inverse", "cp_a2a_unpack", "cp_a2a_unpack_inverse",
     "cp_attn_bwd_workspace", "cp_attn_bwd_delta", "cp_attn_partial_bwd", "cp_attn_ring_bwd", "RingBwdPlan",
 ]
 
@@ -88,6 +88,10 @@ def lib() -> ctypes.CDLL:
         L.cp_attn_ring_stage_bytes.restype = c_size_t
         L.cp_attn_ring_fwd_stepwise.argtypes = [POINTER(CpShape), c_int32, c_int32] + [c_void_p] * 6 + \
             [c_void_p, c_void_p, c_void_p, c_size_t, c_void_p, c_size_t, c_void_p, c_void_p]
+        L.cp_a2a_pack.argtypes = [c_int32, c_int32, c_int64, c_int32, c_int32, c_void_p, c_int64, c_void_p,
+                                  c_int32, c_void_p]
+        L.cp_a2a_unpack.argtypes = [c_int32, c_int32, c_int64, c_int32, c_int32, c_void_p, c_void_p, c_int32,
+                                    c_void_p]
         L.cp_attn_bwd_workspace.argtypes = [POINTER(CpShape), c_int32]
         L.cp_attn_bwd_workspace.restype = c_size_t
         L.cp_attn_bwd_delta.argtypes = [POINTER(CpShape), c_void_p, c_void_p, c_void_p, c_void_p]
@@ -96,7 +100,7 @@ def lib() -> ctypes.CDLL:
             [c_void_p, c_size_t, c_void_p]
         for name in ("cp_shard_zigzag", "cp_unshard_zigzag", "cp_varlen_index", "cp_ring_source",
                      "cp_attn_partial_fwd", "cp_attn_merge", "cp_attn_ring_fwd", "cp_attn_ring_fwd_stepwise",
-                     "cp_attn_bwd_delta",
+                     "cp_attn_bwd_delta", "cp_a2a_pack", "cp_a2a_unpack",
                      "cp_attn_partial_bwd", "cp_attn_ring_bwd"):
             getattr(L, name).restype = c_int32
         _lib_handle = L
@@ -342,6 +346,74 @@ def cp_attn_ring_fwd_stepwise(q_loc, k_all, v_all, cp, rank, q_pos, q_lo, k_pos_
     step), optionally with rotating K/V copies: final fp32 (O, LSE)."""
     return RingFwdStepwisePlan(q_loc, k_all, v_all, cp, rank, q_pos, q_lo, k_pos_all, scale, staged,
                                copy_stream, out, lse, workspace, stage).run()
+
+
+# ------------------------------------------------------------------ head exchange (all-to-all level)
+def _a2a_dtype(t):
+    if t.dtype not in _DT:
+        raise ValueError("head exchange tensors must be float32 or bfloat16")
+    return _DT[t.dtype]
+
+
+def _a2a_packed(t, g, H, rows, d, dtype, what):
+    if t.dtype != dtype or not t.is_contiguous() or tuple(t.shape) != (g, H // g, rows, d):
+        raise ValueError(f"{what} must be contiguous {dtype} [{g}, {H // g}, {rows}, {d}]")
+    return t
+
+
+def _a2a_shard(x, what):
+    if x.dim() != 3 or x.stride(2) != 1 or x.stride(1) != x.shape[2]:
+        raise ValueError(f"{what} must be [rows, heads, d] with heads contiguous within a row")
+    return x
+
+
+def cp_a2a_pack(x, g, send=None):
+    """Sequence shard x [rows, H, d] -> send buffer [g, H/g, rows, d]."""
+    _a2a_shard(x, "x")
+    rows, H, d = x.shape
+    send = torch.empty(g, H // max(g, 1), rows, d, dtype=x.dtype, device=x.device) if send is None else send
+    _a2a_packed(send, g, H, rows, d, x.dtype, "send")
+    _check(lib().cp_a2a_pack(g, H, rows, d, _a2a_dtype(x), x.data_ptr(), x.stride(0), send.data_ptr(), 0,
+                             _stream(x.device)))
+    return send
+
+
+def cp_a2a_pack_inverse(send, x):
+    """Send buffer [g, H/g, rows, d] -> the sequence shard x [rows, H, d] (written in place)."""
+    _a2a_shard(x, "x")
+    rows, H, d = x.shape
+    g = send.shape[0]
+    _a2a_packed(send, g, H, rows, d, x.dtype, "send")
+    _check(lib().cp_a2a_pack(g, H, rows, d, _a2a_dtype(x), x.data_ptr(), x.stride(0), send.data_ptr(), 1,
+                             _stream(x.device)))
+    return x
+
+
+def cp_a2a_unpack(recv, y=None):
+    """Received blocks [g, H/g, rows, d] -> [H/g, g*rows, d] (heads, the group's rows in source order)."""
+    g, Hg, rows, d = recv.shape
+    _a2a_packed(recv, g, g * Hg, rows, d, recv.dtype, "recv")
+    y = torch.empty(Hg, g * rows, d, dtype=recv.dtype, device=recv.device) if y is None else y
+    if y.dtype != recv.dtype or not y.is_contiguous() or tuple(y.shape) != (Hg, g * rows, d):
+        raise ValueError(f"y must be contiguous [{Hg}, {g * rows}, {d}]")
+    _check(lib().cp_a2a_unpack(g, g * Hg, rows, d, _a2a_dtype(recv), recv.data_ptr(), y.data_ptr(), 0,
+                               _stream(recv.device)))
+    return y
+
+
+def cp_a2a_unpack_inverse(y, g, recv=None):
+    """[H/g, g*rows, d] -> the blocks [g, H/g, rows, d] that the reverse exchange sends back."""
+    Hg, n, d = y.shape
+    if g < 1 or n % g != 0:
+        raise ValueError("the row count of y must be a multiple of g")
+    rows = n // g
+    if y.dtype not in _DT or not y.is_contiguous():
+        raise ValueError("y must be contiguous float32 or bfloat16")
+    recv = torch.empty(g, Hg, rows, d, dtype=y.dtype, device=y.device) if recv is None else recv
+    _a2a_packed(recv, g, g * Hg, rows, d, y.dtype, "recv")
+    _check(lib().cp_a2a_unpack(g, g * Hg, rows, d, _a2a_dtype(y), recv.data_ptr(), y.data_ptr(), 1,
+                               _stream(y.device)))
+    return recv
 
 
 # ------------------------------------------------------------------ backward

@@ -16,7 +16,7 @@ OBJDIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libcpattn.so")
 
 ARCH = "gfx950"
-SOURCES = ["index.cpp", "api.cpp", "attn_fwd.hip", "attn_bwd.hip", "merge.hip"]
+SOURCES = ["index.cpp", "api.cpp", "attn_fwd.hip", "attn_bwd.hip", "merge.hip", "a2a.hip"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function", f"-I{INCLUDE}", f"-I{CSRC}"]
 # Packed fp32 VALU forms stay off in every device compile.

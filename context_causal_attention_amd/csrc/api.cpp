@@ -432,6 +432,46 @@ extern "C" int cp_attn_ring_fwd_stepwise(const cp_shape* s, int32_t cp, int32_t 
   return CP_OK;
 }
 
+namespace {
+
+int check_a2a(int32_t g, int32_t heads, int64_t rows, int32_t d, int32_t dtype) {
+  if (g < 1) return fail(CP_EINVAL, "group size g must be >= 1 (got %d)", g);
+  if (heads < 1 || heads > 65535) return fail(CP_EINVAL, "heads must be in [1, 65535] (got %d)", heads);
+  if (heads % g != 0) return fail(CP_EINVAL, "heads %d is not a multiple of g = %d", heads, g);
+  if (rows < 0) return fail(CP_EINVAL, "rows must be >= 0 (got %lld)", (long long)rows);
+  if (rows > (int64_t)1 << 31) return fail(CP_EINVAL, "rows %lld exceed 2^31", (long long)rows);
+  if (d != 64 && d != 128) return fail(CP_EINVAL, "head dimension %d is not 64 or 128", d);
+  return check_dtype(dtype, "dtype");
+}
+
+}  // namespace
+
+extern "C" int cp_a2a_pack(int32_t g, int32_t heads, int64_t rows, int32_t d, int32_t dtype, void* x,
+                           int64_t x_row_stride, void* send, int32_t inverse, hipStream_t stream) {
+  clear_error();
+  if (int rc = check_a2a(g, heads, rows, d, dtype)) return rc;
+  if (x_row_stride < (int64_t)heads * d)
+    return fail(CP_EINVAL, "x row stride %lld is smaller than heads*d = %lld", (long long)x_row_stride,
+                (long long)heads * d);
+  if ((x_row_stride * esize(dtype)) % 16 != 0) return fail(CP_EINVAL, "x row stride is not a multiple of 16 bytes");
+  if (rows == 0) return CP_OK;
+  if (int rc = check_ptrs16({{x, "x"}, {send, "send"}})) return rc;
+  return hip_status(inverse ? launch_a2a(g, heads, rows, d, dtype, send, x, x_row_stride, 0, 0, stream)
+                            : launch_a2a(g, heads, rows, d, dtype, x, send, x_row_stride, 0, 1, stream),
+                    "a2a pack launch");
+}
+
+extern "C" int cp_a2a_unpack(int32_t g, int32_t heads, int64_t rows, int32_t d, int32_t dtype, void* recv,
+                             void* y, int32_t inverse, hipStream_t stream) {
+  clear_error();
+  if (int rc = check_a2a(g, heads, rows, d, dtype)) return rc;
+  if (rows == 0) return CP_OK;
+  if (int rc = check_ptrs16({{recv, "recv"}, {y, "y"}})) return rc;
+  return hip_status(inverse ? launch_a2a(g, heads, rows, d, dtype, y, recv, 0, 1, 1, stream)
+                            : launch_a2a(g, heads, rows, d, dtype, recv, y, 0, 1, 0, stream),
+                    "a2a unpack launch");
+}
+
 extern "C" size_t cp_attn_bwd_workspace(const cp_shape* s, int32_t cp) {
   if (check_shape(s) != CP_OK || cp < 1) return 0;
   return bwd_workspace_layout(s->b, s->hq, s->hkv, s->d, s->sq, s->sk, cp).total;

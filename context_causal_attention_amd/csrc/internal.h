@@ -105,6 +105,12 @@ BwdWorkspace bwd_workspace_layout(int32_t b, int32_t hq, int32_t hkv, int32_t d,
 hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_delta(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
+// Head exchange layout kernels (a2a.hip).  unpack = 0: packed [g][H/g][rows][d]
+// against the sequence shard [rows, H, d] with row stride x_row_stride
+// (elements); unpack = 1: packed against [H/g][g*rows][d].  to_packed = 1
+// copies into the packed layout.
+hipError_t launch_a2a(int32_t g, int32_t heads, int64_t rows, int32_t d, int32_t dtype, const void* src, void* dst,
+                      int64_t x_row_stride, int32_t unpack, int32_t to_packed, hipStream_t stream);
 hipError_t launch_merge(int64_t rows, int32_t d, float* o_acc, float* lse_acc, const float* o_p,
                         const float* lse_p, hipStream_t stream);
 

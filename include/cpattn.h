@@ -202,6 +202,34 @@ int cp_attn_ring_fwd_stepwise(const cp_shape* s, int32_t cp, int32_t rank, const
                               void* ws, size_t ws_bytes, void* stage, size_t stage_bytes,
                               hipStream_t stream, hipStream_t copy_stream);
 
+/* ---------------------------------------------------------------- head exchange
+ * The all-to-all level of hierarchical context parallelism (NeMo
+ * Megatron-Bridge "Hierarchical Context Parallel Skill": with cp_comm_type
+ * "a2a+p2p" the first level is a group of g ranks that communicate
+ * all-to-all; the page gives no data layout).  Reading: the exchange trades
+ * heads for rows.  Before it a rank holds every head of its rows, after it
+ * every row of the group for H/g of the heads.  These calls are the rank-local
+ * halves of that exchange; the exchange itself (block j of rank i's send
+ * buffer becomes block i of rank j's receive buffer) is the collective's.
+ *
+ * cp_a2a_pack: x (device) [rows, heads, d], row stride x_row_stride elements
+ *   (>= heads*d, a multiple of 16 bytes), heads contiguous within a row ->
+ *   send (device) [g][heads/g][rows][d] contiguous: block j holds heads
+ *   j*heads/g .. of every row, head-major, the part rank j receives.
+ *   inverse != 0 copies send back into x.
+ * cp_a2a_unpack: recv (device) [g][heads/g][rows][d] contiguous, block i from
+ *   rank i -> y (device) [heads/g][g*rows][d] contiguous: this rank's heads
+ *   over the group's rows in source-rank order, the [heads, rows, d] layout
+ *   (one batch) the attention calls read.  inverse != 0 copies y back into recv.
+ * heads is the total head count H.  g >= 1 divides heads; heads <= 65535; d is
+ * 64 or 128; dtype CP_BF16 or CP_F32; pointers 16-byte aligned; source and
+ * destination must not overlap.  Every value is copied exactly.  rows == 0 is
+ * a no-op. */
+int cp_a2a_pack(int32_t g, int32_t heads, int64_t rows, int32_t d, int32_t dtype, void* x,
+                int64_t x_row_stride, void* send, int32_t inverse, hipStream_t stream);
+int cp_a2a_unpack(int32_t g, int32_t heads, int64_t rows, int32_t d, int32_t dtype, void* recv,
+                  void* y, int32_t inverse, hipStream_t stream);
+
 /* ---------------------------------------------------------------- backward
  * Gradients of the ring forward above with respect to q, k and v.  The pages
  * train through context-parallel attention (the Accelerate guide wraps the

@@ -249,6 +249,37 @@ def test_ring_fwd_stepwise_validation():
     assert _stepwise(_shape(sq=0)) == cpa.CP_OK  # no query rows: nothing to do, nothing launched
 
 
+def test_a2a_validation():
+    L = cpa.lib()
+    ok = dict(g=2, heads=32, rows=64, d=128, dtype=cpa.CP_BF16)
+
+    def pack(**kw):
+        a = dict(ok, **kw)
+        return L.cp_a2a_pack(a["g"], a["heads"], a["rows"], a["d"], a["dtype"], kw.get("x", FAKE),
+                             kw.get("rs", 32 * 128), kw.get("send", FAKE), 0, None)
+
+    def unpack(**kw):
+        a = dict(ok, **kw)
+        return L.cp_a2a_unpack(a["g"], a["heads"], a["rows"], a["d"], a["dtype"], kw.get("recv", FAKE),
+                               kw.get("y", FAKE), 1, None)
+
+    for f in (pack, unpack):
+        assert f(g=0) == cpa.CP_EINVAL
+        assert f(g=3) == cpa.CP_EINVAL          # 32 heads not a multiple of 3
+        assert f(heads=0) == cpa.CP_EINVAL
+        assert f(heads=70000, g=1) == cpa.CP_EINVAL
+        assert f(rows=-1) == cpa.CP_EINVAL
+        assert f(d=96) == cpa.CP_EINVAL
+        assert f(dtype=9) == cpa.CP_EDTYPE
+        assert f(rows=0) == cpa.CP_OK        # nothing to move, nothing launched
+    assert pack(rs=32 * 128 - 8) == cpa.CP_EINVAL   # row stride below heads*d
+    assert pack(rs=32 * 128 + 1) == cpa.CP_EINVAL   # not a multiple of 16 bytes
+    assert pack(x=0) == cpa.CP_EINVAL
+    assert pack(send=FAKE + 8) == cpa.CP_EINVAL
+    assert unpack(y=0) == cpa.CP_EINVAL
+    assert unpack(recv=FAKE + 4) == cpa.CP_EINVAL
+
+
 def test_workspace_query():
     s = _shape(sk=131072, sq=16384, hq=32, hkv=8)
     n = cpa.lib().cp_attn_fwd_workspace(ctypes.byref(s), 8)
