@@ -44,6 +44,8 @@ __all__ = [
     "all_rank_positions",
     "doc_start_of",
     "doc_end_of",
+    "causal_piece_work",
+    "whole_doc_deal",
     "allowed_mask",
     "pair_count",
     "attention_fwd",
@@ -92,6 +94,58 @@ def all_rank_positions(S: int, cp: int) -> np.ndarray:
 # --------------------------------------------------------------------------
 # Masks
 # --------------------------------------------------------------------------
+def causal_piece_work(doc_start: int, a: int, b: int) -> int:
+    """Causal (query, key) pairs of rows [a, b) of a document that starts at
+    doc_start: row p attends the p - doc_start + 1 positions doc_start..p."""
+    return sum(p - doc_start + 1 for p in range(a, b))
+
+
+def whole_doc_deal(cu_seqlens, cp: int):
+    """Whole-document placement: an own design.  The FlashCP abstract names
+    Whole-Doc sharding (entire documents on one rank) next to Per-Doc, but
+    gives no algorithm; this is a plain greedy under the ring's constraint
+    that every rank holds S/cp positions.
+
+    Documents are taken longest first (ties: lower index first).  A document
+    that fits whole in the remaining room of some rank goes whole to the
+    fitting rank with the least causal work so far (ties: lower rank).  A
+    document that fits nowhere is cut into consecutive pieces from its start,
+    each piece filling the rank with the most room left (ties: lower rank).
+    Work is counted with causal_piece_work.  Returns, per rank, its positions
+    in ascending order."""
+    cu = [int(x) for x in cu_seqlens]
+    n = len(cu) - 1
+    S = cu[-1]
+    C = S // cp
+    room = [C] * cp
+    load = [0] * cp
+    pieces = [[] for _ in range(cp)]
+    for i in sorted(range(n), key=lambda i: (-(cu[i + 1] - cu[i]), i)):
+        s, e = cu[i], cu[i + 1]
+        if e == s:
+            continue
+        fits = [r for r in range(cp) if room[r] >= e - s]
+        if fits:
+            r = min(fits, key=lambda r: (load[r], r))
+            pieces[r].append((s, e))
+            room[r] -= e - s
+            load[r] += causal_piece_work(s, s, e)
+            continue
+        a = s
+        while a < e:
+            r = max(range(cp), key=lambda r: (room[r], -r))
+            m = min(room[r], e - a)
+            pieces[r].append((a, a + m))
+            room[r] -= m
+            load[r] += causal_piece_work(s, a, a + m)
+            a += m
+    out = []
+    for r in range(cp):
+        pos = [p for a, b in pieces[r] for p in range(a, b)]
+        out.append(np.array(sorted(pos), dtype=np.int64))
+    return out
+
+
 def doc_start_of(positions, cu_seqlens) -> np.ndarray:
     """Start of the packed document that holds each global position."""
     positions = np.asarray(positions, dtype=np.int64)

@@ -314,6 +314,59 @@ def test_partial_bwd_own_step_matches_central_differences():
         assert abs(fd - an) <= 1e-7 * max(1.0, abs(an))
 
 
+# ---------------------------------------------------------------- whole-document placement
+def test_whole_doc_deal_worked_example():
+    """Documents of 7, 2, 1, 2 tokens (S = 12), cp = 3, room 4 per rank.
+    Longest first: the 7-token document fits nowhere whole, so it is cut: [0,4)
+    fills rank 0 (most room, lowest rank), [4,7) goes to rank 1 (room 4 > 4 - 0).
+    The 2-token document [7,9) fits only rank 2 (rank 1 has 1 left); the other
+    2-token document [10,12) fits only rank 2 as well (room 2); the 1-token
+    document [9,10) fits only rank 1."""
+    got = orc.whole_doc_deal([0, 7, 9, 10, 12], 3)
+    assert [g.tolist() for g in got] == [[0, 1, 2, 3], [4, 5, 6, 9], [7, 8, 10, 11]]
+
+
+def test_whole_doc_deal_least_loaded_rank_wins():
+    """Lengths 4, 3, 3, 2 (S = 12), cp = 2, room 6: the 4-token document goes to
+    rank 0 (tie, lower rank; work 10), the first 3-token one to rank 1 (work 0 <
+    10; gets 6), the second 3-token one fits only rank 1 (room 3), the 2-token
+    one only rank 0."""
+    got = orc.whole_doc_deal([0, 4, 7, 10, 12], 2)
+    assert [g.tolist() for g in got] == [[0, 1, 2, 3, 10, 11], [4, 5, 6, 7, 8, 9]]
+
+
+def test_causal_piece_work_closed_form():
+    for s, n in ((0, 1), (5, 7), (100, 33)):
+        assert orc.causal_piece_work(s, s, s + n) == n * (n + 1) // 2
+        for cut in range(s, s + n + 1):
+            assert orc.causal_piece_work(s, s, cut) + orc.causal_piece_work(s, cut, s + n) == n * (n + 1) // 2
+
+
+@pytest.mark.parametrize("cp,seed", [(2, 1), (4, 2), (8, 3), (3, 4)])
+def test_whole_doc_deal_properties(cp, seed):
+    """Every position on exactly one rank, S/cp positions per rank; at most
+    cp - 1 documents are cut (a document is cut only when it is longer than
+    every rank's room, so its first piece fills a rank completely, and once a
+    single rank has room every remaining document fits it); the per-rank
+    causal work counted by the pair counter equals the work of the pieces."""
+    total = 2 * cp * 1000
+    L = si.doc_lengths(total=total, mean=300, sigma=1.0, lo=8, hi=2500, seed=seed)
+    cu = si.cu_seqlens_from_lengths(L)
+    parts = orc.whole_doc_deal(cu, cp)
+    allpos = np.concatenate(parts)
+    assert np.array_equal(np.sort(allpos), np.arange(total))
+    assert all(len(p) == total // cp for p in parts)
+    owner = np.empty(total, dtype=np.int64)
+    for r, p in enumerate(parts):
+        owner[p] = r
+    whole = sum(1 for i in range(len(L)) if L[i] > 0 and len(set(owner[cu[i]:cu[i + 1]])) == 1)
+    assert whole >= len(L) - (cp - 1)
+    for p in parts:
+        lo = orc.doc_start_of(p, cu)
+        work = orc.pair_count(p, lo, allpos)
+        assert work == sum(orc.causal_piece_work(int(l), int(x), int(x) + 1) for x, l in zip(p, lo))
+
+
 # ---------------------------------------------------------------- all-to-all head exchange
 def test_a2a_small_example_by_hand():
     """rows = 2, H = 4, d = 1, g = 2, x[t, h] = 10 t + h."""
