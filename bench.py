@@ -91,7 +91,7 @@ def parse():
     ap.add_argument("--ranks", default="all", help="'all' or a comma list of virtual ranks")
     ap.add_argument("--pass", dest="mode", choices=["fwd", "fwdbwd", "rotate", "a2a"], default="fwdbwd")
     ap.add_argument("--a2a-groups", default="2,8", help="--pass a2a: comma list of all-to-all group sizes")
-    ap.add_argument("--varlen-mode", choices=["stream", "per_doc"], default="stream",
+    ap.add_argument("--varlen-mode", choices=["stream", "per_doc", "whole_doc"], default="stream",
                     help="how a varlen workload's packed stream is dealt to ranks")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time for the cpu_baseline sample")
@@ -153,7 +153,7 @@ def main():
         allp = cpa.cp_unshard_zigzag(w.S, w.cp)
         idx = {r: (cpa.cp_shard_zigzag(w.S, w.cp, r), None) for r in ranks}
     else:
-        vmode = cpa.CP_PER_DOC if args.varlen_mode == "per_doc" else cpa.CP_STREAM
+        vmode = {"stream": cpa.CP_STREAM, "per_doc": cpa.CP_PER_DOC, "whole_doc": cpa.CP_WHOLE_DOC}[args.varlen_mode]
         every = [cpa.cp_varlen_index(cu, w.cp, r, vmode) for r in range(w.cp)]
         allp = np.concatenate([e[0] for e in every])
         idx = {r: every[r] for r in ranks}
@@ -372,7 +372,7 @@ def rotate_bench(args, w):
         allp = cpa.cp_unshard_zigzag(w.S, w.cp)
         idx = {r: (cpa.cp_shard_zigzag(w.S, w.cp, r), None) for r in ranks}
     else:
-        vmode = cpa.CP_PER_DOC if args.varlen_mode == "per_doc" else cpa.CP_STREAM
+        vmode = {"stream": cpa.CP_STREAM, "per_doc": cpa.CP_PER_DOC, "whole_doc": cpa.CP_WHOLE_DOC}[args.varlen_mode]
         every = [cpa.cp_varlen_index(cu, w.cp, r, vmode) for r in range(w.cp)]
         allp = np.concatenate([e[0] for e in every])
         idx = {r: every[r] for r in ranks}

@@ -23,7 +23,7 @@ import torch
 
 __all__ = [
     "CP_OK", "CP_EINVAL", "CP_ESHAPE", "CP_EDTYPE", "CP_EWORKSPACE", "CP_EHIP",
-    "CP_F32", "CP_BF16", "CP_STREAM", "CP_PER_DOC", "CpShape", "CpError", "LIB_PATH",
+    "CP_F32", "CP_BF16", "CP_STREAM", "CP_PER_DOC", "CP_WHOLE_DOC", "CpShape", "CpError", "LIB_PATH",
     "lib", "cp_version", "cp_last_error", "cp_shard_zigzag", "cp_unshard_zigzag",
     "cp_varlen_index", "cp_ring_source", "cp_pairs", "cp_attn_fwd_workspace",
     "cp_attn_partial_fwd", "cp_attn_merge", "cp_attn_ring_fwd", "RingFwdPlan", "cp_attn_ring_fwd_stepwise",
@@ -36,7 +36,7 @@ LIB_PATH = os.path.join(_PKG, "libcpattn.so")
 
 CP_OK, CP_EINVAL, CP_ESHAPE, CP_EDTYPE, CP_EWORKSPACE, CP_EHIP = range(6)
 CP_F32, CP_BF16 = 0, 1
-CP_STREAM, CP_PER_DOC = 0, 1
+CP_STREAM, CP_PER_DOC, CP_WHOLE_DOC = 0, 1, 2
 
 _DT = {torch.float32: CP_F32, torch.bfloat16: CP_BF16}
 _I32P = POINTER(c_int32)

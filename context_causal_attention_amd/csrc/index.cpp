@@ -36,6 +36,51 @@ void deal(int64_t base, int64_t len, int32_t cp, int32_t rank, int32_t* out) {
   for (int64_t i = 0; i < c; ++i) out[c + i] = (int32_t)(base + b * c + i);
 }
 
+// Causal pairs of rows [a, b) of a document that starts at s.
+int64_t piece_work(int64_t s, int64_t a, int64_t b) { return (b - a) * ((a - s + 1) + (b - s)) / 2; }
+
+// Whole-document placement over all ranks (rule in cpattn.h); writes rank's
+// positions, ascending.
+void whole_doc(const int32_t* cu, int32_t n_docs, int32_t cp, int32_t rank, int32_t* out) {
+  const int64_t S = cu[n_docs];
+  std::vector<int64_t> room(cp, S / cp), load(cp, 0);
+  std::vector<std::pair<int64_t, int64_t>> mine;  // pieces [a, b) of this rank
+  std::vector<int32_t> order(n_docs);
+  for (int32_t i = 0; i < n_docs; ++i) order[i] = i;
+  std::sort(order.begin(), order.end(), [&](int32_t x, int32_t y) {
+    const int64_t lx = (int64_t)cu[x + 1] - cu[x], ly = (int64_t)cu[y + 1] - cu[y];
+    return lx != ly ? lx > ly : x < y;
+  });
+  auto place = [&](int32_t r, int64_t s, int64_t a, int64_t b) {
+    room[r] -= b - a;
+    load[r] += piece_work(s, a, b);
+    if (r == rank) mine.emplace_back(a, b);
+  };
+  for (int32_t i : order) {
+    const int64_t s = cu[i], e = cu[i + 1];
+    if (e == s) continue;
+    int32_t best = -1;
+    for (int32_t r = 0; r < cp; ++r)
+      if (room[r] >= e - s && (best < 0 || load[r] < load[best])) best = r;
+    if (best >= 0) {
+      place(best, s, s, e);
+      continue;
+    }
+    for (int64_t a = s; a < e;) {
+      int32_t r = 0;
+      for (int32_t q = 1; q < cp; ++q)
+        if (room[q] > room[r]) r = q;
+      const int64_t m = std::min(room[r], e - a);
+      place(r, s, a, a + m);
+      a += m;
+    }
+  }
+  std::sort(mine.begin(), mine.end());
+  int64_t k = 0;
+  for (const auto& pc : mine)
+    for (int64_t p = pc.first; p < pc.second; ++p) out[k++] = (int32_t)p;
+}
+
 }  // namespace
 
 extern "C" int cp_shard_zigzag(int64_t S, int32_t cp, int32_t rank, int32_t* pos_out) {
@@ -63,7 +108,8 @@ extern "C" int cp_varlen_index(const int32_t* cu, int32_t n_docs, int32_t cp, in
   if (!cu || !pos_out || !lo_out) return fail(CP_EINVAL, "null pointer argument");
   if (n_docs < 1) return fail(CP_EINVAL, "n_docs must be >= 1 (got %d)", n_docs);
   if (int rc = check_cp_rank(cp, rank)) return rc;
-  if (mode != CP_STREAM && mode != CP_PER_DOC) return fail(CP_EINVAL, "unknown shard mode %d", mode);
+  if (mode != CP_STREAM && mode != CP_PER_DOC && mode != CP_WHOLE_DOC)
+    return fail(CP_EINVAL, "unknown shard mode %d", mode);
   if (cu[0] != 0) return fail(CP_ESHAPE, "cu_seqlens[0] must be 0 (got %d)", cu[0]);
   for (int32_t i = 0; i < n_docs; ++i)
     if (cu[i + 1] < cu[i]) return fail(CP_ESHAPE, "cu_seqlens decreases at index %d", i);
@@ -72,6 +118,8 @@ extern "C" int cp_varlen_index(const int32_t* cu, int32_t n_docs, int32_t cp, in
   const int64_t per = S / cp;
   if (mode == CP_STREAM) {
     deal(0, S, cp, rank, pos_out);
+  } else if (mode == CP_WHOLE_DOC) {
+    whole_doc(cu, n_docs, cp, rank, pos_out);
   } else {
     int64_t off = 0;
     for (int32_t i = 0; i < n_docs; ++i) {

@@ -65,7 +65,8 @@ enum cp_dtype { CP_F32 = 0, CP_BF16 = 1 };
 
 enum cp_shard_mode {
   CP_STREAM = 0,  /* zigzag of the packed stream: rank r holds stream chunks r and 2cp-1-r */
-  CP_PER_DOC = 1  /* every document cut into 2cp chunks; rank r holds chunks r and 2cp-1-r of each */
+  CP_PER_DOC = 1, /* every document cut into 2cp chunks; rank r holds chunks r and 2cp-1-r of each */
+  CP_WHOLE_DOC = 2 /* whole documents placed greedily (own design, see cp_varlen_index) */
 };
 
 /* Shape and layout descriptor of an attention call. */
@@ -105,8 +106,17 @@ int cp_unshard_zigzag(int64_t S, int32_t cp, int32_t* perm_out);
  * mode CP_STREAM deals the whole packed stream zigzag (needs S % 2cp == 0);
  * CP_PER_DOC deals every document zigzag on its own (needs every document
  * length % 2cp == 0), keeping documents in order, so a rank's local document
- * boundaries are cu_seqlens / cp.  The whole-document and per-document
- * sharding of packed sequences is named in the FlashCP abstract. */
+ * boundaries are cu_seqlens / cp.  CP_WHOLE_DOC keeps documents whole where it
+ * can (needs S % 2cp == 0).  The whole-document and per-document sharding of
+ * packed sequences is named in the FlashCP abstract, without an algorithm for
+ * the former; this one is an own greedy design under the ring's constraint of
+ * S/cp positions per rank: documents longest first (ties: lower index); one
+ * that fits whole in some rank's remaining room goes whole to the fitting rank
+ * with the least causal work so far (ties: lower rank); one that fits nowhere
+ * is cut into consecutive pieces from its start, each filling the rank with the
+ * most room left (ties: lower rank).  Rows of rows [a, b) of a document that
+ * starts at s count sum over p in [a, b) of (p - s + 1) causal pairs.  At most
+ * cp - 1 documents are cut.  A rank's positions come out in ascending order. */
 int cp_varlen_index(const int32_t* cu_seqlens, int32_t n_docs, int32_t cp, int32_t rank,
                     int32_t mode, int32_t* pos_out, int32_t* lo_out);
 

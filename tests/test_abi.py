@@ -147,6 +147,33 @@ def test_varlen_deals_balance_at_workload_size():
     assert max(counts[cpa.CP_STREAM]) > 1.2 * min(counts[cpa.CP_PER_DOC])
 
 
+@pytest.mark.parametrize("cp,seed", [(2, 5), (3, 6), (4, 7), (8, 8)])
+def test_varlen_whole_doc_index_matches_oracle(cp, seed):
+    total = 2 * cp * 1500
+    L = si.doc_lengths(total=total, mean=350, sigma=1.0, lo=8, hi=3000, seed=seed)
+    cu = si.cu_seqlens_from_lengths(L)
+    ref = orc.whole_doc_deal(cu, cp)
+    for r in range(cp):
+        pos, lo = cpa.cp_varlen_index(cu, cp, r, cpa.CP_WHOLE_DOC)
+        assert np.array_equal(pos, ref[r])
+        assert np.array_equal(lo, orc.doc_start_of(pos, cu))
+
+
+def test_varlen_whole_doc_at_workload_size():
+    """The 65536-token packed documents (cp = 4): the whole-document deal
+    matches the oracle and keeps the causal work within 3% of the mean."""
+    w = si.WORKLOADS["varlen_s64k_cp4"]
+    cu = si.workload_cu_seqlens(w)
+    ref = orc.whole_doc_deal(cu, w.cp)
+    every = [cpa.cp_varlen_index(cu, w.cp, r, cpa.CP_WHOLE_DOC) for r in range(w.cp)]
+    for (pos, _), rp in zip(every, ref):
+        assert np.array_equal(pos, rp)
+    allp = np.concatenate([e[0] for e in every])
+    work = [cpa.cp_pairs(p, l, allp) for p, l in every]
+    assert work == [orc.pair_count(p, orc.doc_start_of(p, cu), allp) for p, _ in every]
+    assert max(work) <= 1.03 * (sum(work) / len(work))
+
+
 def test_varlen_errors():
     with pytest.raises(ValueError, match="must be 0"):
         cpa.cp_varlen_index([1, 8], 2, 0)

@@ -128,12 +128,13 @@ def test_ring_bwd_128k_cp8_sampled(rank):
             assert e <= GTOL, f"{name} of the last 128 keys, kv head {kvh}: max-abs error {e:.3e}"
 
 
-@pytest.mark.parametrize("mode", [cpa.CP_STREAM, cpa.CP_PER_DOC])
+@pytest.mark.parametrize("mode", [cpa.CP_STREAM, cpa.CP_PER_DOC, cpa.CP_WHOLE_DOC])
 def test_ring_bwd_varlen(mode):
     """Block-diagonal document masks: each rank's loss against the oracle with
     the same cu_seqlens."""
     cp, d = 2, 128
-    lens = [256, 512, 128, 640, 512] if mode == cpa.CP_STREAM else [256, 512, 128, 640, 512]
+    # whole-document deal: the 300-token document fits no rank whole and is cut
+    lens = [900, 300, 500, 348] if mode == cpa.CP_WHOLE_DOC else [256, 512, 128, 640, 512]
     cu = si.cu_seqlens_from_lengths(lens)
     S = int(cu[-1])
     full = si.make_qkv(1, 4, 2, S, d, "bf16", seed=5, with_dout=True)

@@ -116,10 +116,10 @@ def test_ring_fp32_d128_and_gqa_groups():
         assert_close(o, lse, *R.oracle(), "f32", f"rank {rank}")
 
 
-@pytest.mark.parametrize("mode", [cpa.CP_STREAM, cpa.CP_PER_DOC])
+@pytest.mark.parametrize("mode", [cpa.CP_STREAM, cpa.CP_PER_DOC, cpa.CP_WHOLE_DOC])
 def test_ring_varlen_documents(mode):
     cp = 4
-    if mode == cpa.CP_STREAM:
+    if mode != cpa.CP_PER_DOC:
         L = si.doc_lengths(total=4096, mean=400, sigma=1.0, lo=16, hi=3000, seed=7)
     else:
         L = (si.doc_lengths(total=4096, mean=400, sigma=1.0, lo=16, hi=3000, seed=7) // 8) * 8
