@@ -46,7 +46,7 @@ struct BParams {
   const int* q_lo;       // may be null
   const int* k_pos;
   // workspace
-  const int4* kbounds;   // per 64-key tile {min pos, max pos, valid rows, 0}
+  const int4* kbounds;   // per 64-key tile {min pos, max pos, gap lo, gap hi}
   const int* kpos_pad;   // per key slot, padding = kInvalidKey
   const int4* qbounds;   // per 64-row query tile {min pos, max pos, min lo, max lo}
   const int* qlo_pad;    // per query slot [sq_pad]: document start (padding INT_MIN)
@@ -80,7 +80,8 @@ __global__ __launch_bounds__(64) void key_prep_kernel(BParams p, int4* __restric
   const int kp = ok ? p.k_pos[r0 + tid] : 0;
   const int mn = wave_min(ok ? kp : INT_MAX);
   const int mx = wave_max(ok ? kp : INT_MIN);
-  if (tid == 0) kbounds[tile] = int4{mn, mx, nval, 0};
+  const int2 gp = largest_gap(wave_sort<64>(ok ? kp : INT_MAX, tid), nval, tid);
+  if (tid == 0) kbounds[tile] = int4{mn, mx, gp.x, gp.y};
   kpos_pad[tile * kKT + tid] = ok ? kp : kInvalidKey;
 }
 
@@ -203,7 +204,7 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(BParams p) {
   __shared__ __attribute__((aligned(16))) float sR1[4][kQT];
   __shared__ int2 sList[C::LIST];
   __shared__ int sCnt[NW];
-  __shared__ int sKb[NW][3];  // per wave: min key pos, max key pos, all keys valid
+  __shared__ int sKb[NW][5];  // per wave: min key pos, max key pos, all keys valid, gap lo, gap hi
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -259,10 +260,15 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(BParams p) {
     const int a = wave_min(kvalid ? kp : INT_MAX);
     const int c = wave_max(kvalid ? kp : INT_MIN);
     const bool all_valid = __all(kvalid);
+    // Lanes l and l + 32 hold the same key: sort the 32 keys over lanes 0..31.
+    const int nk = __popcll(__ballot(kvalid) & 0xffffffffull);
+    const int2 gp = largest_gap(wave_sort<32>(kvalid ? kp : INT_MAX, lane), nk, lane);
     if (lane == 0) {
       sKb[wave][0] = a;
       sKb[wave][1] = c;
       sKb[wave][2] = all_valid ? 1 : 0;
+      sKb[wave][3] = gp.x;
+      sKb[wave][4] = gp.y;
     }
   }
   __syncthreads();  // the list builder reads every wave's key bounds
@@ -319,8 +325,10 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(BParams p) {
 
   // ---- list of (query head, query tile) pairs this workgroup needs ---------
   // Entry .x = t | hg << 16 for tile t of query head kvh*g + hg; .y = class of
-  // wave w << 2w: skip when no key of the wave lies in [min lo, max pos] of the
-  // tile, full when every key lies in [max lo, min pos] and the tile is whole.
+  // wave w << 2w: skip when no key of the wave can lie in [min lo, max pos] of
+  // the tile (from the wave's key bounds and its largest gap between
+  // consecutive key positions), full when every key lies in [max lo, min pos]
+  // and the tile is whole.
   auto build = [&](int u0, int u1) {
     int cnt = 0;
     for (int base = u0; base < u1; base += NW * 64) {
@@ -338,7 +346,7 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(BParams p) {
         for (int w = 0; w < NW; ++w) {
           const int kmn = sKb[w][0], kmx = sKb[w][1];
           int cls = kSkip;
-          if (kmn != INT_MAX && kmn <= qb.y && kmx >= qb.z)
+          if (kmn != INT_MAX && kmn <= qb.y && kmx >= qb.z && !(sKb[w][3] < qb.z && qb.y < sKb[w][4]))
             cls = (sKb[w][2] && tile_full && kmx <= qb.x && kmn >= qb.w) ? kFull : kPartial;
           bits |= (unsigned)cls << (2 * w);
           act |= cls != kSkip;
@@ -797,8 +805,8 @@ __global__ __launch_bounds__(512, 1) void dq_kernel(BParams p) {
   const int total = p.cp * p.tpr;
   const int csh = 2 * wave;
   for (int u0 = 0; u0 < total; u0 += C::LIST) {
-    const int cnt = build_key_list<kKT, NW>(p.kbounds, p.tpr, p.rank, p.cp, u0, min(total, u0 + C::LIST), tid, wave,
-                                            lane, sWb, sList, sCnt);
+    const int cnt = build_key_list<kKT, NW>(p.kbounds, p.tpr, p.R, p.rank, p.cp, u0, min(total, u0 + C::LIST), tid,
+                                            wave, lane, sWb, sList, sCnt);
     if (cnt == 0) continue;
     auto ent = [&](int j) {
       int2 e;

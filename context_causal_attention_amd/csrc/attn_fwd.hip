@@ -64,7 +64,7 @@ struct KParams {
   const int* q_lo;          // may be null
   const int* k_pos;
   const int* kpos_pad;      // bf16: key positions per tile slot, padding = kInvalidKey
-  const int4* bounds;       // per key tile {min pos, max pos, valid rows, 0}
+  const int4* bounds;       // per key tile {min pos, max pos, gap lo, gap hi}
   char* o;
   float* lse;
   long long q_sb, q_sh, q_ss;
@@ -426,7 +426,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(KParams p) {
   const int csh = 2 * wave;
   auto cls_of = [&](int2 e) { return (int)(((unsigned)e.y >> csh) & 3); };
   for (int u0 = 0; u0 < total; u0 += kListCap) {
-    const int cnt = build_key_list<C::BN, kWaves>(p.bounds, p.tpr, p.rank, p.cp, u0, min(total, u0 + kListCap), tid,
+    const int cnt = build_key_list<C::BN, kWaves>(p.bounds, p.tpr, p.R, p.rank, p.cp, u0, min(total, u0 + kListCap), tid,
                                                   wave, lane, sWb, sList, sCnt);
     if (cnt == 0) continue;
     // Entry of list slot j (x: tile, y: classes), read as scalars.
@@ -628,7 +628,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_f32_kernel(KParams p) {
   const int csh = 2 * wave;
   auto entry_tile = [&](int2 e) { return (e.x & 0xFF) * p.tpr + ((e.x >> 8) & 0xFFFF); };
   for (int u0 = 0; u0 < total; u0 += kListCap) {
-    const int cnt = build_key_list<C::BN, kWaves>(p.bounds, p.tpr, p.rank, p.cp, u0, min(total, u0 + kListCap), tid,
+    const int cnt = build_key_list<C::BN, kWaves>(p.bounds, p.tpr, p.R, p.rank, p.cp, u0, min(total, u0 + kListCap), tid,
                                                   wave, lane, sWb, sList, sCnt);
     if (cnt == 0) continue;
     stage_load(entry_tile(sList[0]));
@@ -670,7 +670,8 @@ __global__ __launch_bounds__(256) void prep_kernel(const int* __restrict__ k_pos
     const int kp = ok ? k_pos[r0 + tid] : 0;
     const int mn = wave_min(ok ? kp : INT_MAX);
     const int mx = wave_max(ok ? kp : INT_MIN);
-    if (tid == 0) bounds[tile] = int4{mn, mx, nval, 0};
+    const int2 gp = largest_gap(wave_sort<64>(ok ? kp : INT_MAX, tid), nval, tid);
+    if (tid == 0) bounds[tile] = int4{mn, mx, gp.x, gp.y};
     if (BF16 && tid < BN) kpos_pad[tile * BN + tid] = ok ? kp : kInvalidKey;
   }
   if constexpr (BF16) {

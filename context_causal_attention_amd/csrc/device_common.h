@@ -84,6 +84,35 @@ __device__ __forceinline__ int wave_max(int x) {
   return x;
 }
 
+// Sorts x ascending over lanes 0..N-1 of each aligned group of N lanes (a
+// bitonic network over lane exchanges; N a power of two, at most 64).
+template <int N>
+__device__ __forceinline__ int wave_sort(int x, int lane) {
+#pragma unroll
+  for (int k = 2; k <= N; k <<= 1)
+#pragma unroll
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      const int y = __shfl_xor(x, j);
+      const bool up = (lane & k) == 0, low = (lane & j) == 0;
+      x = (up == low) ? min(x, y) : max(x, y);
+    }
+  return x;
+}
+
+// Largest gap between consecutive values of xs, sorted ascending over lanes
+// 0..n-1 (n <= 64): {the value before it, the value after it}, or {INT_MAX,
+// INT_MIN} when no two consecutive values are more than one apart.  Every
+// lane of the wave returns the same pair.
+__device__ __forceinline__ int2 largest_gap(int xs, int n, int lane) {
+  const int nxt = __shfl_down(xs, 1);
+  const int gap = lane + 1 < n ? nxt - xs : 0;
+  const int gmax = wave_max(gap);
+  if (gmax <= 1) return int2{INT_MAX, INT_MIN};
+  const unsigned long long at = __ballot(lane + 1 < n && gap == gmax);
+  const int idx = __builtin_ctzll(at);
+  return int2{__shfl(xs, idx), __shfl(nxt, idx)};
+}
+
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
 
 // Workgroups are dealt round-robin over the 8 XCDs; this gives each XCD a
@@ -97,11 +126,14 @@ __device__ __forceinline__ int xcd_logical_block() {
 
 // Lists, in ring order, the key tiles of schedule slots [u0, u1) that some wave
 // of this workgroup needs.  Slot u is ring step u / tpr (rank (rank - step) mod
-// cp) and tile u % tpr of that rank's shard.  Entry .x = src | i << 8; .y =
-// class(wave w) << 2w, from the tile bounds {min pos, max pos, valid rows} and
-// each wave's row bounds sWb[w] = {min q_pos, max q_pos, min q_lo, max q_lo}.
+// cp) and tile u % tpr of that rank's shard (R rows a shard).  Entry .x = src |
+// i << 8; .y = class(wave w) << 2w, from the tile bounds {min pos, max pos,
+// gap lo, gap hi} (no key of the tile lies strictly between gap lo and gap hi)
+// and each wave's row bounds sWb[w] = {min q_pos, max q_pos, min q_lo, max
+// q_lo}: skip when no key can lie in [min q_lo, max q_pos], full when every
+// key lies in [max q_lo, min q_pos] and the tile is whole.
 template <int BN, int NW>
-__device__ __forceinline__ int build_key_list(const int4* bounds, int tpr, int rank, int cp, int u0, int u1,
+__device__ __forceinline__ int build_key_list(const int4* bounds, int tpr, int R, int rank, int cp, int u0, int u1,
                                               int tid, int wave, int lane, const int (*sWb)[4], int2* sList,
                                               int* sCnt) {
   int cnt = 0;
@@ -115,13 +147,14 @@ __device__ __forceinline__ int build_key_list(const int4* bounds, int tpr, int r
       int src = rank - t;
       if (src < 0) src += cp;
       const int4 bd = bounds[src * tpr + i];
+      const bool whole = R - i * BN >= BN;
       entry.x = src | (i << 8);
       unsigned cls_bits = 0;
 #pragma unroll
       for (int w = 0; w < NW; ++w) {
         int cls = kSkip;
-        if (bd.z > 0 && bd.x <= sWb[w][1] && bd.y >= sWb[w][2])
-          cls = (bd.z == BN && bd.y <= sWb[w][0] && bd.x >= sWb[w][3]) ? kFull : kPartial;
+        if (bd.x <= sWb[w][1] && bd.y >= sWb[w][2] && !(bd.z < sWb[w][2] && sWb[w][1] < bd.w))
+          cls = (whole && bd.y <= sWb[w][0] && bd.x >= sWb[w][3]) ? kFull : kPartial;
         cls_bits |= (unsigned)cls << (2 * w);
         act |= cls != kSkip;
       }
