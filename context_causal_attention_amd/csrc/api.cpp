@@ -137,6 +137,7 @@ BwdWorkspace bwd_workspace_layout(int32_t b, int32_t hq, int32_t hkv, int32_t d,
   w.kbounds_off = take((size_t)nkt * 16);
   w.kpos_off = take((size_t)w.kt_row * 4);
   w.qbounds_off = take((size_t)nqt * 16);
+  w.qholes_off = take((size_t)nqt * 8);
   w.qlo_off = take((size_t)w.sq_pad * 4);
   w.qspan_off = take((size_t)w.sq_pad * 4);
   w.nl2_off = take((size_t)b * hq * (size_t)w.sq_pad * 4);

@@ -49,6 +49,7 @@ struct BParams {
   const int4* kbounds;   // per 64-key tile {min pos, max pos, gap lo, gap hi}
   const int* kpos_pad;   // per key slot, padding = kInvalidKey
   const int4* qbounds;   // per 64-row query tile {min pos, max pos, min lo, max lo}
+  const int2* qholes;    // per query tile: widest hole in the union of its rows' [lo, pos]
   const int* qlo_pad;    // per query slot [sq_pad]: document start (padding INT_MIN)
   const int* qspan_pad;  // position - document start (padding 0)
   const float* nl2;      // [b][hq][sq_pad]: -LSE * log2(e), 0 in padding and where LSE = -inf
@@ -91,8 +92,9 @@ __global__ __launch_bounds__(64) void key_prep_kernel(BParams p, int4* __restric
 // document start), the form the dK/dV kernel's mask test takes.
 __global__ __launch_bounds__(64) void query_prep_kernel(BParams p, const float* __restrict__ lse,
                                                         const float* __restrict__ delta, int4* __restrict__ qbounds,
-                                                        int* __restrict__ qlo_pad, int* __restrict__ qspan_pad,
-                                                        float* __restrict__ nl2, float* __restrict__ dlt) {
+                                                        int2* __restrict__ qholes, int* __restrict__ qlo_pad,
+                                                        int* __restrict__ qspan_pad, float* __restrict__ nl2,
+                                                        float* __restrict__ dlt) {
   const int tile = blockIdx.x;
   const int r0 = tile * kQT;
   const int nval = min(kQT, p.sq - r0);
@@ -104,7 +106,11 @@ __global__ __launch_bounds__(64) void query_prep_kernel(BParams p, const float* 
     const int ql = ok ? (p.q_lo ? p.q_lo[r0 + tid] : 0) : INT_MAX;
     const int a = wave_min(ok ? qp : INT_MAX), b = wave_max(ok ? qp : INT_MIN);
     const int c = wave_min(ok ? ql : INT_MAX), d = wave_max(ok ? ql : INT_MIN);
-    if (tid == 0) qbounds[tile] = int4{a, b, c, d};
+    const int2 hole = interval_hole(ql, qp, ok, tid, nval);
+    if (tid == 0) {
+      qbounds[tile] = int4{a, b, c, d};
+      qholes[tile] = hole;
+    }
     qlo_pad[r0 + tid] = ok ? ql : INT_MIN;
     qspan_pad[r0 + tid] = ok ? (int)((unsigned)qp - (unsigned)ql) : 0;
   }
@@ -339,6 +345,7 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(BParams p) {
         const int hg = u / p.nqt;
         const int t = u - hg * p.nqt;
         const int4 qb = p.qbounds[t];
+        const int2 qh = p.qholes[t];
         const bool tile_full = (t + 1) * kQT <= p.sq;
         entry.x = t | (hg << 16);
         unsigned bits = 0;
@@ -346,7 +353,8 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(BParams p) {
         for (int w = 0; w < NW; ++w) {
           const int kmn = sKb[w][0], kmx = sKb[w][1];
           int cls = kSkip;
-          if (kmn != INT_MAX && kmn <= qb.y && kmx >= qb.z && !(sKb[w][3] < qb.z && qb.y < sKb[w][4]))
+          if (kmn != INT_MAX && kmn <= qb.y && kmx >= qb.z && !(sKb[w][3] < qb.z && qb.y < sKb[w][4]) &&
+              !(qh.x < kmn && kmx < qh.y))
             cls = (sKb[w][2] && tile_full && kmx <= qb.x && kmn >= qb.w) ? kFull : kPartial;
           bits |= (unsigned)cls << (2 * w);
           act |= cls != kSkip;
@@ -612,7 +620,7 @@ __global__ __launch_bounds__(512, 1) void dq_kernel(BParams p) {
   __shared__ __attribute__((aligned(16))) int sP1[kKT];
   __shared__ int2 sList[C::LIST];
   __shared__ int sCnt[NW];
-  __shared__ int sWb[NW][4];
+  __shared__ int sWb[NW][6];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -652,16 +660,7 @@ __global__ __launch_bounds__(512, 1) void dq_kernel(BParams p) {
   const int ql = valid ? (p.q_lo ? p.q_lo[row] : 0) : INT_MAX;
   const float nl2 = valid ? p.nl2[bh * p.sq_pad + row] : 0.f;
   const float ndl = valid ? p.dlt[bh * p.sq_pad + row] : 0.f;
-  {
-    const int a = wave_min(valid ? qp : INT_MAX), bb = wave_max(valid ? qp : INT_MIN);
-    const int c = wave_min(valid ? ql : INT_MAX), d = wave_max(valid ? ql : INT_MIN);
-    if (lane == 0) {
-      sWb[wave][0] = a;
-      sWb[wave][1] = bb;
-      sWb[wave][2] = c;
-      sWb[wave][3] = d;
-    }
-  }
+  wave_row_bounds(wave, lane, valid, qp, ql, sWb);
   __syncthreads();
 
   const long long k_row_bytes = p.k_ss * 2;
@@ -867,6 +866,7 @@ hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
   p.kbounds = reinterpret_cast<const int4*>(ws + w.kbounds_off);
   p.kpos_pad = reinterpret_cast<const int*>(ws + w.kpos_off);
   p.qbounds = reinterpret_cast<const int4*>(ws + w.qbounds_off);
+  p.qholes = reinterpret_cast<const int2*>(ws + w.qholes_off);
   p.qlo_pad = reinterpret_cast<const int*>(ws + w.qlo_off);
   p.qspan_pad = reinterpret_cast<const int*>(ws + w.qspan_off);
   p.nl2 = reinterpret_cast<const float*>(ws + w.nl2_off);
@@ -903,7 +903,8 @@ hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
     if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
   }
   hipLaunchKernelGGL(query_prep_kernel, dim3(p.nqt, a.b * a.hq), dim3(64), 0, stream, p, a.lse, a.delta,
-                     reinterpret_cast<int4*>(ws + w.qbounds_off), reinterpret_cast<int*>(ws + w.qlo_off),
+                     reinterpret_cast<int4*>(ws + w.qbounds_off), reinterpret_cast<int2*>(ws + w.qholes_off),
+                     reinterpret_cast<int*>(ws + w.qlo_off),
                      reinterpret_cast<int*>(ws + w.qspan_off), reinterpret_cast<float*>(ws + w.nl2_off),
                      reinterpret_cast<float*>(ws + w.dlt_off));
   if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;

@@ -97,21 +97,6 @@ __device__ __forceinline__ Item map_block(const KParams& p) {
   return it;
 }
 
-// Row bounds of every wave (sWb[w] = {min q_pos, max q_pos, min q_lo, max q_lo}
-// over the wave's valid rows).
-__device__ __forceinline__ void wave_bounds(int wave, int lane, bool valid, int qp, int ql, int (*sWb)[4]) {
-  const int a = wave_min(valid ? qp : INT_MAX);
-  const int b = wave_max(valid ? qp : INT_MIN);
-  const int c = wave_min(valid ? ql : INT_MAX);
-  const int d = wave_max(valid ? ql : INT_MIN);
-  if (lane == 0) {
-    sWb[wave][0] = a;
-    sWb[wave][1] = b;
-    sWb[wave][2] = c;
-    sWb[wave][3] = d;
-  }
-}
-
 template <int DT>
 __device__ __forceinline__ void store_out(const KParams& p, const Item& it, int row, int hi, float m_run,
                                           float l_tot, const f32x16* oacc) {
@@ -169,7 +154,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(KParams p) {
   __shared__ __attribute__((aligned(16))) int sP1[C::BN];
   __shared__ int2 sList[kListCap];
   __shared__ int sCnt[kWaves];
-  __shared__ int sWb[kWaves][4];
+  __shared__ int sWb[kWaves][6];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps tile-class branches scalar
@@ -192,7 +177,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(KParams p) {
   }
   const int qp = valid ? p.q_pos[row] : -1;
   const int ql = valid ? (p.q_lo ? p.q_lo[row] : 0) : INT_MAX;
-  wave_bounds(wave, lane, valid, qp, ql, sWb);
+  wave_row_bounds(wave, lane, valid, qp, ql, sWb);
   __syncthreads();
 
   // ---- per-lane constant addresses ------------------------------------------
@@ -501,7 +486,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_f32_kernel(KParams p) {
   __shared__ __attribute__((aligned(16))) int sKpos[2][C::BN];
   __shared__ int2 sList[kListCap];
   __shared__ int sCnt[kWaves];
-  __shared__ int sWb[kWaves][4];
+  __shared__ int sWb[kWaves][6];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -525,7 +510,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_f32_kernel(KParams p) {
   }
   const int qp = valid ? p.q_pos[row] : -1;
   const int ql = valid ? (p.q_lo ? p.q_lo[row] : 0) : INT_MAX;
-  wave_bounds(wave, lane, valid, qp, ql, sWb);
+  wave_row_bounds(wave, lane, valid, qp, ql, sWb);
   __syncthreads();
 
   f32x16 oacc[C::DT];

@@ -113,6 +113,43 @@ __device__ __forceinline__ int2 largest_gap(int xs, int n, int lane) {
   return int2{__shfl(xs, idx), __shfl(nxt, idx)};
 }
 
+// Widest hole in the union of the intervals [lo, pos] of the lanes 0..n-1
+// with ok set, looked for between the intervals of adjacent lanes (rows in
+// position order): {h_lo, h_hi} such that no interval meets any k with h_lo <
+// k < h_hi, or {INT_MAX, INT_MIN} when there is none.  The candidate is
+// checked against every interval, so rows in any order give a correct (maybe
+// empty) answer.  Every lane returns the same pair.
+__device__ __forceinline__ int2 interval_hole(int lo, int pos, bool ok, int lane, int n) {
+  const int nlo = __shfl_down(lo, 1);
+  const int nok = __shfl_down(ok ? 1 : 0, 1);
+  const bool cand = lane + 1 < n && ok && nok && nlo > pos;
+  const int width = cand ? nlo - pos : 0;
+  const int wmax = wave_max(width);
+  if (wmax <= 1) return int2{INT_MAX, INT_MIN};
+  const int idx = __builtin_ctzll(__ballot(cand && width == wmax));
+  const int hlo = __shfl(pos, idx), hhi = __shfl(nlo, idx);
+  if (__ballot(lane < n && ok && lo < hhi && pos > hlo)) return int2{INT_MAX, INT_MIN};
+  return int2{hlo, hhi};
+}
+
+// Row bounds of a wave's 32 rows (lanes l and l + 32 hold the same row):
+// sWb[wave] = {min q_pos, max q_pos, min q_lo, max q_lo, hole lo, hole hi}.
+__device__ __forceinline__ void wave_row_bounds(int wave, int lane, bool valid, int qp, int ql, int (*sWb)[6]) {
+  const int a = wave_min(valid ? qp : INT_MAX);
+  const int b = wave_max(valid ? qp : INT_MIN);
+  const int c = wave_min(valid ? ql : INT_MAX);
+  const int d = wave_max(valid ? ql : INT_MIN);
+  const int2 h = interval_hole(ql, qp, valid, lane, 32);
+  if (lane == 0) {
+    sWb[wave][0] = a;
+    sWb[wave][1] = b;
+    sWb[wave][2] = c;
+    sWb[wave][3] = d;
+    sWb[wave][4] = h.x;
+    sWb[wave][5] = h.y;
+  }
+}
+
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
 
 // Workgroups are dealt round-robin over the 8 XCDs; this gives each XCD a
@@ -129,12 +166,12 @@ __device__ __forceinline__ int xcd_logical_block() {
 // cp) and tile u % tpr of that rank's shard (R rows a shard).  Entry .x = src |
 // i << 8; .y = class(wave w) << 2w, from the tile bounds {min pos, max pos,
 // gap lo, gap hi} (no key of the tile lies strictly between gap lo and gap hi)
-// and each wave's row bounds sWb[w] = {min q_pos, max q_pos, min q_lo, max
-// q_lo}: skip when no key can lie in [min q_lo, max q_pos], full when every
-// key lies in [max q_lo, min q_pos] and the tile is whole.
+// and each wave's row bounds sWb[w] (wave_row_bounds): skip when no key can
+// lie in [min q_lo, max q_pos] outside the rows' hole, full when every key
+// lies in [max q_lo, min q_pos] and the tile is whole.
 template <int BN, int NW>
 __device__ __forceinline__ int build_key_list(const int4* bounds, int tpr, int R, int rank, int cp, int u0, int u1,
-                                              int tid, int wave, int lane, const int (*sWb)[4], int2* sList,
+                                              int tid, int wave, int lane, const int (*sWb)[6], int2* sList,
                                               int* sCnt) {
   int cnt = 0;
   for (int base = u0; base < u1; base += NW * 64) {
@@ -153,7 +190,8 @@ __device__ __forceinline__ int build_key_list(const int4* bounds, int tpr, int R
 #pragma unroll
       for (int w = 0; w < NW; ++w) {
         int cls = kSkip;
-        if (bd.x <= sWb[w][1] && bd.y >= sWb[w][2] && !(bd.z < sWb[w][2] && sWb[w][1] < bd.w))
+        if (bd.x <= sWb[w][1] && bd.y >= sWb[w][2] && !(bd.z < sWb[w][2] && sWb[w][1] < bd.w) &&
+            !(sWb[w][4] < bd.x && bd.y < sWb[w][5]))
           cls = (whole && bd.y <= sWb[w][0] && bd.x >= sWb[w][3]) ? kFull : kPartial;
         cls_bits |= (unsigned)cls << (2 * w);
         act |= cls != kSkip;

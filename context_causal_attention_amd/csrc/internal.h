@@ -89,6 +89,7 @@ struct BwdWorkspace {
   size_t kbounds_off;  // int4 per key tile: {min pos, max pos, valid rows, 0}
   size_t kpos_off;     // int32 per key slot, padding = INT32_MAX
   size_t qbounds_off;  // int4 per query tile: {min pos, max pos, min lo, max lo}
+  size_t qholes_off;   // int2 per query tile: widest hole in the union of its rows' [lo, pos]
   size_t qlo_off;      // int32 [sq_pad]: document start, padding = INT32_MIN
   size_t qspan_off;    // int32 [sq_pad]: position - document start, padding = 0
   size_t nl2_off;      // fp32 [b][hq][sq_pad]: -LSE * log2(e)
