@@ -145,6 +145,30 @@ def test_ring_bwd_varlen(mode):
         _check_grads((dq, dk, dv), R.oracle_grads(), f"varlen mode {mode} rank {rank}")
 
 
+def test_ring_bwd_shuffled_rows_and_keys():
+    """The backward with a rank's rows and every shard's keys in random order
+    (whole-document deal): per-tile key gaps, per-wave and per-tile row holes
+    and the dK/dV waves' key gaps must hold for any order."""
+    cp, S, d = 2, 2048, 64
+    cu = si.cu_seqlens_from_lengths([900, 300, 500, 348])
+    full = si.make_qkv(1, 4, 2, S, d, "bf16", seed=24, with_dout=True)
+    rng = np.random.default_rng(25)
+    for rank in range(cp):
+        announce(f"ring bwd shuffled rows/keys rank {rank}")
+        R = Rank(1, 4, 2, S, d, cp, rank, "bf16", cu=cu, mode=cpa.CP_WHOLE_DOC, full=full)
+        pq = rng.permutation(len(R.pos))
+        R.pos, R.lo = R.pos[pq], R.lo[pq]
+        R.q_loc = R.q_loc[:, :, torch.from_numpy(pq)].contiguous()
+        R.do_loc = R.do_loc[:, :, torch.from_numpy(pq)].contiguous()
+        n = S // cp
+        pk = np.concatenate([s * n + rng.permutation(n) for s in range(cp)])
+        R.allp = R.allp[pk]
+        R.k_all = R.k_all[:, :, torch.from_numpy(pk)].contiguous()
+        R.v_all = R.v_all[:, :, torch.from_numpy(pk)].contiguous()
+        _, _, dq, dk, dv = R.ring_bwd()
+        _check_grads((dq, dk, dv), R.oracle_grads(), f"shuffled rank {rank}")
+
+
 def test_partial_bwd_steps_match_ring():
     """The per-step path (one cp_attn_partial_bwd a ring step, each with the
     final LSE and delta) adds up to the fused ring backward and to the oracle."""

@@ -265,3 +265,29 @@ def test_ring_fwd_stepwise_varlen_and_replay():
         torch.cuda.synchronize()
         assert torch.equal(plan.out, o_first) and torch.equal(plan.lse, l_first)
         assert_close(o_first, l_first, *R.oracle(), "bf16", f"stepwise varlen rank {rank}")
+
+
+@pytest.mark.parametrize("mode", [cpa.CP_STREAM, cpa.CP_WHOLE_DOC])
+def test_ring_shuffled_rows_and_keys(mode):
+    """Packed documents with the rank's rows in random order and the keys of
+    every shard in random order: tile bounds, key gaps and row holes must not
+    assume ascending positions (a hole found between adjacent rows is checked
+    against every row)."""
+    cp, S = 4, 4096
+    L = si.doc_lengths(total=S, mean=300, sigma=1.0, lo=16, hi=2000, seed=21)
+    cu = si.cu_seqlens_from_lengths(L)
+    full = si.make_qkv(1, 4, 2, S, 64, "bf16", seed=22)
+    rng = np.random.default_rng(23)
+    for rank in (0, 2):
+        announce(f"shuffled rows/keys mode {mode} rank {rank}")
+        R = Rank(1, 4, 2, S, 64, cp, rank, "bf16", full=full, cu=cu, mode=mode)
+        pq = rng.permutation(len(R.pos))
+        R.pos, R.lo = R.pos[pq], R.lo[pq]
+        R.q_loc = R.q_loc[:, :, torch.from_numpy(pq)].contiguous()
+        n = S // cp
+        pk = np.concatenate([s * n + rng.permutation(n) for s in range(cp)])
+        R.allp = R.allp[pk]
+        R.k_all = R.k_all[:, :, torch.from_numpy(pk)].contiguous()
+        R.v_all = R.v_all[:, :, torch.from_numpy(pk)].contiguous()
+        o, lse = R.ring_fwd()
+        assert_close(o, lse, *R.oracle(), "bf16", f"shuffled rank {rank}")
