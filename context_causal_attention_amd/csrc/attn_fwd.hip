@@ -9,8 +9,9 @@
 // recurrence so no score matrix is ever stored.
 //
 // Work decomposition
-//   A workgroup of 4 wave64s owns 128 query rows of one query head (32 rows a
-//   wave) and walks the ring's key tiles in step order.  Key tiles never cross
+//   A workgroup of 8 wave64s (one per CU: two per SIMD) owns 256 query rows of
+//   one query head (32 rows a wave) and walks the ring's key tiles in step
+//   order; each K and V^T tile copied into LDS serves all 8 waves.  Key tiles never cross
 //   a rank's shard.  Before the walk the workgroup lists the tiles it needs,
 //   each tagged, per wave, as skipped, "full" (no mask needed) or "partial"
 //   (per-element mask q_lo <= k_pos <= q_pos), from the position bounds of the
@@ -49,7 +50,7 @@ namespace fwdk {
 
 using namespace dev;
 
-constexpr int kWaves = 4;
+constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
 constexpr int kRowsPerWave = 32;
 constexpr int kBlockM = kWaves * kRowsPerWave;
@@ -141,7 +142,7 @@ struct Bf16Cfg {
 };
 
 template <int D>
-__global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(KParams p) {
+__global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(KParams p) {
   // The body uses device-only buffer-descriptor types; the host pass only needs
   // the launch stub.
 #if defined(__HIP_DEVICE_COMPILE__)
@@ -479,7 +480,7 @@ struct F32Cfg {
 };
 
 template <int D>
-__global__ __launch_bounds__(kThreads, 2) void fwd_f32_kernel(KParams p) {
+__global__ __launch_bounds__(kThreads, 1) void fwd_f32_kernel(KParams p) {
   using C = F32Cfg<D>;
   __shared__ __attribute__((aligned(16))) u32x4 sK[2][C::CHUNKS];
   __shared__ __attribute__((aligned(16))) u32x4 sV[2][C::CHUNKS];
