@@ -691,6 +691,24 @@ __global__ __launch_bounds__(512, 1) void dq_kernel(BParams p) {
     }
   }
 
+  // Row reads are a per-lane offset yoff(kk) plus a constant (buffer address
+  // and half-tile offset) that the DS offset field holds: the four K/V tiles
+  // lie in the first 64 KiB of LDS.  With ROW = 256 the offsets of slices
+  // 4..7 are those of slices 0..3 with bit 7 flipped.  The offsets pass
+  // through an empty asm in place at each half tile so that the compiler does
+  // not hoist offset + constant out of the loop as one register per read.
+  constexpr int NYO = C::QREG > 4 ? 4 : C::QREG;
+  static_assert(C::QREG <= 4 || C::ROW == 256, "offset reuse");
+  int yo[NYO];
+#pragma unroll
+  for (int kk = 0; kk < NYO; ++kk) yo[kk] = nrow * C::ROW + ((32 * kk) ^ nY);
+  auto yoff = [&](int kk) { return kk < NYO ? yo[kk] : (yo[kk - NYO] ^ 128); };
+  auto refresh = [&]() {
+#pragma unroll
+    for (int kk = 0; kk < NYO; ++kk) asm volatile("" : "+v"(yo[kk]));
+    asm volatile("" : "+v"(tP[0]), "+v"(tP[1]), "+v"(tA));
+  };
+
   const char* kbase = p.k + ((long long)b * p.k_sb + (long long)kvh * p.k_sh) * 2;
   const char* vbase = p.v + ((long long)b * p.v_sb + (long long)kvh * p.v_sh) * 2;
   const __amdgpu_buffer_rsrc_t rsP = __builtin_amdgcn_make_buffer_rsrc((void*)p.kpos_pad, 0, 0x7fffffff, kBufferFlags);
@@ -725,13 +743,6 @@ __global__ __launch_bounds__(512, 1) void dq_kernel(BParams p) {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rsP, (lds_ptr_t)pbuf(bc), 4, lane * 4, tile * kKT * 4, 0, 0);
   };
 
-  // Lane offsets pass through an empty asm where they are used (see the dK/dV
-  // kernel): reads are buffer + lane offset + a DS offset immediate.
-  auto launder = [](int off) {
-    asm volatile("" : "+v"(off));
-    return off;
-  };
-
   f32x16 dqa[C::DT];
 #pragma unroll
   for (int t = 0; t < C::DT; ++t)
@@ -740,9 +751,9 @@ __global__ __launch_bounds__(512, 1) void dq_kernel(BParams p) {
 
   // One half tile (sub: keys 32sub..32sub+31) of the tile in buffer buf.
   auto half = [&](auto bc, int sub, bool full) {
-    const int no = launder(nrow * C::ROW + sub * 32 * C::ROW);
-    const lds_char* kn = to_lds(kbuf(bc)) + no;
-    const lds_char* vn = to_lds(vbuf(bc)) + no;
+    refresh();
+    const lds_char* kn = to_lds(kbuf(bc)) + sub * 32 * C::ROW;
+    const lds_char* vn = to_lds(vbuf(bc)) + sub * 32 * C::ROW;
     // S^T, dP^T: register r is key 32sub + 16(r/8) + 8hi + r%8.  S^T starts
     // at 0, or on partial tiles at -inf for the keys outside [q_lo, q_pos] of
     // the lane's row, which makes P = 0 there: the vector part after the MFMAs
@@ -766,8 +777,9 @@ __global__ __launch_bounds__(512, 1) void dq_kernel(BParams p) {
     }
 #pragma unroll
     for (int kk = 0; kk < C::QREG; ++kk) {
-      const bf16x8 ak = lds_read8(kn + (nY ^ (32 * kk)));
-      const bf16x8 av = lds_read8(vn + (nY ^ (32 * kk)));
+      const int y = yoff(kk);
+      const bf16x8 ak = lds_read8(kn + y);
+      const bf16x8 av = lds_read8(vn + y);
       s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, qreg[kk], s, 0, 0, 0);
       dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, oreg[kk], dp, 0, 0, 0);
     }
@@ -789,14 +801,14 @@ __global__ __launch_bounds__(512, 1) void dq_kernel(BParams p) {
       }
     }
     // dQ^T += K^T dS^T over the half tile's 32 keys.
-    const lds_char* kt0 = to_lds(kbuf(bc)) + launder(tP[0] + sub * 32 * C::ROW);
-    const lds_char* kt1 = to_lds(kbuf(bc)) + launder(tP[1] + sub * 32 * C::ROW);
+    const lds_char* kt = to_lds(kbuf(bc)) + sub * 32 * C::ROW;
 #pragma unroll
     for (int gg = 0; gg < 2; ++gg)
 #pragma unroll
       for (int t = 0; t < C::DT; ++t) {
-        const int o = gg * 16 * C::ROW + ((64 * t) ^ tA);
-        const bf16x8 a = lds_read_tr(kt0 + o, kt1 + o);
+        const int xa = (64 * t) ^ tA;
+        const lds_char* kg = kt + gg * 16 * C::ROW;
+        const bf16x8 a = lds_read_tr(kg + (tP[0] + xa), kg + (tP[1] + xa));
         dqa[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, db[gg], dqa[t], 0, 0, 0);
       }
   };
@@ -823,8 +835,8 @@ __global__ __launch_bounds__(512, 1) void dq_kernel(BParams p) {
       if (j + 1 < cnt) issue(std::integral_constant<int, 1 - decltype(bc)::value>{}, ent(j + 1).x);
       const int cls = (int)(((unsigned)ent(j).y >> csh) & 3);
       if (cls != kSkip) {
-#pragma nounroll
-        for (int sub = 0; sub < 2; ++sub) half(bc, sub, cls == kFull);
+        half(bc, 0, cls == kFull);
+        half(bc, 1, cls == kFull);
       }
       wait_vmem();
       __syncthreads();
