@@ -309,7 +309,8 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(BParams p) {
   }
   // A row read of the loop is a per-lane offset yo[kk] plus a constant
   // (buffer address, half-tile and dO offsets) that the DS offset field holds;
-  // a transposed read adds (64 t) ^ tA to tP[h] first.  These offsets pass
+  // a transposed read of chunk group t uses xo[t] (+ xd for the second row
+  // group) the same way.  These offsets pass
   // through an empty asm, in place, at the start of each half tile, so that
   // the compiler does not hoist offset + constant out of the loop as one
   // register per read.  V and the per-row arrays lie above 64 KiB: their
@@ -318,6 +319,12 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(BParams p) {
   int yo[C::KREG];   // row reads: nrow*ROW + ((32 kk) ^ nY)
 #pragma unroll
   for (int kk = 0; kk < C::KREG; ++kk) yo[kk] = nrow * C::ROW + ((32 * kk) ^ nY);
+  // Transposed-read offsets of chunk group t for row group h = 0, and the
+  // lane's distance to row group h = 1.
+  int xo[C::DT];
+#pragma unroll
+  for (int t = 0; t < C::DT; ++t) xo[t] = tP[0] + ((64 * t) ^ tA);
+  int xd = tP[1] - tP[0];
   constexpr int kVAt = 4 * C::TILE;            // expected address of sV
   constexpr int kRAt = 4 * C::TILE + C::VTILE;  // expected address of sR0
   int vo = vbase + kVAt;
@@ -325,8 +332,9 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(BParams p) {
   auto refresh = [&]() {
 #pragma unroll
     for (int kk = 0; kk < C::KREG; ++kk) asm volatile("" : "+v"(yo[kk]));
-    asm volatile("" : "+v"(tP[0]), "+v"(tP[1]), "+v"(tA));
-    asm volatile("" : "+v"(vo), "+v"(ro8));
+#pragma unroll
+    for (int t = 0; t < C::DT; ++t) asm volatile("" : "+v"(xo[t]));
+    asm volatile("" : "+v"(xd), "+v"(vo), "+v"(ro8));
   };
 
   // ---- list of (query head, query tile) pairs this workgroup needs ---------
@@ -507,8 +515,8 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(BParams p) {
     // Pair m = DT*gg + t: rows +16gg, chunk group t.
     auto trd = [&](auto buf, int m) {
       const lds_char* b = to_lds(buf) + sub * 32 * C::ROW + (m / C::DT) * 16 * C::ROW;
-      const int xa = (64 * (m % C::DT)) ^ tA;
-      return lds_read_tr(b + (tP[0] + xa), b + (tP[1] + xa));
+      const int x0 = xo[m % C::DT];
+      return lds_read_tr(b + x0, b + (x0 + xd));
     };
     bf16x8 to[2], tq[2];
     to[0] = trd(obuf(bc), 0);
@@ -678,7 +686,8 @@ __global__ __launch_bounds__(512, 1) void dq_kernel(BParams p) {
   const int nY = 16 * (hi ^ swz_t<C::CHR>(nrow, 0));
   // Transposed reads of K (A of dQ^T += K^T dS^T): lane s16 of its 16-lane
   // group reads key 8hi + 4h + s16/4 (+16gg + 32sub) at column 32t +
-  // 16*(bit 4 of lane) + 4*(s16%4): byte tP[h] + ((64 t) ^ tA).
+  // 16*(bit 4 of lane) + 4*(s16%4): byte tP[h] + ((64 t) ^ tA), kept as
+  // xo[t] = tP[0] + ((64 t) ^ tA) and the distance xd = tP[1] - tP[0].
   int tP[2], tA;
   {
     const int cl = 2 * ((lane >> 4) & 1) + ((s16 & 3) >> 1);
@@ -703,10 +712,16 @@ __global__ __launch_bounds__(512, 1) void dq_kernel(BParams p) {
 #pragma unroll
   for (int kk = 0; kk < NYO; ++kk) yo[kk] = nrow * C::ROW + ((32 * kk) ^ nY);
   auto yoff = [&](int kk) { return kk < NYO ? yo[kk] : (yo[kk - NYO] ^ 128); };
+  int xo[C::DT];
+#pragma unroll
+  for (int t = 0; t < C::DT; ++t) xo[t] = tP[0] + ((64 * t) ^ tA);
+  int xd = tP[1] - tP[0];
   auto refresh = [&]() {
 #pragma unroll
     for (int kk = 0; kk < NYO; ++kk) asm volatile("" : "+v"(yo[kk]));
-    asm volatile("" : "+v"(tP[0]), "+v"(tP[1]), "+v"(tA));
+#pragma unroll
+    for (int t = 0; t < C::DT; ++t) asm volatile("" : "+v"(xo[t]));
+    asm volatile("" : "+v"(xd));
   };
 
   const char* kbase = p.k + ((long long)b * p.k_sb + (long long)kvh * p.k_sh) * 2;
@@ -806,9 +821,8 @@ __global__ __launch_bounds__(512, 1) void dq_kernel(BParams p) {
     for (int gg = 0; gg < 2; ++gg)
 #pragma unroll
       for (int t = 0; t < C::DT; ++t) {
-        const int xa = (64 * t) ^ tA;
         const lds_char* kg = kt + gg * 16 * C::ROW;
-        const bf16x8 a = lds_read_tr(kg + (tP[0] + xa), kg + (tP[1] + xa));
+        const bf16x8 a = lds_read_tr(kg + xo[t], kg + (xo[t] + xd));
         dqa[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, db[gg], dqa[t], 0, 0, 0);
       }
   };
