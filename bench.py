@@ -19,9 +19,14 @@ shard already resident in HBM (index maps are built once, in set-up):
       shard of the workload's queries ([S/cp, Hq, d]), for a2a group sizes
       --a2a-groups; ``value`` is their HBM rate in GB/s (bytes read + written).
 ``value`` is the algorithmic work of a step divided by the time of the timed
-steps, in TFLOP/s: 4*d*Hq flops per allowed (query, key) pair for the forward
-(Q K^T and P V) and 10*d*Hq for the backward (Q K^T, dO V^T, P^T dO, dS K and
-dS^T Q), with exact pair counts from the index builder.
+steps, in TFLOP/s, with exact pair counts from the index builder: 4*d*Hq flops
+per allowed (query, key) pair for the forward (Q K^T and P V) and 8*d*Hq for
+the backward (dO V^T, P^T dO, dS K and dS^T Q), twice the forward, as in the
+per-token cost of attention the Accelerate context-parallel guide quotes
+(12 H d per token for forward plus backward).  The rate that also counts the
+backward's recomputed Q K^T (10*d*Hq, 14*d*Hq for forward plus backward) is
+reported beside it, and so is the rate of the MFMA work the kernels execute.
+The clocks sampled during the timed steps give the peak at the measured sclk.
 
 Prints one JSON line.  ``--gpus N`` with N > 1 exits: this build runs on one
 GPU and every figure is that GPU's.
@@ -48,7 +53,13 @@ KERNEL_SOURCES = {
     "bwd": ["context_causal_attention_amd/csrc/attn_bwd.hip", "context_causal_attention_amd/csrc/device_common.h"],
     "a2a": ["context_causal_attention_amd/csrc/a2a.hip", "context_causal_attention_amd/csrc/device_common.h"],
 }
-FLOPS_PER_PAIR_HEAD_DIM = {"fwd": 4.0, "bwd": 10.0}
+FLOPS_PER_PAIR_HEAD_DIM = {"fwd": 4.0, "bwd": 8.0}
+# The backward with its recomputed Q K^T counted, and what the kernels execute:
+# the forward kernel 4*d; the dK/dV kernel S, dP, dV, dK (8*d) and the dQ
+# kernel S, dP, dQ (6*d).
+FLOPS_RECOMPUTE_COUNTED = {"fwd": 4.0, "bwd": 10.0}
+FLOPS_EXECUTED = {"fwd": 4.0, "bwd": 14.0}
+MFMA_FLOP_PER_CLK = 256 * 4096  # CUs x dense bf16 flop per CU per clock
 
 
 def source_hash(paths):
@@ -98,6 +109,67 @@ def parse():
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (the reference for HBM byte counters) and exit")
     return ap.parse_args()
+
+
+class ClockSampler:
+    """Samples the GPU's current sclk and mclk (MHz) from sysfs (the level the
+    power-play tables mark as current) every `period` seconds on a host thread
+    while the timed steps run.  Reports None where the files are missing."""
+
+    def __init__(self, period=0.05):
+        import glob
+        import threading
+        self.period = period
+        self.samples = {"sclk": [], "mclk": []}
+        self.files = {}
+        for kind in ("sclk", "mclk"):
+            for f in sorted(glob.glob(f"/sys/class/drm/card*/device/pp_dpm_{kind}")):
+                if self._read(f) is not None:
+                    self.files[kind] = f
+                    break
+        self._stop = threading.Event()
+        self._thread = threading.Thread(target=self._run, daemon=True)
+
+    @staticmethod
+    def _read(path):
+        import re
+        try:
+            with open(path) as fh:
+                for line in fh:
+                    if line.rstrip().endswith("*"):
+                        m = re.search(r"(\d+)\s*[Mm][Hh]z", line)
+                        return int(m.group(1)) if m else None
+        except OSError:
+            return None
+        return None
+
+    def _run(self):
+        while not self._stop.is_set():
+            for kind, f in self.files.items():
+                v = self._read(f)
+                if v is not None:
+                    self.samples[kind].append(v)
+            self._stop.wait(self.period)
+
+    def __enter__(self):
+        if self.files:
+            self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        if self._thread.is_alive():
+            self._thread.join()
+
+    def summary(self):
+        import numpy as np
+        out = {}
+        for kind, vals in self.samples.items():
+            out[kind + "_mhz"] = (None if not vals else
+                                  {"median": float(np.median(vals)), "min": min(vals), "max": max(vals)})
+        out["samples"] = len(self.samples["sclk"])
+        out["source"] = ", ".join(self.files.values()) or None
+        return out
 
 
 def calibrate_copy():
@@ -212,18 +284,25 @@ def main():
     ev = [{ps: {r: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for r in ranks}
            for ps in passes} for _ in range(args.steps)]
     torch.cuda.synchronize()
-    t_start = time.perf_counter()
-    for s in range(args.steps):
-        step(ev[s])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t_start
+    with ClockSampler() as clk:
+        t_start = time.perf_counter()
+        for s in range(args.steps):
+            step(ev[s])
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t_start
+    clocks = clk.summary()
 
-    launch_ms = {ps: {r: float(np.mean([ev[s][ps][r][0].elapsed_time(ev[s][ps][r][1]) for s in range(args.steps)]))
-                      for r in ranks} for ps in passes}
+    every_ms = {ps: {r: [ev[s][ps][r][0].elapsed_time(ev[s][ps][r][1]) for s in range(args.steps)] for r in ranks}
+                for ps in passes}
+    launch_ms = {ps: {r: float(np.mean(every_ms[ps][r])) for r in ranks} for ps in passes}
     step_flops = sum(sum(f.values()) for f in flops.values())
     ms_per_step = wall * 1e3 / args.steps
     value = step_flops / (wall / args.steps) / 1e12
+    recount = sum(FLOPS_RECOMPUTE_COUNTED[ps] / FLOPS_PER_PAIR_HEAD_DIM[ps] * sum(flops[ps].values()) for ps in passes)
+    value_recompute = recount / (wall / args.steps) / 1e12
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
+    sclk = clocks["sclk_mhz"]["median"] if clocks.get("sclk_mhz") else None
+    peak_at_sclk = MFMA_FLOP_PER_CLK * sclk * 1e6 / 1e12 if (sclk and w.dtype == "bf16") else None
     for ps in passes:
         print(f"[bench] {ps} per-rank ms: " + ", ".join(f"{r}:{launch_ms[ps][r]:.3f}" for r in ranks),
               file=sys.stderr, flush=True)
@@ -234,10 +313,18 @@ def main():
         ach = fl / (ms * 1e-3) / 1e12
         kern = {"fwd": "cp_attn_ring_fwd launch (prep_kernel: bounds and V^T; fwd_bf16_kernel)",
                 "bwd": "cp_attn_ring_bwd launch (key_prep_kernel, query_prep_kernel, dkdv_kernel, dq_kernel)"}[ps]
-        return {"bound": "mfma", "achieved": round(ach, 3), "peak": peak, "unit": "TFLOP/s",
-                "frac": round(ach / peak, 4), "traffic": stored_traffic(ps, w.name), "launch_ms": round(ms, 4),
-                "kernel": kern + "; achieved = algorithmic flops per launch / mean launch time from HIP events "
-                "on the launch stream; traffic = calibrated FETCH_SIZE + WRITE_SIZE bytes per launch"}
+        r = {"bound": "mfma", "achieved": round(ach, 3), "peak": peak, "unit": "TFLOP/s",
+             "frac": round(ach / peak, 4), "traffic": stored_traffic(ps, w.name), "launch_ms": round(ms, 4)}
+        if ps == "bwd":
+            r["achieved_recompute_counted"] = round(ach * FLOPS_RECOMPUTE_COUNTED[ps] / FLOPS_PER_PAIR_HEAD_DIM[ps], 3)
+        r["executed_mfma"] = round(ach * FLOPS_EXECUTED[ps] / FLOPS_PER_PAIR_HEAD_DIM[ps], 3)
+        if peak_at_sclk:
+            r["frac_at_measured_sclk"] = round(ach / peak_at_sclk, 4)
+        r["kernel"] = (kern + f"; achieved = algorithmic flops per launch ({FLOPS_PER_PAIR_HEAD_DIM[ps]:g}*d*Hq "
+                       "per allowed pair) / mean launch time from HIP events on the launch stream; executed_mfma "
+                       "counts the MFMA work the kernels run; traffic = calibrated FETCH_SIZE + WRITE_SIZE bytes "
+                       "per launch")
+        return r
 
     rooflines = {ps: roof(ps) for ps in passes}
     dominant = max(passes, key=lambda ps: rooflines[ps]["launch_ms"])
@@ -249,9 +336,17 @@ def main():
     per_pass = {}
     for ps in passes:
         tot_ms = sum(launch_ms[ps].values())
-        per_pass[ps] = {"TFLOP/s": round(sum(flops[ps].values()) / (tot_ms * 1e-3) / 1e12, 3),
-                        "pct_peak": round(100 * sum(flops[ps].values()) / (tot_ms * 1e-3) / 1e12 / peak, 2),
-                        "per_rank_ms": {str(r): round(x, 4) for r, x in launch_ms[ps].items()}}
+        rate = sum(flops[ps].values()) / (tot_ms * 1e-3) / 1e12
+        every = [x for r in ranks for x in every_ms[ps][r]]
+        per_pass[ps] = {"TFLOP/s": round(rate, 3), "pct_peak": round(100 * rate / peak, 2)}
+        if ps == "bwd":
+            per_pass[ps]["TFLOP/s_recompute_counted"] = round(
+                rate * FLOPS_RECOMPUTE_COUNTED[ps] / FLOPS_PER_PAIR_HEAD_DIM[ps], 3)
+        if peak_at_sclk:
+            per_pass[ps]["pct_peak_at_measured_sclk"] = round(100 * rate / peak_at_sclk, 2)
+        per_pass[ps]["launch_ms"] = {"median": round(float(np.median(every)), 4), "min": round(min(every), 4),
+                                     "max": round(max(every), 4), "launches": len(every)}
+        per_pass[ps]["per_rank_ms"] = {str(r): round(x, 4) for r, x in launch_ms[ps].items()}
     out = {
         "metric": METRIC,
         "value": round(value, 3),
@@ -272,6 +367,11 @@ def main():
                             if bwd else "ring forward of each listed virtual rank") +
                            ", ranks sequential, K/V resident"},
         "pct_peak": round(100 * value / peak, 2),
+        **({"value_recompute_counted": round(value_recompute, 3),
+            "flops_per_pair_head_dim": "fwd 4*d, bwd 8*d (value); bwd 10*d (value_recompute_counted)"}
+           if bwd else {}),
+        **({"pct_peak_at_measured_sclk": round(100 * value / peak_at_sclk, 2)} if peak_at_sclk else {}),
+        "clocks": clocks,
         "passes": per_pass,
         "roofline": rooflines[dominant],
         "roofline_by_pass": rooflines,
@@ -322,6 +422,18 @@ def a2a_bench(args, w):
             res[f"g{g}_{name}"] = {"ms": round(ms, 5), "GB/s": round(2 * nbytes / (ms * 1e-3) / 1e9, 1)}
             print(f"[bench] a2a g={g} {name}: {ms * 1e3:.1f} us, {2 * nbytes / (ms * 1e-3) / 1e9:.0f} GB/s",
                   file=sys.stderr, flush=True)
+    # Context: a plain device copy (torch's copy kernel) of the same bytes.
+    dst = torch.empty_like(x)
+    for _ in range(args.warmup):
+        dst.copy_(x)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for a, b in ev:
+        a.record(stream)
+        dst.copy_(x)
+        b.record(stream)
+    torch.cuda.synchronize()
+    copy_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
     rates = [v["GB/s"] for v in res.values()]
     value = float(np.mean(rates))
     dominant = min(res, key=lambda k: res[k]["GB/s"])
@@ -342,6 +454,7 @@ def a2a_bench(args, w):
         "config": {"workload": w.name, "pass": "a2a", "rows": rows, "heads": w.Hq, "d": w.d, "groups": groups,
                    "step": "one call on one rank's query shard [S/cp, Hq, d]"},
         "a2a": res,
+        "plain_copy_same_bytes": {"ms": round(copy_ms, 5), "GB/s": round(2 * nbytes / (copy_ms * 1e-3) / 1e9, 1)},
         "roofline": {"bound": "hbm", "achieved": round(2 * nbytes / (ms_dom * 1e-3) / 1e9, 1),
                      "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(2 * nbytes / (ms_dom * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
@@ -494,8 +607,9 @@ def cpu_baseline(w, full, idx_r, allp, cu, target_s, rank_id, bwd):
     one query head at a time until ~target_s have passed: the forward
     (attention_fwd) over all of one virtual rank's rows, or for --pass fwdbwd
     the backward (attention_bwd, which runs its own forward) over every 16th
-    of those rows; flops counted like the GPU's, from the exact pair count of
-    the rows sampled."""
+    of those rows; flops counted like the GPU's value (4*d per pair for the
+    forward, 8*d more for the backward), from the exact pair count of the rows
+    sampled."""
     import numpy as np
     import oracle as orc
     import context_causal_attention_amd as cpa
@@ -511,7 +625,7 @@ def cpu_baseline(w, full, idx_r, allp, cu, target_s, rank_id, bwd):
     stride = 16 if bwd else 1
     rows = pos[::stride]
     pairs = cpa.cp_pairs(rows, None if lo is None else lo[::stride], allp)
-    per_pair = 14.0 if bwd else 4.0
+    per_pair = FLOPS_PER_PAIR_HEAD_DIM["fwd"] + (FLOPS_PER_PAIR_HEAD_DIM["bwd"] if bwd else 0.0)
     t0 = time.perf_counter()
     done = 0
     while done < w.Hq:
