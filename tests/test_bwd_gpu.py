@@ -43,6 +43,18 @@ def test_delta_matches_oracle(o_dtype, d):
     assert max_err(delta, ref) <= 1e-4
 
 
+def test_delta_many_batch_heads():
+    # 70 000 (batch, head) pairs of 5 rows each: more than 65 535 pairs, and
+    # rows that split across workgroups.
+    announce("delta B=2 H=35000 S=5 d=64")
+    g = torch.Generator().manual_seed(4)
+    dout = torch.randn(2, 35000, 5, 64, generator=g).to(torch.bfloat16)
+    o = torch.randn(2, 35000, 5, 64, generator=g)
+    delta = cpa.cp_attn_bwd_delta(dout.cuda(), o.cuda())
+    ref = orc.bwd_delta(_np(dout), _np(o))
+    assert max_err(delta, ref) <= 1e-4
+
+
 @pytest.mark.parametrize("B,Hq,Hkv,S,d,cp", [
     (1, 2, 1, 1024, 64, 2),     # the C0 shape, bf16
     (1, 4, 2, 768, 128, 3),     # 256 rows a rank: 4 full 64-row tiles
