@@ -114,7 +114,7 @@ int cp_unshard_zigzag(int64_t S, int32_t cp, int32_t* perm_out);
  * that fits whole in some rank's remaining room goes whole to the fitting rank
  * with the least causal work so far (ties: lower rank); one that fits nowhere
  * is cut into consecutive pieces from its start, each filling the rank with the
- * most room left (ties: lower rank).  Rows of rows [a, b) of a document that
+ * most room left (ties: lower rank).  The rows [a, b) of a document that
  * starts at s count sum over p in [a, b) of (p - s + 1) causal pairs.  At most
  * cp - 1 documents are cut.  A rank's positions come out in ascending order. */
 int cp_varlen_index(const int32_t* cu_seqlens, int32_t n_docs, int32_t cp, int32_t rank,
