@@ -336,6 +336,10 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(KParams p) {
       auto kop = [&](int m) {
         return *reinterpret_cast<const bf16x8*>(sK + kaddr[m >> 1] + (m & 1) * 32 * C::KROW);
       };
+      // Issue priority 1 for this block, 0 again from the P V MFMAs on: while
+      // one wave interleaves scores and exponentials, the SIMD's other wave
+      // fills the gaps (1-2% faster than equal priority throughout).
+      __builtin_amdgcn_s_setprio(1);
       constexpr int NM = 2 * C::QREG;  // MFMAs per tile
       constexpr int PF = 4;            // operand reads in flight
       bf16x8 ops[NM];
@@ -389,6 +393,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(KParams p) {
       for (int kg = 0; kg < 4; ++kg) expg(c0, c1, kg, nm2, pb[kg], lj);
     }
     l_run += lj;
+    __builtin_amdgcn_s_setprio(0);
     // O^T += V^T P^T
     bf16x8 va[C::DT];
 #pragma unroll
