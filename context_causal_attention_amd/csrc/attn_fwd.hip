@@ -9,10 +9,11 @@
 // recurrence so no score matrix is ever stored.
 //
 // Work decomposition
-//   A workgroup of 8 wave64s (one per CU: two per SIMD) owns 256 query rows of
-//   one query head (32 rows a wave) and walks the ring's key tiles in step
-//   order; each K and V^T tile copied into LDS serves all 8 waves.  Key tiles never cross
-//   a rank's shard.  Before the walk the workgroup lists the tiles it needs,
+//   A bf16 workgroup of NW wave64s owns NW * 32 query rows of one query head
+//   (32 rows a wave) and walks the ring's key tiles in step order; each K and
+//   V^T tile copied into LDS serves all its waves.  Two waves share each SIMD:
+//   NW = 8 is one workgroup per CU, NW = 4 two (chosen per launch by the
+//   expected keys per row).  Key tiles never cross a rank's shard.  Before the walk the workgroup lists the tiles it needs,
 //   each tagged, per wave, as skipped, "full" (no mask needed) or "partial"
 //   (per-element mask q_lo <= k_pos <= q_pos), from the position bounds of the
 //   tile and of the wave's rows.
@@ -50,10 +51,11 @@ namespace fwdk {
 
 using namespace dev;
 
-constexpr int kWaves = 8;
-constexpr int kThreads = kWaves * 64;
 constexpr int kRowsPerWave = 32;
-constexpr int kBlockM = kWaves * kRowsPerWave;
+// The fp32 kernel: 8 waves, one workgroup per CU.
+constexpr int kF32Waves = 8;
+constexpr int kF32Threads = kF32Waves * 64;
+constexpr int kF32BlockM = kF32Waves * kRowsPerWave;
 constexpr int kListCap = 1024;          // active key tiles listed per pass
 constexpr float kRescaleLog2 = 8.0f;    // keep a stale running max while scores stay within 2^8 of it
 
@@ -125,7 +127,7 @@ __device__ __forceinline__ void store_out(const KParams& p, const Item& it, int 
 // ============================================================================
 // bf16 kernel
 // ============================================================================
-template <int D>
+template <int D, int NW>
 struct Bf16Cfg {
   static constexpr int BN = kTileKeysBf16;       // keys per tile
   static constexpr int KROW = D * 2;             // bytes per K row in LDS
@@ -134,19 +136,21 @@ struct Bf16Cfg {
   static constexpr int VCHR = BN / 8;            // 8
   static constexpr int KBYTES = BN * KROW;
   static constexpr int VBYTES = D * VROW;
-  static constexpr int KPW = KBYTES / 1024 / kWaves;  // 1 KB DMA blocks per wave
-  static constexpr int VPW = VBYTES / 1024 / kWaves;
+  static constexpr int KPW = KBYTES / 1024 / NW;  // 1 KB DMA blocks per wave
+  static constexpr int VPW = VBYTES / 1024 / NW;
   static constexpr int QREG = D / 16;
   static constexpr int DT = D / 32;
   static_assert(KPW >= 1 && VPW >= 1, "tile too small for the DMA split");
 };
 
-template <int D>
-__global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(KParams p) {
+// NW waves of 32 query rows each; two waves share each SIMD (NW = 8: one
+// workgroup per CU; NW = 4: two).
+template <int D, int NW>
+__global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(KParams p) {
   // The body uses device-only buffer-descriptor types; the host pass only needs
   // the launch stub.
 #if defined(__HIP_DEVICE_COMPILE__)
-  using C = Bf16Cfg<D>;
+  using C = Bf16Cfg<D, NW>;
   __shared__ __attribute__((aligned(1024))) char sK0[C::KBYTES];
   __shared__ __attribute__((aligned(1024))) char sK1[C::KBYTES];
   __shared__ __attribute__((aligned(1024))) char sV0[C::VBYTES];
@@ -154,8 +158,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(KParams p) {
   __shared__ __attribute__((aligned(16))) int sP0[C::BN];
   __shared__ __attribute__((aligned(16))) int sP1[C::BN];
   __shared__ int2 sList[kListCap];
-  __shared__ int sCnt[kWaves];
-  __shared__ int sWb[kWaves][6];
+  __shared__ int sCnt[NW];
+  __shared__ int sWb[NW][6];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps tile-class branches scalar
@@ -163,7 +167,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(KParams p) {
   const int l32 = lane & 31;
   const int hi = lane >> 5;
   const Item it = map_block(p);
-  const int row = it.qt * kBlockM + wave * kRowsPerWave + l32;
+  const int row = it.qt * (NW * kRowsPerWave) + wave * kRowsPerWave + l32;
   const bool valid = row < p.sq;
 
   // ---- query operand (B of S^T = K Q^T) in registers ----------------------
@@ -187,14 +191,14 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(KParams p) {
   int voffK[C::KPW], voffV[C::VPW];
 #pragma unroll
   for (int j = 0; j < C::KPW; ++j) {
-    const int c = (wave + kWaves * j) * 64 + lane;  // physical chunk index within the K tile
+    const int c = (wave + NW * j) * 64 + lane;  // physical chunk index within the K tile
     const int r = c / C::KCHR, ph = c % C::KCHR;
     voffK[j] = (int)(r * k_row_bytes) + 16 * swz<C::KCHR>(r, ph);
   }
   const long long vt_row_bytes = p.v_ss * 2;
 #pragma unroll
   for (int j = 0; j < C::VPW; ++j) {
-    const int c = (wave + kWaves * j) * 64 + lane;
+    const int c = (wave + NW * j) * 64 + lane;
     const int r = c / C::VCHR, ph = c % C::VCHR;
     voffV[j] = (int)(r * vt_row_bytes) + 16 * swz<C::VCHR>(r, ph);
   }
@@ -229,7 +233,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(KParams p) {
         (void*)(kbase + (long long)r0 * k_row_bytes), 0, (int)(nval * k_row_bytes), kBufferFlags);
 #pragma unroll
     for (int j = 0; j < C::KPW; ++j)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsK, (lds_ptr_t)(sK + (wave + kWaves * j) * 1024), 16, voffK[j], 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsK, (lds_ptr_t)(sK + (wave + NW * j) * 1024), 16, voffK[j], 0, 0, 0);
   };
   // Copies V^T and the key positions of list entry e into LDS buffer `buf`.
   auto issue_v = [&](auto bufc, int e) {
@@ -239,7 +243,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(KParams p) {
     const int tile = tile_of(e);
 #pragma unroll
     for (int j = 0; j < C::VPW; ++j)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsV, (lds_ptr_t)(sV + (wave + kWaves * j) * 1024), 16, voffV[j],
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsV, (lds_ptr_t)(sV + (wave + NW * j) * 1024), 16, voffV[j],
                                                tile * C::BN * 2, 0, 0);
     if (wave == 0)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rsP, (lds_ptr_t)sP, 4, lane * 4, tile * C::BN * 4, 0, 0);
@@ -417,7 +421,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(KParams p) {
   const int csh = 2 * wave;
   auto cls_of = [&](int2 e) { return (int)(((unsigned)e.y >> csh) & 3); };
   for (int u0 = 0; u0 < total; u0 += kListCap) {
-    const int cnt = build_key_list<C::BN, kWaves>(p.bounds, p.tpr, p.R, p.rank, p.cp, u0, min(total, u0 + kListCap), tid,
+    const int cnt = build_key_list<C::BN, NW>(p.bounds, p.tpr, p.R, p.rank, p.cp, u0, min(total, u0 + kListCap), tid,
                                                   wave, lane, sWb, sList, sCnt);
     if (cnt == 0) continue;
     // Entry of list slot j (x: tile, y: classes), read as scalars.
@@ -478,21 +482,21 @@ struct F32Cfg {
   static constexpr int BN = kTileKeysF32;        // 32 keys per tile
   static constexpr int KCHR = D / 4;             // 16-byte chunks per row
   static constexpr int CHUNKS = BN * KCHR;       // per tile, for K and for V
-  static constexpr int LD = CHUNKS / kThreads;   // staged chunks per thread
+  static constexpr int LD = CHUNKS / kF32Threads;   // staged chunks per thread
   static constexpr int QREG = D / 2;
   static constexpr int DT = D / 32;
-  static_assert(CHUNKS % kThreads == 0, "tile not divisible");
+  static_assert(CHUNKS % kF32Threads == 0, "tile not divisible");
 };
 
 template <int D>
-__global__ __launch_bounds__(kThreads, 1) void fwd_f32_kernel(KParams p) {
+__global__ __launch_bounds__(kF32Threads, 1) void fwd_f32_kernel(KParams p) {
   using C = F32Cfg<D>;
   __shared__ __attribute__((aligned(16))) u32x4 sK[2][C::CHUNKS];
   __shared__ __attribute__((aligned(16))) u32x4 sV[2][C::CHUNKS];
   __shared__ __attribute__((aligned(16))) int sKpos[2][C::BN];
   __shared__ int2 sList[kListCap];
-  __shared__ int sCnt[kWaves];
-  __shared__ int sWb[kWaves][6];
+  __shared__ int sCnt[kF32Waves];
+  __shared__ int sWb[kF32Waves][6];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -500,7 +504,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_f32_kernel(KParams p) {
   const int l32 = lane & 31;
   const int hi = lane >> 5;
   const Item it = map_block(p);
-  const int row = it.qt * kBlockM + wave * kRowsPerWave + l32;
+  const int row = it.qt * kF32BlockM + wave * kRowsPerWave + l32;
   const bool valid = row < p.sq;
 
   // Lane half hi holds d indices hi*D/2 .. hi*D/2 + D/2 - 1 of its row.
@@ -540,7 +544,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_f32_kernel(KParams p) {
     const int nval = min(C::BN, p.R - i * C::BN);
 #pragma unroll
     for (int j = 0; j < C::LD; ++j) {
-      const int c = tid + j * kThreads;
+      const int c = tid + j * kF32Threads;
       const int r = c / C::KCHR, ch = c % C::KCHR;
       kst[j] = r < nval ? *reinterpret_cast<const u32x4*>(p.k + ((kbase + (long long)(r0 + r) * p.k_ss) * 4 + ch * 16))
                         : u32x4{0, 0, 0, 0};
@@ -552,7 +556,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_f32_kernel(KParams p) {
   auto stage_store = [&](int buf) {
 #pragma unroll
     for (int j = 0; j < C::LD; ++j) {
-      const int c = tid + j * kThreads;
+      const int c = tid + j * kF32Threads;
       const int r = c / C::KCHR, ch = c % C::KCHR;
       sK[buf][r * C::KCHR + swz<C::KCHR>(r, ch)] = kst[j];
       sV[buf][c] = vst[j];
@@ -619,7 +623,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_f32_kernel(KParams p) {
   const int csh = 2 * wave;
   auto entry_tile = [&](int2 e) { return (e.x & 0xFF) * p.tpr + ((e.x >> 8) & 0xFFFF); };
   for (int u0 = 0; u0 < total; u0 += kListCap) {
-    const int cnt = build_key_list<C::BN, kWaves>(p.bounds, p.tpr, p.R, p.rank, p.cp, u0, min(total, u0 + kListCap), tid,
+    const int cnt = build_key_list<C::BN, kF32Waves>(p.bounds, p.tpr, p.R, p.rank, p.cp, u0, min(total, u0 + kListCap), tid,
                                                   wave, lane, sWb, sList, sCnt);
     if (cnt == 0) continue;
     stage_load(entry_tile(sList[0]));
@@ -744,14 +748,28 @@ hipError_t launch_t(const FwdArgs& a, hipStream_t stream) {
   p.rank = a.rank;
   p.R = a.rows_per_rank;
   p.tpr = a.tiles_per_rank;
-  p.n_qtiles = (a.sq + kBlockM - 1) / kBlockM;
   p.out_bf16 = a.out_dtype == CP_BF16;
   p.c2 = a.scale_log2;
-  const long long nblk = (long long)p.n_qtiles * a.hq * a.b;
-  if constexpr (BF16)
-    hipLaunchKernelGGL((fwd_bf16_kernel<D>), dim3((unsigned)nblk), dim3(kThreads), 0, stream, p);
-  else
-    hipLaunchKernelGGL((fwd_f32_kernel<D>), dim3((unsigned)nblk), dim3(kThreads), 0, stream, p);
+  if constexpr (BF16) {
+    // Wave count of the bf16 kernel (results are the same bits either way):
+    // 8 waves share each K/V tile copy, the better choice when every row sees
+    // many keys (dense causal rings of >= 65536 keys, 1% faster at 131072);
+    // two 4-wave workgroups per CU keep their barriers apart, better for
+    // shorter rings (1.5% at 32768 keys) and for document masks, whose rows
+    // see few keys (4-10%).
+    const bool wide = a.q_lo == nullptr && a.sk >= 65536;
+    const int nw = wide ? 8 : 4;
+    p.n_qtiles = (a.sq + nw * kRowsPerWave - 1) / (nw * kRowsPerWave);
+    const long long nblk = (long long)p.n_qtiles * a.hq * a.b;
+    if (wide)
+      hipLaunchKernelGGL((fwd_bf16_kernel<D, 8>), dim3((unsigned)nblk), dim3(8 * 64), 0, stream, p);
+    else
+      hipLaunchKernelGGL((fwd_bf16_kernel<D, 4>), dim3((unsigned)nblk), dim3(4 * 64), 0, stream, p);
+  } else {
+    p.n_qtiles = (a.sq + kF32BlockM - 1) / kF32BlockM;
+    const long long nblk = (long long)p.n_qtiles * a.hq * a.b;
+    hipLaunchKernelGGL((fwd_f32_kernel<D>), dim3((unsigned)nblk), dim3(kF32Threads), 0, stream, p);
+  }
   return hipGetLastError();
 }
 
