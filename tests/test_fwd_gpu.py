@@ -174,6 +174,27 @@ def test_llama8b_s128k_cp8_all_ranks_sampled():
         torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_long_dense_ring_sampled(d):
+    """A dense ring of 65536 keys, which the forward launches with 8-wave
+    workgroups (shorter rings and document masks use 4), at both head
+    dimensions: sampled rows of the first and last rank against the oracle."""
+    S, cp, Hq, Hkv = 65536, 4, 4, 1
+    full = si.make_qkv(1, Hq, Hkv, S, d, "bf16", seed=5)
+    q64, k64, v64 = (t.double().numpy() for t in full)
+    rng = np.random.default_rng(2)
+    n = S // cp
+    for rank in (0, cp - 1):
+        announce(f"dense ring S={S} d={d} rank {rank}")
+        R = Rank(1, Hq, Hkv, S, d, cp, rank, "bf16", full=full)
+        o, lse = R.ring_fwd()
+        idx = np.unique(np.concatenate([[0, n // 2 - 1, n // 2, n - 1], rng.integers(0, n, 12)]))
+        O_ref, L_ref = orc.attention_fwd(q64, k64, v64, R.scale, rows=R.pos[idx])
+        assert_close(o[:, :, idx], lse[:, :, idx], O_ref, L_ref, "bf16", f"rank {rank}")
+        del R, o, lse
+        torch.cuda.empty_cache()
+
+
 def test_local_only_schedule_fails_parity():
     """Attending only the local shard (the silent no-communication pitfall) is
     rejected by the same tolerance."""
