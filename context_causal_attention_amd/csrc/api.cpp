@@ -184,6 +184,9 @@ int prep_fwd(const cp_shape* s, int32_t cp, int32_t rank, const void* q, const v
   if ((s->sk / cp + tile_keys(s->in_dtype) - 1) / tile_keys(s->in_dtype) > 65535)
     return fail(CP_EINVAL, "a shard of %lld key rows has more than 65535 key tiles", (long long)(s->sk / cp));
   const FwdWorkspace w = fwd_workspace_layout(s->b, s->hkv, s->d, s->sk, cp, s->in_dtype);
+  // So does its V^T copy: d rows over every key slot of the padded tiles.
+  if (s->in_dtype == CP_BF16 && (double)s->d * (double)w.vt_row * 2.0 >= 4294967040.0)
+    return fail(CP_EINVAL, "%lld key rows exceed the 4 GiB reach of one buffer descriptor for V^T", (long long)s->sk);
   if (!ws) return fail(CP_EWORKSPACE, "workspace is null (%zu bytes needed)", w.total);
   if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0) return fail(CP_EWORKSPACE, "workspace is not 256-byte aligned");
   if (ws_bytes < w.total) return fail(CP_EWORKSPACE, "workspace too small: %zu < %zu bytes", ws_bytes, w.total);
@@ -526,11 +529,12 @@ int run_bwd(const cp_shape* s, int32_t cp, int32_t rank, const void* q, const vo
     return fail(CP_EINVAL, "%lld query rows or %d query heads per kv head are too many for the backward",
                 (long long)s->sq, s->hq / s->hkv);
   const BwdWorkspace w = bwd_workspace_layout(s->b, s->hq, s->hkv, s->d, s->sq, s->sk, cp);
-  // The kernels address the padded per-row and per-key arrays, and one tile's
-  // rows of Q, dO, K or V, with 32-bit buffer offsets.
+  // The kernels address the padded per-row and per-key arrays, one tile's
+  // rows of Q, dO, K or V, and the dK/dV workgroup's 256 rows of V, with
+  // 32-bit buffer offsets.
   if ((double)w.kt_row * 4.0 >= 2147483648.0 || (double)s->b * s->hq * (double)w.sq_pad * 4.0 >= 2147483648.0 ||
       64.0 * (double)s->q_str[2] * 2.0 >= 2147483648.0 || 64.0 * (double)s->k_str[2] * 2.0 >= 2147483648.0 ||
-      64.0 * (double)s->v_str[2] * 2.0 >= 2147483648.0)
+      256.0 * (double)s->v_str[2] * 2.0 >= 2147483648.0)
     return fail(CP_EINVAL, "sequence too long for 32-bit buffer offsets (sq=%lld, sk=%lld)", (long long)s->sq,
                 (long long)s->sk);
   if (!ws) return fail(CP_EWORKSPACE, "workspace is null (%zu bytes needed)", w.total);

@@ -39,6 +39,15 @@
  *   - Query head h reads key/value head h / (hq / hkv) (grouped-query heads).
  *   - cp == 1 is valid and means one rank holding the whole sequence: plain
  *     causal attention (the Accelerate plugin treats a CP size of 1 as off).
+ *   - Size limits (CP_EINVAL beyond them): sq, sk < 2^30; cp <= 255; a rank's
+ *     shard of at most 65535 key tiles (64 keys for bf16, 32 for fp32).  The
+ *     kernels address device memory through 32-bit buffer offsets, so for bf16
+ *     inputs the forward needs one (batch, kv head) of K (rows x row stride x
+ *     2 bytes) and its transposed V copy (d x padded keys x 2 bytes) under
+ *     4 GiB.  The backward needs 64 rows of q, dO and k, and 256 rows of v,
+ *     each under 2 GiB.  Its per-row and per-key tables must also stay under
+ *     2 GiB, with at most 65535 query tiles of 64 rows and 32767 query heads per
+ *     kv head.
  */
 #ifndef CPATTN_H
 #define CPATTN_H

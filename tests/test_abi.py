@@ -244,6 +244,20 @@ def test_ring_fwd_rejects_bad_args():
     assert _ring(s, ws_bytes=need - 1) == cpa.CP_EWORKSPACE
 
 
+def test_ring_fwd_rejects_keys_beyond_one_buffer_descriptor():
+    # 16777200 keys of d = 128 (row stride d, cp = 8): K takes 4294963200
+    # bytes, inside one buffer descriptor's reach, but the V^T copy over the
+    # padded tiles (8 x 32768 tiles of 64 keys) takes 2^32 bytes.
+    s = _shape(sk=16777200, hkv=1, hq=1)
+    assert _ring(s, cp=8) == cpa.CP_EINVAL
+    assert "V^T" in cpa.cp_last_error()
+    # A row stride that stretches 2^22 keys of K beyond 4 GiB.
+    s = _shape(sk=1 << 22, hkv=1, hq=1)
+    s.k_str[2] = 1024
+    assert _ring(s, cp=8) == cpa.CP_EINVAL
+    assert "4 GiB" in cpa.cp_last_error()
+
+
 def _stepwise(s, cp=2, rank=0, ws=FAKE, ws_bytes=1 << 40, stage=None, stage_bytes=0, o=FAKE):
     return cpa.lib().cp_attn_ring_fwd_stepwise(ctypes.byref(s), cp, rank, FAKE, FAKE, FAKE, FAKE, None, FAKE, o,
                                                FAKE, ws, ws_bytes, stage, stage_bytes, None, None)
@@ -371,6 +385,15 @@ def test_ring_bwd_rejects_bad_args():
     need = cpa.lib().cp_attn_bwd_workspace(ctypes.byref(s), 2)
     assert need > 0
     assert _ring_bwd(s, ws_bytes=need - 1) == cpa.CP_EWORKSPACE
+
+
+def test_ring_bwd_rejects_v_rows_beyond_32_bit_offsets():
+    # The dK/dV kernel reads 256 rows of V through one buffer descriptor:
+    # a V row stride of 2^22 elements puts them 2 GiB apart.
+    s = _shape()
+    s.v_str[2] = 1 << 22
+    assert _ring_bwd(s) == cpa.CP_EINVAL
+    assert "32-bit" in cpa.cp_last_error()
 
 
 def test_bwd_workspace_query():
