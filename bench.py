@@ -7,8 +7,9 @@ shard already resident in HBM (index maps are built once, in set-up):
       ring forward (final O, LSE), delta = rowsum(dO * O) and the ring backward
       (dQ of the rank's rows, dK/dV of every shard accumulated in place);
   --pass fwd: the ring forward of each rank only;
-  --pass rotate: the ring forward of each rank as separate steps (partial
-      forward + merge per step, cp_attn_ring_fwd_stepwise), four ways: the
+  --pass rotate: the ring forward of each rank as separate steps (a partial
+      forward per step, merged into the running output in its epilogue,
+      cp_attn_ring_fwd_stepwise), four ways: the
       fused resident ring, steps reading the shards in place, steps whose
       shards are copied into a two-slot stage on a second stream (a rotation
       ring's receive, overlapped), and the same copies on the compute stream.
@@ -595,7 +596,7 @@ def rotate_bench(args, w):
         "roofline": {"bound": "mfma", "achieved": round(ach, 3), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(ach / peak, 4), "traffic": None,
                      "kernel": "cp_attn_ring_fwd_stepwise launch with staging (per step fwd_bf16_kernel over one "
-                               "shard + merge_kernel, copies on a second stream); achieved = algorithmic flops per "
+                               "shard, merging in its epilogue; copies on a second stream); achieved = algorithmic flops per "
                                "launch / mean launch time from HIP events on the launch stream"},
         "cpu_baseline": cpu,
     }

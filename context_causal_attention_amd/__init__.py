@@ -301,8 +301,8 @@ def cp_attn_ring_fwd(q_loc, k_all, v_all, cp, rank, q_pos, q_lo, k_pos_all, scal
 
 
 class RingFwdStepwisePlan:
-    """A validated cp_attn_ring_fwd_stepwise call: one partial forward and one
-    merge per ring step.  staged=True copies each step's K/V shard into a
+    """A validated cp_attn_ring_fwd_stepwise call: one partial forward per ring
+    step, each later step merging into (O, LSE) in its epilogue.  staged=True copies each step's K/V shard into a
     two-slot staging buffer on copy_stream (a torch.cuda.Stream, or None for a
     new one) first, overlapped with the previous step, as a rotation ring
     receives the shards; staged=False reads every shard in place.  O is fp32."""
@@ -342,8 +342,9 @@ class RingFwdStepwisePlan:
 
 def cp_attn_ring_fwd_stepwise(q_loc, k_all, v_all, cp, rank, q_pos, q_lo, k_pos_all, scale=None, staged=True,
                               copy_stream=None, out=None, lse=None, workspace=None, stage=None):
-    """A virtual rank's ring as separate steps (partial forward + merge per
-    step), optionally with rotating K/V copies: final fp32 (O, LSE)."""
+    """A virtual rank's ring as separate steps (a partial forward per step,
+    merged into the running (O, LSE) in the kernel's epilogue), optionally with
+    rotating K/V copies: final fp32 (O, LSE)."""
     return RingFwdStepwisePlan(q_loc, k_all, v_all, cp, rank, q_pos, q_lo, k_pos_all, scale, staged,
                                copy_stream, out, lse, workspace, stage).run()
 

@@ -260,7 +260,7 @@ namespace {
 // Workspace of the stepwise ring: the step's partial O and LSE, then the
 // tables of the step kernel (cp = 1 over one shard).
 struct StepwiseLayout {
-  size_t opart_off, lpart_off, kern_off, kern_bytes, total;
+  size_t kern_off, kern_bytes, total;
 };
 
 StepwiseLayout stepwise_layout(const cp_shape* s, int32_t cp) {
@@ -271,9 +271,6 @@ StepwiseLayout stepwise_layout(const cp_shape* s, int32_t cp) {
     off += align_up(bytes, 256);
     return at;
   };
-  const size_t rows = (size_t)s->b * s->hq * (size_t)s->sq;
-  w.opart_off = take(rows * s->d * 4);
-  w.lpart_off = take(rows * 4);
   w.kern_bytes = fwd_workspace_layout(s->b, s->hkv, s->d, s->sk / cp, 1, s->in_dtype).total;
   w.kern_off = take(w.kern_bytes);
   w.total = off;
@@ -359,8 +356,6 @@ extern "C" int cp_attn_ring_fwd_stepwise(const cp_shape* s, int32_t cp, int32_t 
       return fail(CP_EINVAL, "staging copies need k_all and v_all with contiguous rows and heads of sk rows");
   }
   char* wsb = static_cast<char*>(ws);
-  float* o_part = reinterpret_cast<float*>(wsb + w.opart_off);
-  float* l_part = reinterpret_cast<float*>(wsb + w.lpart_off);
   void* kws = wsb + w.kern_off;
   const size_t e = esize(s->in_dtype);
   char* st = static_cast<char*>(stage);
@@ -381,14 +376,14 @@ extern "C" int cp_attn_ring_fwd_stepwise(const cp_shape* s, int32_t cp, int32_t 
       const int64_t packed[3] = {(int64_t)s->hkv * R * s->d, R * s->d, s->d};
       for (int i = 0; i < 3; ++i) ss.k_str[i] = ss.v_str[i] = packed[i];
     }
-    float* ot = t == 0 ? o : o_part;
-    float* lt = t == 0 ? lse : l_part;
-    if (int rc = prep_fwd(&ss, 1, 0, q_loc, k, v, q_pos, q_lo, k_pos_all + (size_t)src * R, ot, CP_F32, lt, kws,
+    // Step 0 writes (o, lse); every later step merges its partial into them
+    // in the kernel's epilogue.
+    if (int rc = prep_fwd(&ss, 1, 0, q_loc, k, v, q_pos, q_lo, k_pos_all + (size_t)src * R, o, CP_F32, lse, kws,
                           w.kern_bytes, &steps[t]))
       return rc;
+    steps[t].merge_acc = t > 0 ? 1 : 0;
   }
 
-  const int64_t rows = (int64_t)s->b * s->hq * s->sq;
   const bool staged = stage != nullptr && cp > 1;
   CallEvents ev;
   std::vector<hipEvent_t> copied(cp, nullptr);
@@ -426,8 +421,6 @@ extern "C" int cp_attn_ring_fwd_stepwise(const cp_shape* s, int32_t cp, int32_t 
     if (int rc = hip_status(launch_fwd(steps[t], stream), "forward launch")) return rc;
     if (staged && t > 0)
       if (int rc = hip_status(hipEventRecord(slot_free[t & 1], stream), "event record")) return rc;
-    if (t > 0)
-      if (int rc = hip_status(launch_merge(rows, s->d, o, lse, o_part, l_part, stream), "merge launch")) return rc;
   }
   if (staged) {
     if (int rc = hip_status(hipEventRecord(joined, copy_stream), "event record")) return rc;

@@ -75,6 +75,7 @@ struct KParams {
   long long v_sb, v_sh, v_ss;  // fp32 V strides; for bf16 V^T: v_ss = row length, v_sh = d * v_ss
   long long o_sb, o_sh, o_ss;
   int B, Hq, Hkv, sq, sk, cp, rank, R, tpr, n_qtiles, out_bf16;
+  int merge_acc;            // 1: (o, lse) hold a partial result over other keys (fp32) to merge into
   float c2;                 // softmax scale * log2(e)
 };
 
@@ -105,9 +106,37 @@ __device__ __forceinline__ void store_out(const KParams& p, const Item& it, int 
                                           float l_tot, const f32x16* oacc) {
   const bool empty = !(l_tot > 0.f);
   const float inv = empty ? 0.f : 1.f / l_tot;
-  if (hi == 0)
-    p.lse[((long long)it.b * p.Hq + it.h) * p.sq + row] = empty ? -INFINITY : (m_run + log2f(l_tot)) * kLn2;
+  const long long li = ((long long)it.b * p.Hq + it.h) * p.sq + row;
+  const float lse_new = empty ? -INFINITY : (m_run + log2f(l_tot)) * kLn2;
   const long long obase = (long long)it.b * p.o_sb + (long long)it.h * p.o_sh + (long long)row * p.o_ss;
+  if (p.merge_acc) {
+    // combine() with the partial already in (o, lse), which covers other keys:
+    // L = M + ln(e^(l1 - M) + e^(l2 - M)), O = e^(l1 - L) O1 + e^(l2 - L) O2;
+    // (0, -inf) on either side is the identity.  Both lanes of the row read
+    // the old LSE in the same load, before either writes.
+    const float l1 = p.lse[li];
+    const float M = fmaxf(l1, lse_new);
+    float L = -INFINITY, w1 = 0.f, w2 = 0.f;
+    if (M != -INFINITY) {
+      L = M + logf(expf(l1 - M) + expf(lse_new - M));
+      w1 = expf(l1 - L);
+      w2 = expf(lse_new - L) * inv;
+    }
+    if (hi == 0) p.lse[li] = L;
+#pragma unroll
+    for (int t = 0; t < DT; ++t)
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        f32x4* dst = reinterpret_cast<f32x4*>(p.o + (obase + 32 * t + 8 * rg + 4 * hi) * 4);
+        const f32x4 old = *dst;
+        f32x4 val;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) val[e] = w1 * old[e] + w2 * oacc[t][4 * rg + e];
+        *dst = val;
+      }
+    return;
+  }
+  if (hi == 0) p.lse[li] = lse_new;
 #pragma unroll
   for (int t = 0; t < DT; ++t)
 #pragma unroll
@@ -749,6 +778,7 @@ hipError_t launch_t(const FwdArgs& a, hipStream_t stream) {
   p.R = a.rows_per_rank;
   p.tpr = a.tiles_per_rank;
   p.out_bf16 = a.out_dtype == CP_BF16;
+  p.merge_acc = a.merge_acc;
   p.c2 = a.scale_log2;
   if constexpr (BF16) {
     // Wave count of the bf16 kernel (results are the same bits either way):

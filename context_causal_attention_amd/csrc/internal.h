@@ -43,6 +43,7 @@ struct FwdArgs {
   int32_t in_dtype;
   int32_t out_dtype;       // dtype of o (CP_F32 for partial outputs)
   void* ws;                // workspace (layout: see fwd_workspace_layout)
+  int32_t merge_acc;       // 1: merge the result into (o, lse) instead of writing it
 };
 
 struct FwdWorkspace {

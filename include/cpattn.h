@@ -191,8 +191,10 @@ int cp_attn_ring_fwd(const cp_shape* s, int32_t cp, int32_t rank, const void* q_
  * to one K/V shard, then combine, once per shard; the rotation of the shards
  * is the "all-to-all" method of "How to choose the right rotation method?").
  * Step t = 0..cp-1 attends q_loc to the shard of rank (rank - t) mod cp with
- * the kernel of cp_attn_partial_fwd and merges the partial into (o, lse) with
- * the kernel of cp_attn_merge; step 0 writes (o, lse) directly.
+ * the kernel of cp_attn_partial_fwd.  Step 0 writes (o, lse); every later
+ * step combines its partial with them by the rule of cp_attn_merge, in the
+ * kernel's epilogue (each row is read, merged and written by the wave that
+ * owns it), so no partial is stored.
  *
  * stage == NULL: every step reads its shard where it lies in k_all / v_all.
  * stage != NULL: the shards of steps 1..cp-1 are first copied into stage, two
@@ -208,8 +210,8 @@ int cp_attn_ring_fwd(const cp_shape* s, int32_t cp, int32_t rank, const void* q_
  * Arguments as for cp_attn_ring_fwd, except: o (device fp32, contiguous
  * [b,hq,sq,d], o_str = {hq*sq*d, sq*d, d}) and s->out_dtype must be CP_F32
  * (the merge works on fp32; CP_EDTYPE otherwise).  ws (device) of at least
- * cp_attn_ring_fwd_stepwise_workspace(s, cp) bytes holds the per-step partial
- * (O, LSE) and the step kernel's tables; stage (device) of at least
+ * cp_attn_ring_fwd_stepwise_workspace(s, cp) bytes holds the step kernel's
+ * tables; stage (device) of at least
  * cp_attn_ring_stage_bytes(s, cp) bytes.  Both 256-byte aligned.  Both are
  * owned by the caller and must stay untouched until stream has passed the call.
  * CP_ESHAPE unless sk % (2cp) == 0. */
