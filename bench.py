@@ -13,8 +13,9 @@ shard already resident in HBM (index maps are built once, in set-up):
       fused resident ring, steps reading the shards in place, steps whose
       shards are copied into a two-slot stage on a second stream (a rotation
       ring's receive, overlapped), and the same copies on the compute stream.
-      ``value`` is the staged, overlapped rate; ``rotate`` gives all four and
-      the copies alone;
+      ``value`` is the staged, overlapped rate; ``rotate`` gives all four,
+      the copies alone, and one LSE merge (cp_attn_merge) of a rank-sized
+      fp32 partial alone with its HBM rate;
   --pass a2a: the head exchange layout calls of hierarchical CP's all-to-all
       level (cp_a2a_pack, cp_a2a_unpack and their inverses) on one rank's
       shard of the workload's queries ([S/cp, Hq, d]), for a2a group sizes
@@ -515,6 +516,16 @@ def rotate_bench(args, w):
     src_v = [v_all[:, :, s * R:(s + 1) * R] for s in range(w.cp)]
     slot = [torch.empty_like(src_k[0]) for _ in range(4)]
     stream = torch.cuda.current_stream(dev)
+    # The LSE merge alone (cp_attn_merge): one rank's fp32 partial (O, LSE)
+    # merged into an accumulator of the same size, as an unfused ring step
+    # would after its partial forward.
+    mrows = w.B * w.Hq * R
+    gm = torch.Generator(device="cpu")
+    gm.manual_seed(w.seed)
+    m_part = (torch.randn(mrows, w.d, generator=gm).to(dev), torch.randn(mrows, generator=gm).to(dev))
+    m_acc = (torch.randn(mrows, w.d, generator=gm).to(dev), torch.randn(mrows, generator=gm).to(dev))
+    merge_bytes = mrows * (3 * w.d * 4 + 3 * 4)
+    extra = ["copies", "merge"]
 
     def copies():
         copy_stream.wait_stream(stream)
@@ -526,11 +537,13 @@ def rotate_bench(args, w):
 
     def step(ev=None):
         for r in ranks:
-            for kd in kinds + ["copies"]:
+            for kd in kinds + extra:
                 if ev is not None:
                     ev[kd][r][0].record(stream)
                 if kd == "copies":
                     copies()
+                elif kd == "merge":
+                    cpa.cp_attn_merge(m_acc[0], m_acc[1], m_part[0], m_part[1])
                 else:
                     plans[r][kd].run()
                 if ev is not None:
@@ -540,14 +553,14 @@ def rotate_bench(args, w):
         step()
     torch.cuda.synchronize()
     evs = [{kd: {r: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for r in ranks}
-            for kd in kinds + ["copies"]} for _ in range(args.steps)]
+            for kd in kinds + extra} for _ in range(args.steps)]
     t0 = time.perf_counter()
     for s_ in range(args.steps):
         step(evs[s_])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms = {kd: {r: float(np.mean([evs[s_][kd][r][0].elapsed_time(evs[s_][kd][r][1]) for s_ in range(args.steps)]))
-               for r in ranks} for kd in kinds + ["copies"]}
+               for r in ranks} for kd in kinds + extra}
     fl = {r: FLOPS_PER_PAIR_HEAD_DIM["fwd"] * w.d * w.Hq * w.B * pairs[r] for r in ranks}
     tot = sum(fl.values())
 
@@ -559,7 +572,8 @@ def rotate_bench(args, w):
     inplace = sum(ms["steps_in_place"].values())
     shard_bytes = 2 * w.B * w.Hkv * R * w.d * (2 if w.dtype == "bf16" else 4)
     copy_ms = sum(ms["copies"].values()) / len(ranks)
-    for kd in kinds + ["copies"]:
+    merge_ms = sum(ms["merge"].values()) / len(ranks)
+    for kd in kinds + extra:
         print(f"[bench] {kd} per-rank ms: " + ", ".join(f"{r}:{ms[kd][r]:.3f}" for r in ranks),
               file=sys.stderr, flush=True)
     cpu = None
@@ -582,16 +596,18 @@ def rotate_bench(args, w):
         "config": {"workload": w.name, "pass": "rotate", "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "d": w.d, "S": w.S,
                    "cp": w.cp, "ranks": ranks,
                    "step": "per rank, one after another: the fused ring, the steps in place, the steps with "
-                           "staged copies on a second stream, the same in line, and the copies alone; "
-                           "value is the staged, overlapped rate"},
+                           "staged copies on a second stream, the same in line, the copies alone and one LSE "
+                           "merge of a rank-sized partial alone; value is the staged, overlapped rate"},
         "pct_peak": round(100 * rate("steps_staged") / peak, 2),
         "rotate": {
             "TFLOP/s": {kd: rate(kd) for kd in kinds},
-            "per_rank_ms": {kd: {str(r): round(x, 4) for r, x in ms[kd].items()} for kd in kinds + ["copies"]},
+            "per_rank_ms": {kd: {str(r): round(x, 4) for r, x in ms[kd].items()} for kd in kinds + extra},
             "copy_bytes_per_rank": shard_bytes * (w.cp - 1),
             "copies_alone_GB/s": round(shard_bytes * (w.cp - 1) / (copy_ms * 1e-3) / 1e9, 1),
             "staged_over_in_place": round(staged / inplace, 4),
             "exposed_copy_ms_per_rank": round((staged - inplace) / len(ranks), 4),
+            "merge_alone": {"rows": mrows, "bytes": merge_bytes, "ms": round(merge_ms, 5),
+                            "GB/s": round(merge_bytes / (merge_ms * 1e-3) / 1e9, 1), "peak_GB/s": PEAK_HBM_GBS},
         },
         "roofline": {"bound": "mfma", "achieved": round(ach, 3), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(ach / peak, 4), "traffic": None,
