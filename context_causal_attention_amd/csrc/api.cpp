@@ -28,10 +28,21 @@ int check_dtype(int32_t dt, const char* what) {
 int check_strides(const int64_t* st, int32_t dtype, const char* what) {
   for (int i = 0; i < 3; ++i) {
     if (st[i] < 0) return fail(CP_EINVAL, "%s stride %d is negative", what, i);
-    if ((st[i] * esize(dtype)) % 16 != 0)
+    // Element size 2 or 4 divides 16: a multiple of 16 bytes is a multiple
+    // of 16 / esize elements (tested without forming the byte count).
+    if (st[i] % (16 / (int64_t)esize(dtype)) != 0)
       return fail(CP_EINVAL, "%s stride %d (%lld elements) is not a multiple of 16 bytes", what, i,
                   (long long)st[i]);
   }
+  return CP_OK;
+}
+
+// The kernels form element offsets b*sb + h*sh + row*ss in 64-bit integers:
+// the largest one, plus a row, must stay below 2^62.
+int check_extent(int64_t nb, int64_t nh, int64_t rows, int32_t d, const int64_t* st, const char* what) {
+  const double ext = (double)(nb > 0 ? nb - 1 : 0) * (double)st[0] + (double)(nh > 0 ? nh - 1 : 0) * (double)st[1] +
+                     (double)(rows > 0 ? rows - 1 : 0) * (double)st[2] + (double)d;
+  if (ext >= 4.6e18) return fail(CP_EINVAL, "%s spans more than 2^62 elements with these strides", what);
   return CP_OK;
 }
 
@@ -45,6 +56,10 @@ int check_shape(const cp_shape* s) {
   if (s->sq < 0 || s->sk < 0 || s->sq > (INT32_MAX / 2) || s->sk > (INT32_MAX / 2))
     return fail(CP_EINVAL, "row counts sq=%lld sk=%lld outside [0, 2^30)", (long long)s->sq,
                 (long long)s->sk);
+  // Element counts of q and k/v (and the products the calls form from them)
+  // stay below 2^62.
+  if ((double)s->b * s->hq * (double)s->sq * s->d >= 4.6e18 || (double)s->b * s->hkv * (double)s->sk * s->d >= 4.6e18)
+    return fail(CP_EINVAL, "b x heads x rows x d beyond 2^62 elements");
   if (!std::isfinite(s->scale) || !(s->scale > 0.0f))
     return fail(CP_EINVAL, "scale must be finite and > 0 (got %g)", (double)s->scale);
   if (int rc = check_dtype(s->in_dtype, "in_dtype")) return rc;
@@ -52,6 +67,10 @@ int check_shape(const cp_shape* s) {
   if (int rc = check_strides(s->q_str, s->in_dtype, "q")) return rc;
   if (int rc = check_strides(s->k_str, s->in_dtype, "k")) return rc;
   if (int rc = check_strides(s->v_str, s->in_dtype, "v")) return rc;
+  if (int rc = check_extent(s->b, s->hq, s->sq, s->d, s->q_str, "q")) return rc;
+  if (int rc = check_extent(s->b, s->hkv, s->sk, s->d, s->k_str, "k")) return rc;
+  if (int rc = check_extent(s->b, s->hkv, s->sk, s->d, s->v_str, "v")) return rc;
+  if (int rc = check_extent(s->b, s->hq, s->sq, s->d, s->o_str, "o")) return rc;
   return CP_OK;
 }
 
@@ -248,6 +267,7 @@ extern "C" int cp_attn_merge(int64_t rows, int32_t d, float* o_acc, float* lse_a
                              const float* lse_p, hipStream_t stream) {
   clear_error();
   if (rows < 0) return fail(CP_EINVAL, "rows must be >= 0 (got %lld)", (long long)rows);
+  if (rows > (int64_t)1 << 31) return fail(CP_EINVAL, "rows %lld exceed 2^31", (long long)rows);
   if (d != 64 && d != 128) return fail(CP_EINVAL, "head dimension %d is not 64 or 128", d);
   if (int rc = check_ptrs16({{o_acc, "o_acc"}, {o_p, "o_p"}})) return rc;
   if (!lse_acc || !lse_p) return fail(CP_EINVAL, "lse pointer is null");
@@ -450,7 +470,10 @@ extern "C" int cp_a2a_pack(int32_t g, int32_t heads, int64_t rows, int32_t d, in
   if (x_row_stride < (int64_t)heads * d)
     return fail(CP_EINVAL, "x row stride %lld is smaller than heads*d = %lld", (long long)x_row_stride,
                 (long long)heads * d);
-  if ((x_row_stride * esize(dtype)) % 16 != 0) return fail(CP_EINVAL, "x row stride is not a multiple of 16 bytes");
+  if (x_row_stride % (16 / (int64_t)esize(dtype)) != 0)
+    return fail(CP_EINVAL, "x row stride is not a multiple of 16 bytes");
+  if ((double)rows * (double)x_row_stride * esize(dtype) >= 4.6e18)
+    return fail(CP_EINVAL, "x spans more than 2^62 bytes with this row stride");
   if (rows == 0) return CP_OK;
   if (int rc = check_ptrs16({{x, "x"}, {send, "send"}})) return rc;
   return hip_status(inverse ? launch_a2a(g, heads, rows, d, dtype, send, x, x_row_stride, 0, 0, stream)

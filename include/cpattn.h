@@ -40,7 +40,9 @@
  *   - cp == 1 is valid and means one rank holding the whole sequence: plain
  *     causal attention (the Accelerate plugin treats a CP size of 1 as off).
  *   - Size limits (CP_EINVAL beyond them): sq, sk < 2^30; cp <= 255; a rank's
- *     shard of at most 65535 key tiles (64 keys for bf16, 32 for fp32).  The
+ *     shard of at most 65535 key tiles (64 keys for bf16, 32 for fp32);
+ *     b x heads x rows x d below 2^62 for q and for k/v, and every tensor's
+ *     largest element offset under its strides below 2^62.  The
  *     kernels address device memory through 32-bit buffer offsets, so for bf16
  *     inputs the forward needs one (batch, kv head) of K (rows x row stride x
  *     2 bytes) and its transposed V copy (d x padded keys x 2 bytes) under
@@ -164,7 +166,7 @@ int cp_attn_partial_fwd(const cp_shape* s, const void* q, const void* k, const v
  * L = max(l1,l2) + ln(e^(l1-max) + e^(l2-max)) and O = e^(l1-L) o1 + e^(l2-L) o2.
  * (0, -inf) is the identity; two empty rows stay (0, -inf).  The operation is
  * symmetric in its operands bit for bit.  Contiguous device fp32 arrays:
- * o_* [rows, d], lse_* [rows]; d is 64 or 128.  The pages name combine() but
+ * o_* [rows, d], lse_* [rows], 0 <= rows <= 2^31; d is 64 or 128.  The pages name combine() but
  * print no formula; this is the exact recombination of softmax over disjoint
  * key sets. */
 int cp_attn_merge(int64_t rows, int32_t d, float* o_acc, float* lse_acc,
@@ -242,10 +244,11 @@ int cp_attn_ring_fwd_stepwise(const cp_shape* s, int32_t cp, int32_t rank, const
  *   rank i -> y (device) [heads/g][g*rows][d] contiguous: this rank's heads
  *   over the group's rows in source-rank order, the [heads, rows, d] layout
  *   (one batch) the attention calls read.  inverse != 0 copies y back into recv.
- * heads is the total head count H.  g >= 1 divides heads; heads <= 65535; d is
- * 64 or 128; dtype CP_BF16 or CP_F32; pointers 16-byte aligned; source and
- * destination must not overlap.  Every value is copied exactly.  rows == 0 is
- * a no-op. */
+ * heads is the total head count H.  g >= 1 divides heads; heads <= 65535;
+ * 0 <= rows <= 2^31, with rows x x_row_stride x element size below 2^62
+ * bytes; d is 64 or 128; dtype CP_BF16 or CP_F32; pointers 16-byte aligned;
+ * source and destination must not overlap.  Every value is copied exactly.
+ * rows == 0 is a no-op. */
 int cp_a2a_pack(int32_t g, int32_t heads, int64_t rows, int32_t d, int32_t dtype, void* x,
                 int64_t x_row_stride, void* send, int32_t inverse, hipStream_t stream);
 int cp_a2a_unpack(int32_t g, int32_t heads, int64_t rows, int32_t d, int32_t dtype, void* recv,
