@@ -633,9 +633,13 @@ def cpu_baseline(w, full, idx_r, allp, cu, target_s, rank_id, bwd):
 
     pos, lo = idx_r
     q, k, v = full[:3]
+    blas = None
     try:
         from threadpoolctl import threadpool_info
-        cores = max(int(i.get("num_threads", 1)) for i in threadpool_info() if i.get("user_api") == "blas")
+        np.dot(np.ones((2, 2)), np.ones((2, 2)))  # loads the BLAS library so that it is listed
+        infos = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        cores = max(int(i.get("num_threads", 1)) for i in infos)
+        blas = ", ".join(f"{i.get('internal_api')} {i.get('version')}" for i in infos)
     except Exception:
         cores = len(os.sched_getaffinity(0))
     g = w.Hq // w.Hkv
@@ -661,7 +665,7 @@ def cpu_baseline(w, full, idx_r, allp, cu, target_s, rank_id, bwd):
     el = time.perf_counter() - t0
     fl = per_pair * w.d * done * pairs
     what = (f"forward+backward (attention_bwd) of every {stride}th row" if bwd else "forward of the rows")
-    return {"value": round(fl / el / 1e12, 5), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+    return {"value": round(fl / el / 1e12, 5), "unit": "TFLOP/s", "cores": cores, "blas": blas, "kind": "oracle",
             "sample": f"{w.name}: {what} of virtual rank {rank_id}, {done} of {w.Hq} query heads, "
                       f"fp64 numpy, {el:.1f}s"}
 
