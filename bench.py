@@ -195,7 +195,7 @@ def main():
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the path is one GPU's share; "
-              "see DESIGN.md for how it would shard.", file=sys.stderr)
+              "the multi-GPU sharding is a design, not built.", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
