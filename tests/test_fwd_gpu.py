@@ -152,6 +152,18 @@ def test_llama8b_s32k_cp8_all_ranks_sampled():
         assert_close(o[:, :, idx], lse[:, :, idx], O_ref, L_ref, "bf16", f"rank {rank}")
 
 
+def test_llama8b_s32k_cp8_rank0_every_row():
+    """Every row of virtual rank 0 of the 32768-token workload (32q/8kv heads,
+    d=128, bf16, cp=8: chunks 0 and 15, 4096 rows per head) against the oracle
+    computed for all of them: the full output, not a sample."""
+    w = si.WORKLOADS["llama8b_s32k_cp8"]
+    announce("llama8b 32k rank 0, every row")
+    R = Rank(w.B, w.Hq, w.Hkv, w.S, w.d, w.cp, 0, w.dtype, seed=w.seed)
+    o, lse = R.ring_fwd()
+    O_ref, L_ref = R.oracle()
+    assert_close(o, lse, O_ref, L_ref, "bf16", "rank 0 every row")
+
+
 def test_llama8b_s128k_cp8_all_ranks_sampled():
     """The bench workload itself (131072 tokens, 32q/8kv heads, d=128, cp=8,
     bf16), in the launch configuration the bench times: every rank's full ring,
