@@ -101,6 +101,22 @@ def test_ring_bwd_32k_cp8_per_rank(rank):
         assert torch.isfinite(t).all()
 
 
+def test_ring_bwd_32k_cp8_rank0_every_head():
+    """Virtual rank 0 of the 32 768-token backward, every kv group (all 32
+    query heads and 8 kv heads), against the oracle's gradients of that rank's
+    loss: the full dQ of its rows and the full dK/dV of every shard."""
+    w = si.WORKLOADS["bwd_s32k_cp8"]
+    R = Rank(w.B, w.Hq, w.Hkv, w.S, w.d, w.cp, 0, "bf16", seed=w.seed, with_dout=True)
+    _, _, dq, dk, dv = R.ring_bwd()
+    torch.cuda.synchronize()
+    g = w.Hq // w.Hkv
+    for kvh in range(w.Hkv):
+        announce(f"ring bwd 32k cp8 rank 0, kv group {kvh}")
+        ref = R.oracle_grads(q_heads=slice(kvh * g, (kvh + 1) * g))
+        _check_grads((dq[:, kvh * g:(kvh + 1) * g], dk[:, kvh:kvh + 1], dv[:, kvh:kvh + 1]), ref,
+                     f"32k rank 0 group {kvh}")
+
+
 @pytest.mark.parametrize("rank", [0, 7])
 def test_ring_bwd_128k_cp8_sampled(rank):
     """The backward at the bench workload's size (131072 tokens, cp=8, 32q/8kv
