@@ -61,6 +61,7 @@ def test_delta_many_batch_heads():
     (1, 2, 2, 1200, 64, 3),     # 400 rows a rank: ragged key and query tiles
     (2, 8, 2, 640, 128, 5),     # batch 2, four query heads a group
     (1, 4, 1, 4096, 128, 1),    # cp = 1: plain causal attention
+    (1, 4, 1, 32768, 128, 8),   # the 32 768-token cp = 8 backward, one kv group of its 32/8 heads
 ])
 def test_ring_bwd_all_ranks_sum_to_full_gradients(B, Hq, Hkv, S, d, cp):
     """Every rank's ring backward, summed, gives the gradients of the whole
