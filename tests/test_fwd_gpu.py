@@ -152,6 +152,28 @@ def test_llama8b_s32k_cp8_all_ranks_sampled():
         assert_close(o[:, :, idx], lse[:, :, idx], O_ref, L_ref, "bf16", f"rank {rank}")
 
 
+@pytest.mark.parametrize("mode", [cpa.CP_STREAM, cpa.CP_WHOLE_DOC])
+def test_varlen_s64k_cp4_all_ranks_sampled(mode):
+    """The packed-document workload itself (65536 tokens of 42 lognormal
+    documents, 32q/8kv heads, d=128, bf16, cp=4), in the deals the bench
+    times: every rank's ring, checked on sampled rows (each rank's first and
+    last rows, rows at its document starts, random rows) against the oracle."""
+    w = si.WORKLOADS["varlen_s64k_cp4"]
+    cu = si.workload_cu_seqlens(w)
+    full = si.make_qkv(w.B, w.Hq, w.Hkv, w.S, w.d, w.dtype, seed=w.seed)
+    rng = np.random.default_rng(3)
+    n = w.S // w.cp
+    for rank in range(w.cp):
+        announce(f"varlen 64k mode {mode} rank {rank}")
+        R = Rank(w.B, w.Hq, w.Hkv, w.S, w.d, w.cp, rank, w.dtype, full=full, cu=cu, mode=mode)
+        o, lse = R.ring_fwd()
+        starts = np.flatnonzero(R.pos == R.lo)  # rows that begin a document
+        idx = np.unique(np.concatenate([[0, n - 1], rng.choice(starts, min(8, len(starts)), replace=False),
+                                        rng.integers(0, n, 40)]))
+        O_ref, L_ref = R.oracle(idx)
+        assert_close(o[:, :, idx], lse[:, :, idx], O_ref, L_ref, "bf16", f"rank {rank}")
+
+
 def test_llama8b_s32k_cp8_rank0_every_row():
     """Every row of virtual rank 0 of the 32768-token workload (32q/8kv heads,
     d=128, bf16, cp=8: chunks 0 and 15, 4096 rows per head) against the oracle
