@@ -25,7 +25,7 @@ __all__ = [
     "CP_OK", "CP_EINVAL", "CP_ESHAPE", "CP_EDTYPE", "CP_EWORKSPACE", "CP_EHIP",
     "CP_F32", "CP_BF16", "CP_STREAM", "CP_PER_DOC", "CP_WHOLE_DOC", "CpShape", "CpError", "LIB_PATH",
     "lib", "cp_version", "cp_last_error", "cp_shard_zigzag", "cp_unshard_zigzag",
-    "cp_varlen_index", "cp_ring_source", "cp_pairs", "cp_attn_fwd_workspace",
+    "cp_varlen_index", "cp_ring_source", "cp_pairs", "cp_attn_ring_fwd_workspace",
     "cp_attn_partial_fwd", "cp_attn_merge", "cp_attn_ring_fwd", "RingFwdPlan", "cp_attn_ring_fwd_stepwise",
     "RingFwdStepwisePlan", "cp_a2a_pack", "cp_a2a_pack_inverse", "cp_a2a_unpack", "cp_a2a_unpack_inverse",
     "cp_attn_bwd_workspace", "cp_attn_bwd_delta", "cp_attn_partial_bwd", "cp_attn_ring_bwd", "RingBwdPlan",
@@ -75,8 +75,8 @@ def lib() -> ctypes.CDLL:
         L.cp_ring_source.argtypes = [c_int32, c_int32, c_int32]
         L.cp_pairs.argtypes = [_I32P, _I32P, c_int64, _I32P, c_int64]
         L.cp_pairs.restype = c_int64
-        L.cp_attn_fwd_workspace.argtypes = [POINTER(CpShape), c_int32]
-        L.cp_attn_fwd_workspace.restype = c_size_t
+        L.cp_attn_ring_fwd_workspace.argtypes = [POINTER(CpShape), c_int32]
+        L.cp_attn_ring_fwd_workspace.restype = c_size_t
         L.cp_attn_partial_fwd.argtypes = [POINTER(CpShape)] + [c_void_p] * 6 + [c_void_p, c_void_p, c_void_p,
                                                                                 c_size_t, c_void_p]
         L.cp_attn_merge.argtypes = [c_int64, c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]
@@ -214,9 +214,9 @@ def _dev_i32(a, device) -> torch.Tensor:
     return torch.from_numpy(_i32(a)).to(device)
 
 
-def cp_attn_fwd_workspace(q, k, v, cp: int = 1) -> int:
+def cp_attn_ring_fwd_workspace(q, k, v, cp: int = 1) -> int:
     s = _shape(q, k, v, (ctypes.c_int64 * 3)(0, 0, 0), None, torch.float32)
-    n = int(lib().cp_attn_fwd_workspace(ctypes.byref(s), cp))
+    n = int(lib().cp_attn_ring_fwd_workspace(ctypes.byref(s), cp))
     if n == 0:
         raise ValueError(cp_last_error() or "invalid shape")
     return n
@@ -241,7 +241,7 @@ def cp_attn_partial_fwd(q, k, v, q_pos, q_lo, k_pos, scale=None, out=None, lse=N
     s = _shape(q, k, v, _strides(out), scale, torch.float32)
     qp, kp = _dev_i32(q_pos, dev), _dev_i32(k_pos, dev)
     ql = None if q_lo is None else _dev_i32(q_lo, dev)
-    ws = _workspace(int(lib().cp_attn_fwd_workspace(ctypes.byref(s), 1)) or 256, dev, workspace)
+    ws = _workspace(int(lib().cp_attn_ring_fwd_workspace(ctypes.byref(s), 1)) or 256, dev, workspace)
     _check(lib().cp_attn_partial_fwd(ctypes.byref(s), q.data_ptr(), k.data_ptr(), v.data_ptr(), qp.data_ptr(),
                                      None if ql is None else ql.data_ptr(), kp.data_ptr(), out.data_ptr(),
                                      lse.data_ptr(), ws.data_ptr(), ws.numel(), _stream(dev)))
@@ -279,7 +279,7 @@ class RingFwdPlan:
         self.qp = _dev_i32(q_pos, dev)
         self.ql = None if q_lo is None else _dev_i32(q_lo, dev)
         self.kp = _dev_i32(k_pos_all, dev)
-        nws = int(lib().cp_attn_fwd_workspace(ctypes.byref(self.shape), cp))
+        nws = int(lib().cp_attn_ring_fwd_workspace(ctypes.byref(self.shape), cp))
         self.ws = _workspace(nws or 256, dev, workspace)
         self.keep = (q_loc, k_all, v_all)
         self.args = (ctypes.byref(self.shape), cp, rank, q_loc.data_ptr(), k_all.data_ptr(), v_all.data_ptr(),

@@ -11,8 +11,8 @@
 // 512 bytes) is moved whole as 16-byte vectors, with ordinary loads and stores
 // (nontemporal hints measured 10-25% slower here).  Grid y is the head-block row
 // (packed layout [g][H/g] = [H] rows of `rows` rows each), grid x covers the
-// rows, so every lane's addresses come from one 32-bit division by a
-// compile-time constant.
+// rows in a grid-stride loop, so every lane's addresses come from one division
+// by a compile-time constant.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -39,23 +39,25 @@ struct RowMap {
 // VPR 16-byte vectors per row.
 template <int VPR>
 __global__ __launch_bounds__(256) void rows_kernel(RowMap m) {
-  const int64_t v = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (v >= m.rows * VPR) return;
-  const int64_t t = v / VPR;
-  const int c = (int)(v - t * VPR);
   const int hd = blockIdx.y;  // head index in [g][H/g] order
-  const int64_t packed = ((int64_t)hd * m.rows + t) * m.row_bytes + 16 * c;
-  int64_t other;
-  if (!m.unpack) {
-    other = t * m.x_rs_bytes + (int64_t)hd * m.row_bytes + 16 * c;  // x[t, hd]
-  } else {
-    const int i = hd / m.hg, hh = hd - i * m.hg;  // block i of head hh
-    other = ((int64_t)hh * m.g * m.rows + (int64_t)i * m.rows + t) * m.row_bytes + 16 * c;  // y[hh, i*rows + t]
+  const int64_t n = m.rows * VPR;
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  for (int64_t v = (int64_t)blockIdx.x * 256 + threadIdx.x; v < n; v += stride) {
+    const int64_t t = v / VPR;
+    const int c = (int)(v - t * VPR);
+    const int64_t packed = ((int64_t)hd * m.rows + t) * m.row_bytes + 16 * c;
+    int64_t other;
+    if (!m.unpack) {
+      other = t * m.x_rs_bytes + (int64_t)hd * m.row_bytes + 16 * c;  // x[t, hd]
+    } else {
+      const int i = hd / m.hg, hh = hd - i * m.hg;  // block i of head hh
+      other = ((int64_t)hh * m.g * m.rows + (int64_t)i * m.rows + t) * m.row_bytes + 16 * c;  // y[hh, i*rows + t]
+    }
+    const int64_t so = m.to_packed ? other : packed;
+    const int64_t dof = m.to_packed ? packed : other;
+    const u32x4 val = *reinterpret_cast<const u32x4*>(m.src + so);
+    *reinterpret_cast<u32x4*>(m.dst + dof) = val;
   }
-  const int64_t so = m.to_packed ? other : packed;
-  const int64_t dof = m.to_packed ? packed : other;
-  const u32x4 val = *reinterpret_cast<const u32x4*>(m.src + so);
-  *reinterpret_cast<u32x4*>(m.dst + dof) = val;
 }
 
 }  // namespace a2ak
@@ -74,7 +76,10 @@ hipError_t launch_a2a(int32_t g, int32_t heads, int64_t rows, int32_t d, int32_t
   m.unpack = unpack;
   m.to_packed = to_packed;
   const int vpr = (int)(m.row_bytes / 16);
-  const dim3 grid((unsigned)((rows * vpr + 255) / 256), (unsigned)heads);
+  // Grid x covers up to 2^22 workgroups (2^30 vectors, the whole row range of
+  // every shard up to 2^25 rows at 512 bytes a row); larger shards loop, so the
+  // grid's work-item count stays inside its 32-bit limit for every row count.
+  const dim3 grid(stride_blocks(rows * vpr), (unsigned)heads);
   switch (vpr) {
     case 8: a2ak::rows_kernel<8><<<grid, 256, 0, stream>>>(m); break;
     case 16: a2ak::rows_kernel<16><<<grid, 256, 0, stream>>>(m); break;

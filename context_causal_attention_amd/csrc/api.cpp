@@ -173,7 +173,7 @@ extern "C" const char* cp_last_error(void) { return g_last_error.c_str(); }
 
 extern "C" int cp_version(void) { return 200; }
 
-extern "C" size_t cp_attn_fwd_workspace(const cp_shape* s, int32_t cp) {
+extern "C" size_t cp_attn_ring_fwd_workspace(const cp_shape* s, int32_t cp) {
   if (check_shape(s) != CP_OK || cp < 1) return 0;
   return fwd_workspace_layout(s->b, s->hkv, s->d, s->sk, cp, s->in_dtype).total;
 }

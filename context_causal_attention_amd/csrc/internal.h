@@ -103,6 +103,16 @@ struct BwdWorkspace {
 BwdWorkspace bwd_workspace_layout(int32_t b, int32_t hq, int32_t hkv, int32_t d, int64_t sq, int64_t sk,
                                   int32_t cp);
 
+// Workgroups of 256 threads for a grid-stride loop over `items` work items:
+// enough for one item per thread up to 2^30 items, never more than 2^22
+// workgroups, so the grid's work-item count (a 32-bit quantity) stays below
+// 2^32 for every size; kernels loop over the rest.
+constexpr int64_t kStrideMaxBlocks = (int64_t)1 << 22;
+inline unsigned stride_blocks(int64_t items) {
+  const int64_t n = items <= 0 ? 0 : (items + 255) / 256;
+  return (unsigned)(n < kStrideMaxBlocks ? n : kStrideMaxBlocks);
+}
+
 // Kernel launchers (attn_fwd.hip, attn_bwd.hip, merge.hip).  Return hipError_t codes.
 hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_delta(const BwdArgs& a, hipStream_t stream);

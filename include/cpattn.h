@@ -138,8 +138,13 @@ int cp_varlen_index(const int32_t* cu_seqlens, int32_t n_docs, int32_t cp, int32
 int cp_ring_source(int32_t cp, int32_t rank, int32_t step);
 
 /* Exact number of allowed (query, key) pairs, q_lo[i] <= k_pos[j] <= q_pos[i],
- * over host arrays (q_lo may be NULL).  Used for FLOP accounting and the
- * zigzag balance check.  Returns the count, or -1 on a null array with n > 0
+ * over host arrays (q_lo may be NULL).  It measures the work balance that the
+ * 2*cp chunking exists for: the "Required constraints" of the NeMo
+ * Megatron-Bridge "Hierarchical Context Parallel Skill" page ask for a sequence
+ * length that is a multiple of 2*cp, and with the zigzag deal every rank of a
+ * dense causal sequence then gets S(S+1)/(2cp) pairs; the FlashCP abstract
+ * names the imbalance that uneven pair counts cause.  Used for FLOP accounting
+ * and that balance check.  Returns the count, or -1 on a null array with n > 0
  * or a negative length. */
 int64_t cp_pairs(const int32_t* q_pos, const int32_t* q_lo, int64_t nq,
                  const int32_t* k_pos, int64_t nk);
@@ -148,7 +153,7 @@ int64_t cp_pairs(const int32_t* q_pos, const int32_t* q_lo, int64_t nq,
 
 /* Workspace bytes needed by cp_attn_partial_fwd (cp = 1) and cp_attn_ring_fwd
  * (cp = ring size).  Returns 0 for an invalid descriptor. */
-size_t cp_attn_fwd_workspace(const cp_shape* s, int32_t cp);
+size_t cp_attn_ring_fwd_workspace(const cp_shape* s, int32_t cp);
 
 /* One ring step, the guide's attn(Q_i, K_j, V_j): every query row attends to
  * the allowed keys among the sk key rows.  q (device, in_dtype) [b,hq,sq,d];
@@ -157,7 +162,7 @@ size_t cp_attn_fwd_workspace(const cp_shape* s, int32_t cp);
  * strides o_str) normalised over this step's allowed keys and LSE (device fp32,
  * contiguous [b,hq,sq]).  A row with no allowed key gets O = 0, LSE = -inf (the
  * identity of cp_attn_merge).  ws (device) of at least
- * cp_attn_fwd_workspace(s, 1) bytes, 256-byte aligned. */
+ * cp_attn_ring_fwd_workspace(s, 1) bytes, 256-byte aligned. */
 int cp_attn_partial_fwd(const cp_shape* s, const void* q, const void* k, const void* v,
                         const int32_t* q_pos, const int32_t* q_lo, const int32_t* k_pos,
                         float* o, float* lse, void* ws, size_t ws_bytes, hipStream_t stream);
@@ -180,7 +185,7 @@ int cp_attn_merge(int64_t rows, int32_t d, float* o_acc, float* lse_acc,
  * all-gather of the shards lays them out; k_pos_all (device int32 [sk]) their
  * global positions.  Writes the final O (device, out_dtype, strides o_str) and
  * LSE (device fp32, contiguous [b,hq,sq]).  CP_ESHAPE unless sk % (2cp) == 0.
- * ws (device) of at least cp_attn_fwd_workspace(s, cp) bytes, 256-byte
+ * ws (device) of at least cp_attn_ring_fwd_workspace(s, cp) bytes, 256-byte
  * aligned. */
 int cp_attn_ring_fwd(const cp_shape* s, int32_t cp, int32_t rank, const void* q_loc,
                      const void* k_all, const void* v_all, const int32_t* q_pos,

@@ -25,9 +25,14 @@ def _declared_functions():
 def test_library_exports_every_declared_symbol():
     L = cpa.lib()
     names = _declared_functions()
-    for must in ("cp_attn_ring_fwd", "cp_shard_zigzag", "cp_attn_ring_bwd", "cp_attn_ring_fwd_stepwise", "cp_a2a_pack",
-                 "cp_a2a_unpack", "cp_varlen_index"):
+    # The boundary's calls: the index map, one step, the merge, the whole ring and
+    # its workspace query, the backward, then the stepwise ring and the head exchange.
+    for must in ("cp_shard_zigzag", "cp_unshard_zigzag", "cp_varlen_index", "cp_ring_source", "cp_pairs",
+                 "cp_attn_partial_fwd", "cp_attn_merge", "cp_attn_ring_fwd", "cp_attn_ring_fwd_workspace",
+                 "cp_attn_bwd_delta", "cp_attn_partial_bwd", "cp_attn_ring_bwd", "cp_last_error", "cp_version",
+                 "cp_attn_ring_fwd_stepwise", "cp_a2a_pack", "cp_a2a_unpack"):
         assert must in names
+    assert "cp_attn_fwd_workspace" not in names
     for n in names:
         assert hasattr(L, n), f"{n} declared in cpattn.h but not exported"
     assert cpa.cp_version() >= 100
@@ -239,7 +244,7 @@ def test_ring_fwd_rejects_bad_args():
     assert _ring(s, qpos=0) == cpa.CP_EINVAL
     assert _ring(s, ws=0) == cpa.CP_EWORKSPACE
     assert _ring(s, ws=FAKE + 16) == cpa.CP_EWORKSPACE
-    need = cpa.lib().cp_attn_fwd_workspace(ctypes.byref(s), 2)
+    need = cpa.lib().cp_attn_ring_fwd_workspace(ctypes.byref(s), 2)
     assert need > 0
     assert _ring(s, ws_bytes=need - 1) == cpa.CP_EWORKSPACE
 
@@ -271,7 +276,7 @@ def test_ring_fwd_stepwise_validation():
     # its epilogue, so no partial is stored.  That is the one-step forward's
     # workspace over one shard of sk / cp = 256 keys.
     one = _shape(sk=256)
-    assert need == L.cp_attn_fwd_workspace(ctypes.byref(one), 1) > 0
+    assert need == L.cp_attn_ring_fwd_workspace(ctypes.byref(one), 1) > 0
     # two slots of K and V, one shard each: 2 kv heads x 256 rows x 128 x bf16
     assert L.cp_attn_ring_stage_bytes(ctypes.byref(s), 2) == 4 * 2 * 256 * 128 * 2
     assert L.cp_attn_ring_fwd_stepwise_workspace(ctypes.byref(_shape(d=96)), 2) == 0
@@ -328,11 +333,11 @@ def test_a2a_validation():
 
 def test_workspace_query():
     s = _shape(sk=131072, sq=16384, hq=32, hkv=8)
-    n = cpa.lib().cp_attn_fwd_workspace(ctypes.byref(s), 8)
+    n = cpa.lib().cp_attn_ring_fwd_workspace(ctypes.byref(s), 8)
     # bf16 V^T copy (8 heads x 128 x 131072 x 2 B) plus the tile bounds table
     assert n >= 8 * 128 * 131072 * 2
     assert n < 8 * 128 * 131072 * 2 + (1 << 20)
-    assert cpa.lib().cp_attn_fwd_workspace(ctypes.byref(_shape(d=96)), 8) == 0
+    assert cpa.lib().cp_attn_ring_fwd_workspace(ctypes.byref(_shape(d=96)), 8) == 0
 
 
 def test_merge_and_partial_validation():
@@ -349,7 +354,7 @@ def test_merge_and_partial_validation():
 def test_python_wrappers_raise_value_error():
     q = torch.zeros(1, 2, 8, 96)
     with pytest.raises(ValueError):
-        cpa.cp_attn_fwd_workspace(q, q, q, 1)
+        cpa.cp_attn_ring_fwd_workspace(q, q, q, 1)
     with pytest.raises(ValueError):
         cpa.cp_attn_merge(torch.zeros(4, 64), torch.zeros(3), torch.zeros(4, 64), torch.zeros(4))
 

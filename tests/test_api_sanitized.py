@@ -54,6 +54,7 @@ DRIVER = r"""
 #include <initializer_list>
 #include <limits>
 #include "cpattn.h"
+#include "internal.h"
 
 int stub_live_events();
 static int failures = 0;
@@ -79,7 +80,7 @@ int main() {
   // Valid calls run their whole host path.
   for (int32_t in : {CP_BF16, CP_F32}) {
     cp_shape s = shape(256, 512, 128, in);
-    CHECK(cp_attn_fwd_workspace(&s, 2) > 0);
+    CHECK(cp_attn_ring_fwd_workspace(&s, 2) > 0);
     CHECK(cp_attn_partial_fwd(&s, F, F, F, FI, nullptr, FI, FF, FF, WS, BIG, nullptr) == CP_OK);
     CHECK(cp_attn_ring_fwd(&s, 2, 1, F, F, F, FI, FI, FI, F, FF, WS, BIG, nullptr) == CP_OK);
     CHECK(cp_attn_ring_fwd_stepwise(&s, 2, 0, F, F, F, FI, nullptr, FI, FF, FF, WS, BIG, nullptr, 0, nullptr,
@@ -115,7 +116,7 @@ int main() {
         case 4: s.v_str[2] = h; break;
         case 5: s.o_str[0] = h; break;
       }
-      cp_attn_fwd_workspace(&s, 2);
+      cp_attn_ring_fwd_workspace(&s, 2);
       cp_attn_bwd_workspace(&s, 2);
       cp_attn_ring_fwd_stepwise_workspace(&s, 2);
       cp_attn_ring_stage_bytes(&s, 2);
@@ -147,6 +148,19 @@ int main() {
   CHECK(cp_attn_merge(i64max, 128, FF, FF, FF, FF, nullptr) != CP_OK);
   CHECK(cp_a2a_pack(2, 32, i64max, 128, CP_BF16, F, 4096, F, 0, nullptr) != CP_OK);
   CHECK(cp_a2a_pack(2, 32, 1024, 128, CP_BF16, F, i64max, F, 0, nullptr) != CP_OK);
+  // The grid of the merge and head-exchange launches: for every row count the
+  // calls accept (2^31 rows, 16-byte vectors of d = 128 fp32 rows: 2^36
+  // items), one workgroup per 256 items up to the cap, and a work-item count
+  // below 2^32.
+  for (int64_t items : {int64_t(0), int64_t(1), int64_t(256), int64_t(257), int64_t(1) << 30, (int64_t(1) << 30) + 1,
+                        int64_t(1) << 32, (int64_t(1) << 31) * 32, (int64_t(1) << 31) * 32 * 65535}) {
+    const int64_t blocks = cpattn::stride_blocks(items);
+    CHECK(blocks * 256 <= int64_t(0xFFFFFFFF));
+    CHECK((items == 0) == (blocks == 0));
+    if (items <= (int64_t(1) << 30)) CHECK(blocks * 256 >= items && (blocks - 1) * 256 < items);
+  }
+  CHECK(cp_attn_merge(int64_t(1) << 31, 128, FF, FF, FF, FF, nullptr) == CP_OK);
+  CHECK(cp_attn_merge((int64_t(1) << 31) + 1, 128, FF, FF, FF, FF, nullptr) != CP_OK);
   CHECK(stub_live_events() == 0);
   if (failures) { std::fprintf(stderr, "%d checks failed\n", failures); return 1; }
   std::printf("api host code ok\n");
