@@ -60,6 +60,7 @@ __all__ = [
     "a2a_unpack",
     "a2a_pack_unpack",
     "ring_partials_fwd",
+    "per_doc_positions",
     "attention_matrix_bytes",
 ]
 
@@ -144,6 +145,24 @@ def whole_doc_deal(cu_seqlens, cp: int):
         pos = [p for a, b in pieces[r] for p in range(a, b)]
         out.append(np.array(sorted(pos), dtype=np.int64))
     return out
+
+
+def per_doc_positions(cu_seqlens, cp: int, rank: int) -> np.ndarray:
+    """Per-document zigzag (the Per-Doc sharding named in the FlashCP
+    abstract): every document is cut into 2*cp equal chunks on its own and rank
+    ``rank`` takes chunks ``rank`` and ``2cp-1-rank`` of each, documents kept in
+    their packed order.  Every document length must be a multiple of 2*cp (the
+    divisibility rule of the hierarchical-CP page's "Required constraints",
+    applied per document)."""
+    cu = [int(x) for x in cu_seqlens]
+    out = []
+    for s, e in zip(cu[:-1], cu[1:]):
+        n = e - s
+        if n % (2 * cp) != 0:
+            raise ValueError("every document length must be a multiple of 2*cp")
+        if n:
+            out.append(s + zigzag_positions(n, cp, rank))
+    return np.concatenate(out) if out else np.zeros(0, dtype=np.int64)
 
 
 def doc_start_of(positions, cu_seqlens) -> np.ndarray:

@@ -9,7 +9,8 @@ Recipe (one generator for every workload):
 * q, k, v (and dO for the backward) are drawn as fp32 ``torch.randn`` from a CPU
   ``torch.Generator`` seeded with ``seed``, in the order q, k, v, dO, then cast to
   the workload dtype (bf16 casts round to nearest even).  fp64 copies of the cast
-  values are exact, which is what the oracle sees.
+  values are exact, which is what the oracle sees.  Large-range cases scale the
+  fp32 q draw by a constant before the cast.
 * Packed-document lengths are lognormal with distribution mean 2048 and log-sd
   1.0 (so the underlying normal has mean ln 2048 - 1/2), rounded to integers,
   clipped to [128, 16384] and drawn in order until the total is reached; the
@@ -78,12 +79,16 @@ def _torch_dtype(name: str):
 
 
 def make_qkv(B: int, Hq: int, Hkv: int, S: int, d: int, dtype: str = "bf16", seed: int = 0,
-             with_dout: bool = False):
+             with_dout: bool = False, q_scale: float = 1.0):
     """CPU tensors q [B,Hq,S,d], k, v [B,Hkv,S,d] (and dO [B,Hq,S,d]) drawn as
-    fp32 N(0,1) in the order q, k, v, dO from one seeded generator, then cast."""
+    fp32 N(0,1) in the order q, k, v, dO from one seeded generator, then cast.
+    q_scale multiplies the fp32 q draw before the cast (q ~ N(0, q_scale^2)):
+    scores then span q_scale times their usual range."""
     g = torch.Generator(device="cpu")
     g.manual_seed(seed)
     q = torch.randn(B, Hq, S, d, generator=g, dtype=torch.float32)
+    if q_scale != 1.0:
+        q = q * q_scale
     k = torch.randn(B, Hkv, S, d, generator=g, dtype=torch.float32)
     v = torch.randn(B, Hkv, S, d, generator=g, dtype=torch.float32)
     out = [q, k, v]

@@ -18,6 +18,23 @@ def announce(msg):
     print(f"[case] {msg}", flush=True)
 
 
+def oracle_deal(S, cp, rank, cu=None, mode=cpa.CP_STREAM):
+    """The oracle's positions and document starts of `rank`'s rows: the zigzag
+    deal of the sequence (or packed stream), the per-document zigzag, or the
+    whole-document placement."""
+    if cu is None:
+        return orc.zigzag_positions(S, cp, rank), None
+    if mode == cpa.CP_STREAM:
+        pos = orc.zigzag_positions(S, cp, rank)
+    elif mode == cpa.CP_PER_DOC:
+        pos = orc.per_doc_positions(cu, cp, rank)
+    elif mode == cpa.CP_WHOLE_DOC:
+        pos = orc.whole_doc_deal(cu, cp)[rank]
+    else:
+        raise ValueError(f"unknown deal {mode}")
+    return pos, orc.doc_start_of(pos, cu)
+
+
 class Rank:
     """Inputs of one virtual rank, on the GPU, plus fp64 copies for the oracle."""
 
@@ -29,13 +46,17 @@ class Rank:
             full = si.make_qkv(B, Hq, Hkv, S, d, dtype, seed=seed, with_dout=with_dout)
         self.full = full
         q, k, v = full[:3]
+        # Every index map comes from the oracle's own deal; the library's map
+        # must equal it bit for bit before anything runs on the GPU.
+        self.pos, self.lo = oracle_deal(S, cp, rank, cu, mode)
+        self.allp = np.concatenate([oracle_deal(S, cp, r, cu, mode)[0] for r in range(cp)])
         if cu is None:
-            self.pos = cpa.cp_shard_zigzag(S, cp, rank)
-            self.lo = None
-            self.allp = cpa.cp_unshard_zigzag(S, cp)
+            lib_pos, lib_lo = cpa.cp_shard_zigzag(S, cp, rank), None
+            assert np.array_equal(cpa.cp_unshard_zigzag(S, cp), self.allp)
         else:
-            self.pos, self.lo = cpa.cp_varlen_index(cu, cp, rank, mode)
-            self.allp = np.concatenate([cpa.cp_varlen_index(cu, cp, r, mode)[0] for r in range(cp)])
+            lib_pos, lib_lo = cpa.cp_varlen_index(cu, cp, rank, mode)
+            assert np.array_equal(lib_lo, self.lo)
+        assert np.array_equal(lib_pos, self.pos), "library index map differs from the oracle's deal"
         pi = torch.from_numpy(self.pos.astype(np.int64))
         ai = torch.from_numpy(self.allp.astype(np.int64))
         self.q_loc = q.index_select(2, pi).cuda()

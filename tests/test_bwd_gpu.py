@@ -61,7 +61,6 @@ def test_delta_many_batch_heads():
     (1, 2, 2, 1200, 64, 3),     # 400 rows a rank: ragged key and query tiles
     (2, 8, 2, 640, 128, 5),     # batch 2, four query heads a group
     (1, 4, 1, 4096, 128, 1),    # cp = 1: plain causal attention
-    (1, 4, 1, 32768, 128, 8),   # the 32 768-token cp = 8 backward, one kv group of its 32/8 heads
 ])
 def test_ring_bwd_all_ranks_sum_to_full_gradients(B, Hq, Hkv, S, d, cp):
     """Every rank's ring backward, summed, gives the gradients of the whole
@@ -78,10 +77,40 @@ def test_ring_bwd_all_ranks_sum_to_full_gradients(B, Hq, Hkv, S, d, cp):
         assert e <= GTOL, f"rank {rank}: dq max-abs error {e:.3e}"
         dk_sum = dk if dk_sum is None else dk_sum + dk
         dv_sum = dv if dv_sum is None else dv_sum + dv
-    allp = cpa.cp_unshard_zigzag(S, cp)
+    allp = orc.all_rank_positions(S, cp)
     for name, g, r in (("dk", dk_sum, dk_ref[:, :, allp]), ("dv", dv_sum, dv_ref[:, :, allp])):
         e = max_err(g, r)
         assert e <= GTOL, f"{name} summed over ranks: max-abs error {e:.3e}"
+
+
+@pytest.mark.parametrize("kvh", [0, 7])
+def test_c4_all_ranks_sum_to_full_gradients(kvh):
+    """The backward workload itself (32 768 tokens, cp = 8, 32 query / 8 kv
+    heads, d = 128, bf16, dO ~ N(0,1)): all 8 virtual ranks' ring backwards
+    over every head, their dK/dV summed, against the oracle's gradients of the
+    whole sequence for one kv group (query heads 4kvh..4kvh+3): dQ row by row
+    on every rank, dK and dV from every rank's contribution.  kv groups 0 and
+    7, the first and the last."""
+    w = si.WORKLOADS["bwd_s32k_cp8"]
+    full = si.make_qkv(w.B, w.Hq, w.Hkv, w.S, w.d, "bf16", seed=w.seed, with_dout=True)
+    g = w.Hq // w.Hkv
+    hs, ks = slice(kvh * g, (kvh + 1) * g), slice(kvh, kvh + 1)
+    q, k, v, do = (_np(t) for t in full)
+    dq_ref, dk_ref, dv_ref = orc.attention_bwd(q[:, hs], k[:, ks], v[:, ks], do[:, hs], w.scale)
+    dk_sum = dv_sum = None
+    for rank in range(w.cp):
+        announce(f"c4 all ranks summed, kv group {kvh}: rank {rank}")
+        R = Rank(w.B, w.Hq, w.Hkv, w.S, w.d, w.cp, rank, "bf16", full=full)
+        _, _, dq, dk, dv = R.ring_bwd()
+        e = max_err(dq[:, hs], dq_ref[:, :, R.pos])
+        assert e <= GTOL, f"rank {rank}: dq max-abs error {e:.3e}"
+        dk_sum = dk[:, ks].clone() if dk_sum is None else dk_sum + dk[:, ks]
+        dv_sum = dv[:, ks].clone() if dv_sum is None else dv_sum + dv[:, ks]
+        del R, dq, dk, dv
+    allp = orc.all_rank_positions(w.S, w.cp)
+    for name, got, ref in (("dk", dk_sum, dk_ref[:, :, allp]), ("dv", dv_sum, dv_ref[:, :, allp])):
+        e = max_err(got, ref)
+        assert e <= GTOL, f"{name} summed over ranks, kv group {kvh}: max-abs error {e:.3e}"
 
 
 @pytest.mark.parametrize("rank", [0, 7])

@@ -152,19 +152,23 @@ def test_llama8b_s32k_cp8_all_ranks_sampled():
         assert_close(o[:, :, idx], lse[:, :, idx], O_ref, L_ref, "bf16", f"rank {rank}")
 
 
-@pytest.mark.parametrize("mode", [cpa.CP_STREAM, cpa.CP_WHOLE_DOC])
-def test_varlen_s64k_cp4_all_ranks_sampled(mode):
-    """The packed-document workload itself (65536 tokens of 42 lognormal
-    documents, 32q/8kv heads, d=128, bf16, cp=4), in the deals the bench
-    times: every rank's ring, checked on sampled rows (each rank's first and
-    last rows, rows at its document starts, random rows) against the oracle."""
-    w = si.WORKLOADS["varlen_s64k_cp4"]
+@pytest.mark.parametrize("name,mode", [("varlen_s64k_cp4", cpa.CP_STREAM), ("varlen_s64k_cp4", cpa.CP_WHOLE_DOC),
+                                       ("varlen8_s64k_cp4", cpa.CP_STREAM), ("varlen8_s64k_cp4", cpa.CP_PER_DOC),
+                                       ("varlen8_s64k_cp4", cpa.CP_WHOLE_DOC)])
+def test_varlen_s64k_cp4_all_ranks_sampled(name, mode):
+    """The packed-document workloads themselves (65536 tokens of 42 lognormal
+    documents, and the same documents with lengths rounded to multiples of
+    2cp = 8 so that the per-document deal applies; 32q/8kv heads, d=128,
+    bf16, cp=4), in every deal the bench times: every rank's ring, checked on
+    sampled rows (each rank's first and last rows, rows at its document
+    starts, random rows) against the oracle."""
+    w = si.WORKLOADS[name]
     cu = si.workload_cu_seqlens(w)
     full = si.make_qkv(w.B, w.Hq, w.Hkv, w.S, w.d, w.dtype, seed=w.seed)
     rng = np.random.default_rng(3)
     n = w.S // w.cp
     for rank in range(w.cp):
-        announce(f"varlen 64k mode {mode} rank {rank}")
+        announce(f"{name} mode {mode} rank {rank}")
         R = Rank(w.B, w.Hq, w.Hkv, w.S, w.d, w.cp, rank, w.dtype, full=full, cu=cu, mode=mode)
         o, lse = R.ring_fwd()
         starts = np.flatnonzero(R.pos == R.lo)  # rows that begin a document
@@ -227,6 +231,19 @@ def test_long_dense_ring_sampled(d):
         assert_close(o[:, :, idx], lse[:, :, idx], O_ref, L_ref, "bf16", f"rank {rank}")
         del R, o, lse
         torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("rank", [0, 3])
+def test_long_dense_ring_every_row(rank):
+    """Every row of one rank of a dense ring of 65536 keys (cp = 4, 4 query
+    heads on 1 kv head, d = 128): the 8-wave launch the bench times for its
+    131072-token workload, checked in full against the oracle."""
+    S, cp, Hq, Hkv, d = 65536, 4, 4, 1, 128
+    announce(f"dense ring S={S} rank {rank}, every row (8-wave launch)")
+    R = Rank(1, Hq, Hkv, S, d, cp, rank, "bf16", seed=5)
+    o, lse = R.ring_fwd()
+    O_ref, L_ref = R.oracle()
+    assert_close(o, lse, O_ref, L_ref, "bf16", f"rank {rank} every row")
 
 
 def test_local_only_schedule_fails_parity():

@@ -314,6 +314,37 @@ def test_partial_bwd_own_step_matches_central_differences():
         assert abs(fd - an) <= 1e-7 * max(1.0, abs(an))
 
 
+# ---------------------------------------------------------------- per-document zigzag
+def test_per_doc_positions_worked_example():
+    """Documents of 8 and 4 tokens (S = 12), cp = 2, so 2cp = 4 chunks per
+    document: 2-token chunks of [0, 8) and 1-token chunks of [8, 12).  Rank 0
+    takes chunks 0 and 3 of each: {0, 1, 6, 7} then {8, 11}; rank 1 chunks 1
+    and 2: {2, 3, 4, 5} then {9, 10}."""
+    assert orc.per_doc_positions([0, 8, 12], 2, 0).tolist() == [0, 1, 6, 7, 8, 11]
+    assert orc.per_doc_positions([0, 8, 12], 2, 1).tolist() == [2, 3, 4, 5, 9, 10]
+    with pytest.raises(ValueError, match="multiple of 2"):
+        orc.per_doc_positions([0, 6, 16], 2, 0)
+
+
+@pytest.mark.parametrize("cp,seed", [(2, 1), (4, 2), (8, 3)])
+def test_per_doc_positions_balance(cp, seed):
+    """Every position on exactly one rank; within each document a rank holds
+    2/(2cp) of its tokens; and every rank gets the same number of causal
+    pairs inside documents: a document of n = 2cp*c tokens gives each rank
+    (2cp*c^2 + c) pairs, the dense zigzag identity applied per document."""
+    L = si.round_doc_lengths(si.doc_lengths(total=2 * cp * 600, mean=300, sigma=1.0, lo=8, hi=2500, seed=seed),
+                             2 * cp)
+    cu = si.cu_seqlens_from_lengths(L)
+    S = int(cu[-1])
+    parts = [orc.per_doc_positions(cu, cp, r) for r in range(cp)]
+    assert np.array_equal(np.sort(np.concatenate(parts)), np.arange(S))
+    expect = sum((n // (2 * cp)) * (2 * cp * (n // (2 * cp)) + 1) for n in L)
+    for p in parts:
+        assert orc.pair_count(p, orc.doc_start_of(p, cu), np.arange(S)) == expect
+        for a, b in zip(cu[:-1], cu[1:]):
+            assert np.sum((p >= a) & (p < b)) == (b - a) // cp
+
+
 # ---------------------------------------------------------------- whole-document placement
 def test_whole_doc_deal_worked_example():
     """Documents of 7, 2, 1, 2 tokens (S = 12), cp = 3, room 4 per rank.

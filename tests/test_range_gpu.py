@@ -1,0 +1,229 @@
+"""GPU parity where scores span tens of log units, against the fp64 oracle.
+
+The forward keeps a running maximum per row and takes exponentials against it
+as it stands; it rescales only when a tile's scores run far above it (the bf16
+kernel when a lane's partial sum of a tile passes 2^40, the fp32 kernel when a
+tile's maximum passes the running one by 8 log2 units).  The stepwise ring
+merges each step's partial into the running output by LSE weighting.  With
+N(0,1) inputs and scale 1/sqrt(d) scores stay within a few units and a row's
+maximum nearly always arrives in its first tile, so none of these branches is
+reached.  Here:
+  * q is drawn 24x wider (scores of std ~24, spanning ~200 natural-log units),
+    so running maxima keep being overtaken;
+  * for chosen rows, one key in the last shard the ring visits (its last
+    allowed key there, so in the last tile that row sees) is replaced by a
+    multiple of that row's query, so its score beats every earlier score of
+    the row by a set margin of 8 to 70 natural-log units: the row's maximum
+    arrives last, with and without the 2^40 rescale, and the stepwise ring
+    merges partials whose LSEs differ by tens of units.
+Tolerances are the acceptance bars (bf16: O 2e-2, LSE 1e-3; fp32: 1e-5;
+gradients 5e-2).  fp32 margins stay small: an fp32 score of size s carries an
+accumulation error near s * 2^-24 * sqrt(d), which a 1e-5 absolute bar allows
+only for scores of a few tens of units.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as orc
+import seeded_inputs as si
+import context_causal_attention_amd as cpa
+from gpu_cases import Rank, announce, assert_close, max_err
+
+pytestmark = pytest.mark.gpu
+
+GTOL = 5e-2
+MARGINS_BF16 = (8.0, 20.0, 32.0, 45.0, 70.0)
+MARGINS_F32 = (6.0, 9.0, 12.0)
+
+
+def plant_late_spikes(full, S, cp, rank, margins, head=0):
+    """Copies of (q, k, v[, dO]) in which, for len(margins) rows of `rank`
+    (half from each of its two chunks where the first chunk has earlier
+    shards to see), the last key the ring visits among the row's allowed keys
+    is replaced by a multiple of the row's query, so that its score exceeds
+    the row's largest other score by the margin (natural log units) for query
+    head `head`.  Dense causal positions.  Returns (tensors, [(row, key,
+    margin)])."""
+    q, k = full[0], full[1].clone()
+    Hq, Hkv, d = q.shape[1], k.shape[1], q.shape[3]
+    kvh = head // (Hq // Hkv)
+    scale = 1.0 / math.sqrt(d)
+    pos = orc.zigzag_positions(S, cp, rank)
+    c = S // (2 * cp)
+    n_a = len(margins) // 2 if rank > 0 else 0
+    picks = list(np.linspace(c // 3, c - 1, n_a).astype(int)) + \
+        list(c + np.linspace(c // 3, c - 1, len(margins) - n_a).astype(int))
+    planted = []
+    # Largest margin first.  A later plant can raise an earlier row's best
+    # other score, so the targets are then taken again, against every other
+    # key as it stands, for a few passes (the tests check the realized margins).
+    for at, m in zip(picks, sorted(margins, reverse=True)):
+        row = int(pos[at])
+        key = None
+        for t in reversed(range(cp)):  # ring steps, last first
+            shard = orc.zigzag_positions(S, cp, (rank - t) % cp)
+            ok = [int(p) for p in shard if p <= row and all(int(p) != u for _, u, _ in planted)]
+            if ok:
+                key = ok[-1]  # last in the shard's storage order
+                break
+        planted.append((row, key, m))
+    for _ in range(4):
+        for row, key, m in planted:
+            qr = q[0, head, row].double().numpy()
+            s = scale * (k[0, kvh, :row + 1].double().numpy() @ qr)
+            s[key] = -np.inf
+            target = float(s.max()) + m
+            k[0, kvh, key] = torch.from_numpy(qr * (target / (scale * float(qr @ qr)))).to(k.dtype)
+    return (q, k) + tuple(full[2:]), planted
+
+
+def realized_margins(full, planted, head=0):
+    """Score of each planted key minus the row's largest other score (head `head`)."""
+    q, k = full[0], full[1]
+    Hq, Hkv, d = q.shape[1], k.shape[1], q.shape[3]
+    kvh = head // (Hq // Hkv)
+    out = []
+    for row, key, _ in planted:
+        s = (k[0, kvh, :row + 1].double().numpy() @ q[0, head, row].double().numpy()) / math.sqrt(d)
+        top = s[key]
+        s[key] = -np.inf
+        out.append(float(top - s.max()))
+    return out
+
+
+def _rows_to_check(R, planted, n_random, seed):
+    rng = np.random.default_rng(seed)
+    n = len(R.pos)
+    where = {int(p): i for i, p in enumerate(R.pos)}
+    idx = [where[r] for r, _, _ in planted] + [0, n // 2 - 1, n // 2, n - 1] + list(rng.integers(0, n, n_random))
+    return np.unique(np.array(idx))
+
+
+# ------------------------------------------------------------------ forward, bf16, both launch widths
+@pytest.mark.parametrize("S,cp,d", [(65536, 4, 128), (8192, 4, 128), (4096, 2, 64)])
+def test_late_spike_ring_fwd_bf16(S, cp, d):
+    """Rows whose maximum arrives in the last tile they see, beating every
+    earlier score by 8-70 units, on a dense ring of 65536 keys (8-wave
+    launch) and of 8192 and 4096 keys (4-wave launch)."""
+    base = si.make_qkv(1, 4, 1, S, d, "bf16", seed=31)
+    for rank in (0, cp - 1):
+        full, planted = plant_late_spikes(base, S, cp, rank, MARGINS_BF16)
+        got = realized_margins(full, planted)
+        assert all(g > m - 0.5 for g, (_, _, m) in zip(got, planted)), got
+        announce(f"late spikes bf16 S={S} cp={cp} d={d} rank {rank}: margins {[round(g, 1) for g in got]}")
+        R = Rank(1, 4, 1, S, d, cp, rank, "bf16", full=full)
+        o, lse = R.ring_fwd()
+        idx = _rows_to_check(R, planted, 24, rank) if S > 16384 else None
+        O_ref, L_ref = R.oracle(idx)
+        if idx is not None:
+            o, lse = o[:, :, idx], lse[:, :, idx]
+        assert_close(o, lse, O_ref, L_ref, "bf16", f"late spikes rank {rank}")
+        del R
+        torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("S,cp,d", [(65536, 4, 128), (8192, 4, 128)])
+def test_wide_scores_ring_fwd_bf16(S, cp, d):
+    """q drawn 24x wider: scores of std ~24 over ~200 natural-log units, so
+    rows keep finding new maxima far above the running one."""
+    full = si.make_qkv(1, 4, 1, S, d, "bf16", seed=32, q_scale=24.0)
+    for rank in (0, cp - 1):
+        announce(f"wide scores bf16 S={S} cp={cp} d={d} rank {rank}")
+        R = Rank(1, 4, 1, S, d, cp, rank, "bf16", full=full)
+        o, lse = R.ring_fwd()
+        if S > 16384:
+            idx = _rows_to_check(R, [], 48, 10 + rank)
+            O_ref, L_ref = R.oracle(idx)
+            o, lse = o[:, :, idx], lse[:, :, idx]
+        else:
+            O_ref, L_ref = R.oracle()
+        assert_close(o, lse, O_ref, L_ref, "bf16", f"wide scores rank {rank}")
+        del R
+        torch.cuda.empty_cache()
+
+
+def test_wide_scores_varlen_bf16():
+    """Wide scores with packed documents (4-wave launch with document masks)."""
+    cp = 4
+    cu = si.cu_seqlens_from_lengths(si.doc_lengths(total=8192, mean=700, sigma=1.0, lo=16, hi=4000, seed=33))
+    full = si.make_qkv(1, 4, 2, 8192, 128, "bf16", seed=34, q_scale=24.0)
+    for mode in (cpa.CP_STREAM, cpa.CP_WHOLE_DOC):
+        for rank in range(cp):
+            announce(f"wide scores varlen mode {mode} rank {rank}")
+            R = Rank(1, 4, 2, 8192, 128, cp, rank, "bf16", full=full, cu=cu, mode=mode)
+            o, lse = R.ring_fwd()
+            assert_close(o, lse, *R.oracle(), "bf16", f"wide scores varlen rank {rank}")
+
+
+# ------------------------------------------------------------------ forward, fp32
+def test_late_spike_ring_fwd_f32_c0_shape():
+    """The 1024-token fp32 shape (1 head, d = 64, cp = 2): rows whose maximum
+    arrives last, 6-12 units above every earlier score (past the fp32
+    kernel's 8-log2-unit rescale trigger), and q drawn 4x wider."""
+    w = si.WORKLOADS["c0_f32_s1024_cp2"]
+    base = si.make_qkv(w.B, w.Hq, w.Hkv, w.S, w.d, "f32", seed=w.seed)
+    for rank in range(w.cp):
+        full, planted = plant_late_spikes(base, w.S, w.cp, rank, MARGINS_F32)
+        announce(f"late spikes f32 c0 rank {rank}: margins {[round(g, 1) for g in realized_margins(full, planted)]}")
+        R = Rank(w.B, w.Hq, w.Hkv, w.S, w.d, w.cp, rank, "f32", full=full)
+        assert_close(*R.ring_fwd(), *R.oracle(), "f32", f"late spikes f32 rank {rank}")
+    wide = si.make_qkv(w.B, w.Hq, w.Hkv, w.S, w.d, "f32", seed=w.seed, q_scale=4.0)
+    for rank in range(w.cp):
+        announce(f"wide scores f32 c0 rank {rank}")
+        R = Rank(w.B, w.Hq, w.Hkv, w.S, w.d, w.cp, rank, "f32", full=wide)
+        assert_close(*R.ring_fwd(), *R.oracle(), "f32", f"wide f32 rank {rank}")
+
+
+# ------------------------------------------------------------------ the stepwise ring's epilogue merge
+@pytest.mark.parametrize("staged", [False, True])
+def test_late_spike_stepwise_bf16(staged):
+    """The ring as separate steps, each merged into the running (O, LSE) in
+    the kernel's epilogue: the planted keys sit in the last step's shard, so
+    the last merge combines LSEs tens of units apart.  Also q drawn 24x
+    wider.  Every row against the oracle."""
+    S, cp, d = 8192, 4, 128
+    base = si.make_qkv(1, 4, 1, S, d, "bf16", seed=35)
+    wide = si.make_qkv(1, 4, 1, S, d, "bf16", seed=36, q_scale=24.0)
+    for rank in range(cp):
+        full, _ = plant_late_spikes(base, S, cp, rank, MARGINS_BF16)
+        for name, inp in (("late spikes", full), ("wide scores", wide)):
+            announce(f"stepwise {name} staged={staged} rank {rank}")
+            R = Rank(1, 4, 1, S, d, cp, rank, "bf16", full=inp)
+            o, lse = cpa.cp_attn_ring_fwd_stepwise(R.q_loc, R.k_all, R.v_all, cp, rank, R.pos, R.lo, R.allp,
+                                                   scale=R.scale, staged=staged)
+            torch.cuda.synchronize()
+            assert_close(o, lse, *R.oracle(), "bf16", f"stepwise {name} rank {rank}")
+
+
+def test_late_spike_stepwise_f32():
+    w = si.WORKLOADS["c0_f32_s1024_cp2"]
+    base = si.make_qkv(w.B, w.Hq, w.Hkv, w.S, w.d, "f32", seed=w.seed)
+    for rank in range(w.cp):
+        full, _ = plant_late_spikes(base, w.S, w.cp, rank, MARGINS_F32)
+        announce(f"stepwise late spikes f32 rank {rank}")
+        R = Rank(w.B, w.Hq, w.Hkv, w.S, w.d, w.cp, rank, "f32", full=full)
+        o, lse = cpa.cp_attn_ring_fwd_stepwise(R.q_loc, R.k_all, R.v_all, w.cp, rank, R.pos, R.lo, R.allp,
+                                               scale=R.scale, staged=True)
+        torch.cuda.synchronize()
+        assert_close(o, lse, *R.oracle(), "f32", f"stepwise f32 rank {rank}")
+
+
+# ------------------------------------------------------------------ backward
+def test_late_spike_ring_bwd():
+    """The ring backward with planted late maxima: every rank's gradients
+    against the oracle's gradients of that rank's loss."""
+    S, cp, d = 8192, 4, 128
+    base = si.make_qkv(1, 4, 1, S, d, "bf16", seed=37, with_dout=True)
+    for rank in range(cp):
+        full, _ = plant_late_spikes(base, S, cp, rank, MARGINS_BF16)
+        announce(f"late spikes ring bwd rank {rank}")
+        R = Rank(1, 4, 1, S, d, cp, rank, "bf16", full=full)
+        o, lse, dq, dk, dv = R.ring_bwd()
+        torch.cuda.synchronize()
+        assert_close(o, lse, *R.oracle(), "bf16", f"late spikes fwd rank {rank}")
+        for name, g, r in zip(("dq", "dk", "dv"), (dq, dk, dv), R.oracle_grads()):
+            e = max_err(g, r)
+            assert np.isfinite(e) and e <= GTOL, f"rank {rank}: {name} max-abs error {e:.3e} > {GTOL}"
