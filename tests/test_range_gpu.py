@@ -37,6 +37,16 @@ pytestmark = pytest.mark.gpu
 GTOL = 5e-2
 MARGINS_BF16 = (8.0, 20.0, 32.0, 45.0, 70.0)
 MARGINS_F32 = (6.0, 9.0, 12.0)
+# The backward's margins stay at 20 or below.  delta = dO . O takes the
+# forward's O, whose P entered the P V product rounded to bf16 (relative error
+# up to 2^-9), and dQ = scale * sum_j dS_ij k_j multiplies that error by the
+# planted key, whose size grows with the margin.  Emulating exactly that
+# rounding (bf16 P in O, bf16 dS) on the 8192-token inputs gives dQ errors of
+# 0.06-0.11 at margins up to 70, past the 5e-2 bar the method's own arithmetic
+# can meet, and 0.003-0.02 at margins up to 20.  A margin of 20 still puts every
+# earlier key of a planted row 20 units under the final LSE: a P recomputed
+# from any stale statistic would be off by a factor near e^20.
+MARGINS_BWD = (6.0, 12.0, 20.0)
 
 
 def plant_late_spikes(full, S, cp, rank, margins, head=0):
@@ -218,7 +228,7 @@ def test_late_spike_ring_bwd():
     S, cp, d = 8192, 4, 128
     base = si.make_qkv(1, 4, 1, S, d, "bf16", seed=37, with_dout=True)
     for rank in range(cp):
-        full, _ = plant_late_spikes(base, S, cp, rank, MARGINS_BF16)
+        full, _ = plant_late_spikes(base, S, cp, rank, MARGINS_BWD)
         announce(f"late spikes ring bwd rank {rank}")
         R = Rank(1, 4, 1, S, d, cp, rank, "bf16", full=full)
         o, lse, dq, dk, dv = R.ring_bwd()
