@@ -102,7 +102,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="llama8b_s128k_cp8")
     ap.add_argument("--ranks", default="all", help="'all' or a comma list of virtual ranks")
-    ap.add_argument("--pass", dest="mode", choices=["fwd", "fwdbwd", "rotate", "a2a"], default="fwdbwd")
+    ap.add_argument("--pass", dest="mode", choices=["fwd", "fwdbwd", "rotate", "a2a", "probe"], default="fwdbwd")
     ap.add_argument("--a2a-groups", default="2,8", help="--pass a2a: comma list of all-to-all group sizes")
     ap.add_argument("--varlen-mode", choices=["stream", "per_doc", "whole_doc"], default="stream",
                     help="how a varlen workload's packed stream is dealt to ranks")
@@ -188,6 +188,85 @@ def calibrate_copy():
     print(json.dumps({"calibrate_copy_bytes": n, "repeats": 3}), flush=True)
 
 
+PROBES = {
+    0: ("mfma", "v_mfma_f32_32x32x16_bf16, 4 independent accumulators per wave"),
+    5: ("mfma_chain", "v_mfma_f32_32x32x16_bf16, one dependent accumulator chain per wave"),
+    1: ("exp", "v_exp_f32, 8 independent chains per lane"),
+    2: ("fma", "v_fma_f32, 8 independent chains per lane"),
+    3: ("mix_same_wave", "per MFMA: 2 FMA + 2 exp + 1 bf16 pack + 2 add, all in every wave"),
+    4: ("mix_split_waves", "the same work, MFMAs in waves 0-3 and the vector part in waves 4-7"),
+    8: ("mfma_agpr", "as mfma, accumulators in AGPRs"),
+    6: ("mix_same_wave_agpr", "as mix_same_wave, MFMA accumulators in AGPRs"),
+    7: ("mix_split_waves_agpr", "as mix_split_waves, MFMA accumulators in AGPRs"),
+}
+
+
+def probe_bench(args):
+    """Unit throughput of one MI355X under the attention kernels' occupancy
+    (one 8-wave workgroup per CU, two waves per SIMD), from the probe kernels
+    of libcpattn_probe.so: sustained bf16 MFMA rate, exp and FMA issue rates,
+    and the forward's MFMA + exponential mix with the two kinds of work in the
+    same waves or in different waves of each SIMD.  Cycles are counted at the
+    sclk sampled during each probe."""
+    import ctypes
+    import numpy as np
+    import torch
+    from context_causal_attention_amd import build as cpb
+    if not os.path.exists(cpb.PROBE_LIB):
+        raise RuntimeError(f"{cpb.PROBE_LIB} is not built; run __graft_entry__.build() first")
+    L = ctypes.CDLL(cpb.PROBE_LIB)
+    L.cp_probe_run.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    blocks = 256
+    out = torch.empty(blocks * 512, device="cuda:0")
+    stream = torch.cuda.current_stream().cuda_stream
+    # iterations per launch, sized for ~20-60 ms per launch
+    iters = {0: 20000, 5: 20000, 8: 20000, 1: 100000, 2: 100000, 3: 40000, 4: 40000, 6: 40000, 7: 40000}
+    res = {}
+    for kind, (name, what) in PROBES.items():
+        def launch():
+            rc = L.cp_probe_run(kind, blocks, iters[kind], ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(stream))
+            if rc != 0:
+                raise RuntimeError(f"probe {name}: hip error {rc}")
+        launch()
+        torch.cuda.synchronize()
+        times = []
+        with ClockSampler(0.01) as clk:
+            for _ in range(max(3, args.steps)):
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record(); launch(); b.record()
+                b.synchronize()
+                times.append(a.elapsed_time(b) / 1e3)
+        t = float(np.median(times))
+        cs = clk.summary()
+        mhz = cs["sclk_mhz"]["median"] if cs.get("sclk_mhz") else None
+        it = iters[kind]
+        per_simd = {}
+        if kind in (0, 5, 8):
+            n = 2 * it * 4 if kind == 5 else 2 * it * 16           # MFMAs per SIMD
+            flop = blocks * 8 * (it * (4 if kind == 5 else 16)) * 32768
+            per_simd = {"mfma_per_simd": n, "TFLOP/s": round(flop / t / 1e12, 1),
+                        "pct_of_2516.6": round(100 * flop / t / 1e12 / PEAK_BF16_TFLOPS, 1)}
+            unit = n
+        elif kind in (1, 2):
+            unit = 2 * it * 32                                      # wave64 instructions per SIMD
+            per_simd = {"instructions_per_simd": unit}
+        else:
+            same = kind in (3, 6)
+            unit = 2 * it * 8 if same else it * 8                   # MFMA steps per SIMD
+            flop = blocks * (8 if same else 4) * it * 8 * 32768
+            per_simd = {"mfma_steps_per_simd": unit, "TFLOP/s": round(flop / t / 1e12, 1)}
+        r = {"what": what, "ms": round(t * 1e3, 3), **per_simd, "sclk_mhz": mhz}
+        if mhz:
+            r["cycles_per_unit"] = round(t * mhz * 1e6 / unit, 2)
+        res[name] = r
+        print(f"[probe] {name}: {r}", file=sys.stderr, flush=True)
+    line = {"metric": "unit throughput probes (one 8-wave workgroup per CU)", "value": res["mfma"]["TFLOP/s"],
+            "unit": "TFLOP/s (sustained bf16 MFMA)", "n_gpus": 1, "steps": max(3, args.steps), "warmup": 1,
+            "higher_is_better": True, "dtype": "bf16", "data": "synthetic", "config": {"workload": "probe"},
+            "probes": res}
+    print(json.dumps(line), flush=True)
+
+
 def main():
     args = parse()
     if args.calibrate_copy:
@@ -204,6 +283,9 @@ def main():
     import context_causal_attention_amd as cpa
     import seeded_inputs as si
 
+    if args.mode == "probe":
+        probe_bench(args)
+        return
     w = si.WORKLOADS[args.workload]
     if args.mode == "rotate":
         rotate_bench(args, w)

@@ -14,6 +14,10 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OBJDIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libcpattn.so")
+# Unit-throughput probes for the measurement harness (bench.py --pass probe);
+# not part of the C ABI.
+PROBE_LIB = os.path.join(PKG, "libcpattn_probe.so")
+PROBE_SOURCES = ["probe.hip"]
 
 ARCH = "gfx950"
 SOURCES = ["index.cpp", "api.cpp", "attn_fwd.hip", "attn_bwd.hip", "merge.hip", "a2a.hip"]
@@ -60,6 +64,12 @@ def build(verbose: bool = False) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"linking libcpattn.so failed:\n{r.stdout}{r.stderr}")
     os.replace(tmp, LIB)
+    pobjs = [_compile(s, verbose) for s in PROBE_SOURCES]
+    r = subprocess.run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", PROBE_LIB + ".tmp", *pobjs],
+                       capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"linking libcpattn_probe.so failed:\n{r.stdout}{r.stderr}")
+    os.replace(PROBE_LIB + ".tmp", PROBE_LIB)
     return LIB
 
 

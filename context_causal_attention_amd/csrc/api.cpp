@@ -133,7 +133,7 @@ FwdWorkspace fwd_workspace_layout(int32_t b, int32_t hkv, int32_t d, int64_t sk,
   if (in_dtype == CP_BF16) off += align_up((size_t)ntiles * tk * 4, 256);
   w.vt_off = off;
   w.vt_row = ntiles * tk;
-  if (in_dtype == CP_BF16) off += align_up((size_t)b * hkv * d * (size_t)w.vt_row * 2, 256);
+  if (fwd_wide_keys(in_dtype, sk)) off += align_up((size_t)b * hkv * d * (size_t)w.vt_row * 2, 256);
   w.total = off < 256 ? 256 : off;
   return w;
 }
@@ -194,8 +194,11 @@ int prep_fwd(const cp_shape* s, int32_t cp, int32_t rank, const void* q, const v
   if (s->o_str[2] < s->d) return fail(CP_EINVAL, "o row stride %lld is smaller than d", (long long)s->o_str[2]);
   if (s->sk > 0 && (s->k_str[2] < s->d || s->v_str[2] < s->d))
     return fail(CP_EINVAL, "k/v row strides must be at least d");
-  // The bf16 kernel addresses one (batch, kv head) of K with 32-bit buffer offsets.
-  if (s->in_dtype == CP_BF16 && (double)s->sk * (double)s->k_str[2] * 2.0 >= 4294967040.0)
+  // The bf16 kernel addresses one (batch, kv head) of K and of V with 32-bit
+  // buffer offsets.
+  if (s->in_dtype == CP_BF16 &&
+      ((double)s->sk * (double)s->k_str[2] * 2.0 >= 4294967040.0 ||
+       (double)s->sk * (double)s->v_str[2] * 2.0 >= 4294967040.0))
     return fail(CP_EINVAL, "key rows x row stride exceed the 4 GiB reach of one buffer descriptor");
   // Listed key tiles carry the ring rank in 8 bits and the tile index within
   // the rank's shard in 16 bits.
@@ -203,8 +206,8 @@ int prep_fwd(const cp_shape* s, int32_t cp, int32_t rank, const void* q, const v
   if ((s->sk / cp + tile_keys(s->in_dtype) - 1) / tile_keys(s->in_dtype) > 65535)
     return fail(CP_EINVAL, "a shard of %lld key rows has more than 65535 key tiles", (long long)(s->sk / cp));
   const FwdWorkspace w = fwd_workspace_layout(s->b, s->hkv, s->d, s->sk, cp, s->in_dtype);
-  // So does its V^T copy: d rows over every key slot of the padded tiles.
-  if (s->in_dtype == CP_BF16 && (double)s->d * (double)w.vt_row * 2.0 >= 4294967040.0)
+  // So does the wide launch's V^T copy: d rows over every key slot of the padded tiles.
+  if (fwd_wide_keys(s->in_dtype, s->sk) && (double)s->d * (double)w.vt_row * 2.0 >= 4294967040.0)
     return fail(CP_EINVAL, "%lld key rows exceed the 4 GiB reach of one buffer descriptor for V^T", (long long)s->sk);
   if (!ws) return fail(CP_EWORKSPACE, "workspace is null (%zu bytes needed)", w.total);
   if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0) return fail(CP_EWORKSPACE, "workspace is not 256-byte aligned");

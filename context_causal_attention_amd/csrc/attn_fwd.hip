@@ -62,7 +62,7 @@ constexpr float kRescaleLog2 = 8.0f;    // keep a stale running max while scores
 struct KParams {
   const char* q;
   const char* k;
-  const char* v;            // bf16: V^T in the workspace; fp32: V itself
+  const char* v;
   const int* q_pos;
   const int* q_lo;          // may be null
   const int* k_pos;
@@ -72,7 +72,7 @@ struct KParams {
   float* lse;
   long long q_sb, q_sh, q_ss;
   long long k_sb, k_sh, k_ss;
-  long long v_sb, v_sh, v_ss;  // fp32 V strides; for bf16 V^T: v_ss = row length, v_sh = d * v_ss
+  long long v_sb, v_sh, v_ss;
   long long o_sb, o_sh, o_ss;
   int B, Hq, Hkv, sq, sk, cp, rank, R, tpr, n_qtiles, out_bf16;
   int merge_acc;            // 1: (o, lse) hold a partial result over other keys (fp32) to merge into
@@ -156,34 +156,73 @@ __device__ __forceinline__ void store_out(const KParams& p, const Item& it, int 
 // ============================================================================
 // bf16 kernel
 // ============================================================================
-template <int D, int NW>
+template <int D>
 struct Bf16Cfg {
   static constexpr int BN = kTileKeysBf16;       // keys per tile
-  static constexpr int KROW = D * 2;             // bytes per K row in LDS
-  static constexpr int KCHR = D / 8;             // 16-byte chunks per K row
-  static constexpr int VROW = BN * 2;            // bytes per V^T row in LDS (128)
-  static constexpr int VCHR = BN / 8;            // 8
-  static constexpr int KBYTES = BN * KROW;
-  static constexpr int VBYTES = D * VROW;
-  static constexpr int KPW = KBYTES / 1024 / NW;  // 1 KB DMA blocks per wave
-  static constexpr int VPW = VBYTES / 1024 / NW;
+  static constexpr int ROW = D * 2;              // bytes per K (or row-major V) row in LDS
+  static constexpr int CHR = D / 8;              // 16-byte chunks per such row
+  static constexpr int TROW = BN * 2;            // bytes per V^T row in LDS (transposed layout)
+  static constexpr int TCHR = BN / 8;            // 16-byte chunks per V^T row
+  static constexpr int TILE = BN * ROW;          // bytes per K or V tile (either layout)
+  static constexpr int NBLK = TILE / 1024;       // 1 KB copy blocks per tile
   static constexpr int QREG = D / 16;
   static constexpr int DT = D / 32;
-  static_assert(KPW >= 1 && VPW >= 1, "tile too small for the DMA split");
 };
 
+// Copies 16 bytes per lane from buffer rs at byte offset voff + soff into LDS
+// at lds + 16 * lane (one 1 KB block per wave), or 4 bytes per lane into
+// lds + 4 * lane (copy_lds4).  Written as inline assembly so that the
+// compiler neither tracks these copies nor inserts waits for them: every wait
+// for them in this file is an explicit vmcnt (its alias tracking otherwise
+// makes some LDS reads wait for copies issued just before them).  The block
+// sets M0 (the LDS base), gives the load the one wait state an M0 write needs
+// before it, and puts M0 back, so the compiler's M0 survives; it has no
+// register results.
+__device__ __forceinline__ void copy_lds16(__amdgpu_buffer_rsrc_t rs, int voff, int soff, unsigned lds) {
+  unsigned saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %2, %3, %4 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds), "v"(voff), "s"(rs), "s"(soff)
+      : "memory");
+}
+__device__ __forceinline__ void copy_lds4(__amdgpu_buffer_rsrc_t rs, int voff, unsigned lds) {
+  unsigned saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dword %2, %3, 0 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds), "v"(voff), "s"(rs)
+      : "memory");
+}
+__device__ __forceinline__ unsigned lds_addr(const void* p) {
+  return (unsigned)(size_t)(const __attribute__((address_space(3))) char*)p;
+}
+
 // NW waves of 32 query rows each; two waves share each SIMD (NW = 8: one
-// workgroup per CU; NW = 4: two).
-template <int D, int NW>
+// workgroup per CU; NW = 4: two).  VT: V is read from the transposed copy the
+// prep kernel writes into the workspace ([d][keys] tiles, one 16-byte LDS read
+// per V^T operand); otherwise from V itself, row-major tiles read transposed
+// by ds_read_b64_tr_b16 (two 8-byte reads per operand, no copy of V).
+template <int D, int NW, bool VT>
 __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(KParams p) {
   // The body uses device-only buffer-descriptor types; the host pass only needs
   // the launch stub.
 #if defined(__HIP_DEVICE_COMPILE__)
-  using C = Bf16Cfg<D, NW>;
-  __shared__ __attribute__((aligned(1024))) char sK0[C::KBYTES];
-  __shared__ __attribute__((aligned(1024))) char sK1[C::KBYTES];
-  __shared__ __attribute__((aligned(1024))) char sV0[C::VBYTES];
-  __shared__ __attribute__((aligned(1024))) char sV1[C::VBYTES];
+  using C = Bf16Cfg<D>;
+  constexpr int BPW = C::NBLK / NW;  // 1 KB blocks of a K or V tile per wave
+  static_assert(BPW >= 1 && C::NBLK % NW == 0, "copy split");
+  __shared__ __attribute__((aligned(1024))) char sK0[C::TILE];
+  __shared__ __attribute__((aligned(1024))) char sK1[C::TILE];
+  __shared__ __attribute__((aligned(1024))) char sV0[C::TILE];
+  __shared__ __attribute__((aligned(1024))) char sV1[C::TILE];
   __shared__ __attribute__((aligned(16))) int sP0[C::BN];
   __shared__ __attribute__((aligned(16))) int sP1[C::BN];
   __shared__ int2 sList[kListCap];
@@ -215,67 +254,105 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(KParams p) {
   __syncthreads();
 
   // ---- per-lane constant addresses ------------------------------------------
-  // DMA: this lane's 16-byte slot in each of the wave's 1 KB blocks.
+  // Copies: each wave fills blocks wave, wave + NW, ... of every K and V tile;
+  // lane l of a block fills the block's 16-byte physical slot l, holding the
+  // logical chunk the row's swizzle maps there.
   const long long k_row_bytes = p.k_ss * 2;
-  int voffK[C::KPW], voffV[C::VPW];
+  const long long v_row_bytes = p.v_ss * 2;
+  int voffK[BPW], voffV[BPW];
 #pragma unroll
-  for (int j = 0; j < C::KPW; ++j) {
-    const int c = (wave + NW * j) * 64 + lane;  // physical chunk index within the K tile
-    const int r = c / C::KCHR, ph = c % C::KCHR;
-    voffK[j] = (int)(r * k_row_bytes) + 16 * swz<C::KCHR>(r, ph);
+  for (int j = 0; j < BPW; ++j) {
+    const int c = (wave + NW * j) * 64 + lane;  // physical 16-byte slot of the tile
+    {
+      const int r = c / C::CHR, ph = c % C::CHR;
+      voffK[j] = (int)(r * k_row_bytes) + 16 * swz<C::CHR>(r, ph);
+      if constexpr (!VT) voffV[j] = (int)(r * v_row_bytes) + 16 * swz_t<C::CHR>(r, ph);
+    }
+    if constexpr (VT) {
+      const int r = c / C::TCHR, ph = c % C::TCHR;  // V^T: row d, chunk of 8 keys
+      voffV[j] = (int)(r * v_row_bytes) + 16 * swz<C::TCHR>(r, ph);
+    }
   }
-  const long long vt_row_bytes = p.v_ss * 2;
-#pragma unroll
-  for (int j = 0; j < C::VPW; ++j) {
-    const int c = (wave + NW * j) * 64 + lane;
-    const int r = c / C::VCHR, ph = c % C::VCHR;
-    voffV[j] = (int)(r * vt_row_bytes) + 16 * swz<C::VCHR>(r, ph);
-  }
-  // LDS reads: K operand rows key_perm(l32) (+32 for the second sub-tile),
-  // V^T operand rows l32 (+32 per output tile).
+  // K operand reads: rows key_perm(l32) (+32 for the second sub-tile), logical
+  // chunk 2kk + hi of the row-swizzled K tile.
   const int krow = key_perm(l32);
   int kaddr[C::QREG];
 #pragma unroll
-  for (int kk = 0; kk < C::QREG; ++kk) kaddr[kk] = krow * C::KROW + 16 * swz<C::KCHR>(krow, 2 * kk + hi);
-  int vaddr[4];
+  for (int kk = 0; kk < C::QREG; ++kk) kaddr[kk] = krow * C::ROW + 16 * swz<C::CHR>(krow, 2 * kk + hi);
+  // V^T operand of key group kg (16 keys) and output tile t (32 columns of d):
+  //  - VT: V^T row 32t + l32 (a column of d), chunk 2kg + hi (8 keys): one
+  //    16-byte read at vaddr[kg] + t*32*TROW;
+  //  - row-major: lane s16 of its 16-lane group reads key 16kg + 8hi + 4h +
+  //    s16/4 at column 32t + 16*(bit 4 of lane) + 4*(s16%4) (h = 0, 1: two
+  //    8-byte transposing reads), so the lane receives column 32t + l32 at
+  //    keys 16kg + 8hi .. +7; byte offset xo[t] (+ xd for h = 1) + 16kg*ROW.
+  int vaddr[VT ? 4 : 1], xo[VT ? 1 : C::DT], xd = 0;
+  if constexpr (VT) {
 #pragma unroll
-  for (int kg = 0; kg < 4; ++kg) vaddr[kg] = l32 * C::VROW + 16 * swz<C::VCHR>(l32, 2 * kg + hi);
+    for (int kg = 0; kg < 4; ++kg) vaddr[kg] = l32 * C::TROW + 16 * swz<C::TCHR>(l32, 2 * kg + hi);
+  } else {
+    const int s16 = lane & 15;
+    const int cl = 2 * ((lane >> 4) & 1) + ((s16 & 3) >> 1);
+    int tP[2], tA = 0;
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const int r = 8 * hi + 4 * hh + (s16 >> 2);
+      const int f = swz_t<C::CHR>(r, 0);
+      tP[hh] = r * C::ROW + 16 * (cl ^ (f & 3)) + 8 * (s16 & 1);
+      tA = 64 * (f >> 2);
+    }
+#pragma unroll
+    for (int t = 0; t < C::DT; ++t) xo[t] = tP[0] + ((64 * t) ^ tA);
+    xd = tP[1] - tP[0];
+  }
 
   const char* kbase = p.k + ((long long)it.b * p.k_sb + (long long)it.kvh * p.k_sh) * 2;
-  const char* vtbase = p.v + ((long long)it.b * p.v_sb + (long long)it.kvh * p.v_sh) * 2;
-  const __amdgpu_buffer_rsrc_t rsV =
-      __builtin_amdgcn_make_buffer_rsrc((void*)vtbase, 0, (int)(D * vt_row_bytes), kBufferFlags);
+  const char* vbase = p.v + ((long long)it.b * p.v_sb + (long long)it.kvh * p.v_sh) * 2;
+  // V^T: one descriptor over this (batch, kv head)'s whole copy (d rows).
+  const __amdgpu_buffer_rsrc_t rsVT =
+      __builtin_amdgcn_make_buffer_rsrc((void*)vbase, 0, VT ? (int)(D * v_row_bytes) : 0, kBufferFlags);
   const __amdgpu_buffer_rsrc_t rsP =
       __builtin_amdgcn_make_buffer_rsrc((void*)p.kpos_pad, 0, 0x7fffffff, kBufferFlags);
 
-  // List entry: src | i << 8 | class(wave w) << (24 + 2w) for key tile i of
-  // rank src's shard (tile id src * tpr + i).
-  auto tile_of = [&](int e) { return (e & 0xFF) * p.tpr + ((e >> 8) & 0xFFFF); };
-  // Copies K of list entry e (uniform) into LDS buffer `buf` (static).
-  auto issue_k = [&](auto bufc, int e) {
-    constexpr int buf = decltype(bufc)::value;
-    char* sK = buf ? sK1 : sK0;
+  auto kbuf = [&](auto bc) -> char* { if constexpr (decltype(bc)::value) return sK1; else return sK0; };
+  auto vbuf = [&](auto bc) -> char* { if constexpr (decltype(bc)::value) return sV1; else return sV0; };
+  auto pbuf = [&](auto bc) -> int* { if constexpr (decltype(bc)::value) return sP1; else return sP0; };
+  // List entry .x: src | i << 8 for key tile i of rank src's shard (tile id
+  // src * tpr + i); .y: class of wave w in bits 2w, 2w+1.
+  auto rows_of = [&](int e, int& r0, int& nval) {
     const int src = e & 0xFF, i = (e >> 8) & 0xFFFF;
-    const int r0 = src * p.R + i * C::BN;
-    const int nval = min(C::BN, p.R - i * C::BN);
-    const __amdgpu_buffer_rsrc_t rsK = __builtin_amdgcn_make_buffer_rsrc(
+    r0 = src * p.R + i * C::BN;
+    nval = min(C::BN, p.R - i * C::BN);
+  };
+  // Copies this wave's share of K of list entry e into buffer bc.  Each tile
+  // gets a descriptor whose record count ends at the shard's last valid row, so
+  // rows past it read as zero.
+  auto issue_k = [&](auto bc, int e) {
+    int r0, nval;
+    rows_of(e, r0, nval);
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(kbase + (long long)r0 * k_row_bytes), 0, (int)(nval * k_row_bytes), kBufferFlags);
 #pragma unroll
-    for (int j = 0; j < C::KPW; ++j)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsK, (lds_ptr_t)(sK + (wave + NW * j) * 1024), 16, voffK[j], 0, 0, 0);
+    for (int j = 0; j < BPW; ++j) copy_lds16(rs, voffK[j], 0, lds_addr(kbuf(bc) + (wave + NW * j) * 1024));
   };
-  // Copies V^T and the key positions of list entry e into LDS buffer `buf`.
-  auto issue_v = [&](auto bufc, int e) {
-    constexpr int buf = decltype(bufc)::value;
-    char* sV = buf ? sV1 : sV0;
-    int* sP = buf ? sP1 : sP0;
-    const int tile = tile_of(e);
+  // Copies this wave's share of V (or V^T: the tile's 64 key columns, zero in
+  // the padding of a shard's last tile) of entry e into buffer bc, and (wave
+  // 0) the tile's key positions, padding slots kInvalidKey.
+  auto issue_v = [&](auto bc, int e) {
+    const int tile = (e & 0xFF) * p.tpr + ((e >> 8) & 0xFFFF);
+    if constexpr (VT) {
 #pragma unroll
-    for (int j = 0; j < C::VPW; ++j)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsV, (lds_ptr_t)(sV + (wave + NW * j) * 1024), 16, voffV[j],
-                                               tile * C::BN * 2, 0, 0);
-    if (wave == 0)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsP, (lds_ptr_t)sP, 4, lane * 4, tile * C::BN * 4, 0, 0);
+      for (int j = 0; j < BPW; ++j)
+        copy_lds16(rsVT, voffV[j], tile * C::BN * 2, lds_addr(vbuf(bc) + (wave + NW * j) * 1024));
+    } else {
+      int r0, nval;
+      rows_of(e, r0, nval);
+      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(vbase + (long long)r0 * v_row_bytes), 0, (int)(nval * v_row_bytes), kBufferFlags);
+#pragma unroll
+      for (int j = 0; j < BPW; ++j) copy_lds16(rs, voffV[j], 0, lds_addr(vbuf(bc) + (wave + NW * j) * 1024));
+    }
+    if (wave == 0) copy_lds4(rsP, tile * C::BN * 4 + lane * 4, lds_addr(pbuf(bc)));
   };
 
   // ---- online softmax state ------------------------------------------------
@@ -292,11 +369,11 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(KParams p) {
   float m_run = -INFINITY;
   float l_run = 0.f;
   constexpr float kRedo = 1099511627776.0f;  // 2^40
+  bf16x8 pb[4];  // P^T of the current tile, bf16: the B operands of its P V MFMAs
 
-  // S^T = K Q^T of the tile in K buffer kb: 16 MFMAs into (s0, s1).
+  // S^T = K Q^T of the tile in K buffer kbc: 16 MFMAs into (s0, s1).
   auto scores = [&](auto kbc, f32x16& s0, f32x16& s1) {
-    constexpr int kb = decltype(kbc)::value;
-    const char* sK = kb ? sK1 : sK0;
+    const char* sK = kbuf(kbc);
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       s0[r] = 0.f;
@@ -305,14 +382,14 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(KParams p) {
 #pragma unroll
     for (int kk = 0; kk < C::QREG; ++kk) {
       const bf16x8 a = *reinterpret_cast<const bf16x8*>(sK + kaddr[kk]);
-      const bf16x8 b = *reinterpret_cast<const bf16x8*>(sK + kaddr[kk] + 32 * C::KROW);
+      const bf16x8 b = *reinterpret_cast<const bf16x8*>(sK + kaddr[kk] + 32 * C::ROW);
       s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[kk], s0, 0, 0, 0);
       s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b, qreg[kk], s1, 0, 0, 0);
     }
   };
   // P = exp2(c2*s - m) of group kg (8 keys) rounded to bf16; the fp32 values
   // go into the tile's row sum (the LSE needs them unrounded).
-  auto expg = [&](const f32x16& c0, const f32x16& c1, int kg, float nm, bf16x8& pb, float& lj) {
+  auto expg = [&](const f32x16& c0, const f32x16& c1, int kg, float nm, bf16x8& pbk, float& lj) {
     const f32x16& sv = kg < 2 ? c0 : c1;
     const int base = 8 * (kg & 1);
 #pragma unroll
@@ -321,18 +398,16 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(KParams p) {
       const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[base + j + 1], p.c2, nm));
       const bf16x2 pr = __builtin_convertvector((f32x2){e0, e1}, bf16x2);
       lj += e0 + e1;
-      pb[j] = pr[0];
-      pb[j + 1] = pr[1];
+      pbk[j] = pr[0];
+      pbk[j + 1] = pr[1];
     }
   };
 
-  // One pipeline stage: tile j's scores (c0, c1) are masked, exponentiated
-  // and multiplied into O (V^T from buffer vb) while tile j+1's scores are
-  // computed into (n0, n1) from K buffer kb.
+  // One tile: its scores (c0, c1) are masked (key positions in buffer vbc),
+  // exponentiated into pb while the next tile's scores are computed into (n0,
+  // n1) from K buffer kbc, then multiplied into O with V from buffer vbc.
   auto stage = [&](auto kbc, auto vbc, f32x16& c0, f32x16& c1, f32x16& n0, f32x16& n1, int cls_cur) {
-    constexpr int vb = decltype(vbc)::value;
-    const char* sV = vb ? sV1 : sV0;
-    const int* sP = vb ? sP1 : sP0;
+    const int* sP = pbuf(vbc);
     // Register r of sub-tile sub holds key 32*sub + 16*(r/8) + 8*hi + r%8.
     if (cls_cur == kPartial) {
 #pragma unroll
@@ -352,26 +427,24 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(KParams p) {
     // One straight-line block: the next tile's scores are computed even when
     // there is no next tile or this wave skips it, and this tile's
     // exponentials even when this wave skips it; such results go unused.
-    bf16x8 pb[4];
     float lj = 0.f;
     const float nm = -m_run;
     {
       // 16 chunks, fenced from each other: chunk m reads the K operand of MFMA
       // m+4, issues MFMA m of the next tile's scores (sub-tile m%2, d-slice
       // m/2), and exponentiates scores 2m, 2m+1 of this tile.
-      constexpr int kb = decltype(kbc)::value;
-      const char* sK = kb ? sK1 : sK0;
+      const char* sK = kbuf(kbc);
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         n0[r] = 0.f;
         n1[r] = 0.f;
       }
       auto kop = [&](int m) {
-        return *reinterpret_cast<const bf16x8*>(sK + kaddr[m >> 1] + (m & 1) * 32 * C::KROW);
+        return *reinterpret_cast<const bf16x8*>(sK + kaddr[m >> 1] + (m & 1) * 32 * C::ROW);
       };
-      // Issue priority 1 for this block, 0 again from the P V MFMAs on: while
-      // one wave interleaves scores and exponentials, the SIMD's other wave
-      // fills the gaps (1-2% faster than equal priority throughout).
+      // Issue priority 1 for this block, 0 again for the P V MFMAs: while one
+      // wave interleaves scores and exponentials, the SIMD's other wave fills
+      // the gaps.
       __builtin_amdgcn_s_setprio(1);
       constexpr int NM = 2 * C::QREG;  // MFMAs per tile
       constexpr int PF = 4;            // operand reads in flight
@@ -427,28 +500,46 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(KParams p) {
     }
     l_run += lj;
     __builtin_amdgcn_s_setprio(0);
-    // O^T += V^T P^T
-    bf16x8 va[C::DT];
-#pragma unroll
-    for (int t = 0; t < C::DT; ++t) va[t] = *reinterpret_cast<const bf16x8*>(sV + vaddr[0] + t * 32 * C::VROW);
-#pragma unroll
-    for (int kg = 0; kg < 4; ++kg) {
-#pragma unroll
-      for (int t = 0; t < C::DT; ++t) {
-        oacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[t], pb[kg], oacc[t], 0, 0, 0);
-        if (kg < 3) va[t] = *reinterpret_cast<const bf16x8*>(sV + vaddr[kg + 1] + t * 32 * C::VROW);
+    // O^T += V^T P^T in 16 fenced chunks: chunk m reads the V^T operand of
+    // MFMA m+PF (key group (m+PF)/DT, output tile (m+PF)%DT) and issues MFMA
+    // m, so every MFMA finds its operand read PF MFMAs earlier (left to
+    // itself the compiler reads each pair just before use, which exposes the
+    // LDS latency on every pair).
+    const char* sV = vbuf(vbc);
+    constexpr int NMV = 4 * C::DT;  // P V MFMAs per tile
+    constexpr int PFV = 4;
+    auto vop = [&](int m) {
+      const int kg = m / C::DT, t = m % C::DT;
+      if constexpr (VT) {
+        return *reinterpret_cast<const bf16x8*>(sV + vaddr[kg] + t * 32 * C::TROW);
+      } else {
+        const lds_char* g = to_lds(const_cast<char*>(sV)) + kg * 16 * C::ROW;
+        return lds_read_tr(g + xo[t], g + (xo[t] + xd));
       }
+    };
+    bf16x8 va[NMV];
+#pragma unroll
+    for (int m = 0; m < PFV; ++m) va[m] = vop(m);
+#pragma unroll
+    for (int m = 0; m < NMV; ++m) {
+      if (m + PFV < NMV) va[m + PFV] = vop(m + PFV);
+      oacc[m % C::DT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[m], pb[m / C::DT], oacc[m % C::DT], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
   // ---- walk the ring: list the needed key tiles, then stream them ---------
-  // Iteration j reads K of tile j+1 and V^T of tile j while tile j+2's K and
-  // tile j+1's V^T are copied in; buffers alternate, so the loop is unrolled
-  // by two with static buffer and register roles.
+  // Iteration j reads K of tile j+1 and V of tile j while tile j+2's K and
+  // tile j+1's V are copied in; buffers alternate, so the loop is unrolled by
+  // two with static buffer and register roles.  Each copy has the iteration
+  // to land: every wave waits for its own copies at the end of the iteration,
+  // before the barrier after which any wave reads them.
   f32x16 sa0, sa1, sb0, sb1;
   const int total = p.cp * p.tpr;
   const int csh = 2 * wave;
   auto cls_of = [&](int2 e) { return (int)(((unsigned)e.y >> csh) & 3); };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
   for (int u0 = 0; u0 < total; u0 += kListCap) {
     const int cnt = build_key_list<C::BN, NW>(p.bounds, p.tpr, p.R, p.rank, p.cp, u0, min(total, u0 + kListCap), tid,
                                                   wave, lane, sWb, sList, sCnt);
@@ -463,32 +554,32 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(KParams p) {
       return e;
     };
     int2 e_cur = entry(0), e_nxt = entry(1);
-    issue_k(std::integral_constant<int, 0>{}, e_cur.x);
-    issue_v(std::integral_constant<int, 0>{}, e_cur.x);
-    if (cnt > 1) issue_k(std::integral_constant<int, 1>{}, e_nxt.x);
+    issue_k(I0{}, e_cur.x);
+    issue_v(I0{}, e_cur.x);
+    if (cnt > 1) issue_k(I1{}, e_nxt.x);
     wait_vmem();
     __syncthreads();
-    if (cls_of(e_cur) != kSkip) scores(std::integral_constant<int, 0>{}, sa0, sa1);
+    if (cls_of(e_cur) != kSkip) scores(I0{}, sa0, sa1);
     __syncthreads();
     for (int j = 0;;) {
-      // K of tile j+1 in buffer 1, V^T of tile j in buffer 0; scores of tile j in sa.
+      // K of tile j+1 in buffer 1, V of tile j in buffer 0; scores of tile j in sa.
       {
         const int2 e2 = entry(j + 2);
-        if (j + 2 < cnt) issue_k(std::integral_constant<int, 0>{}, e2.x);
-        if (j + 1 < cnt) issue_v(std::integral_constant<int, 1>{}, e_nxt.x);
-        stage(std::integral_constant<int, 1>{}, std::integral_constant<int, 0>{}, sa0, sa1, sb0, sb1, cls_of(e_cur));
+        if (j + 2 < cnt) issue_k(I0{}, e2.x);
+        if (j + 1 < cnt) issue_v(I1{}, e_nxt.x);
+        stage(I1{}, I0{}, sa0, sa1, sb0, sb1, cls_of(e_cur));
         wait_vmem();
         __syncthreads();
         e_cur = e_nxt;
         e_nxt = e2;
       }
       if (++j >= cnt) break;
-      // K of tile j+1 in buffer 0, V^T of tile j in buffer 1; scores of tile j in sb.
+      // K of tile j+1 in buffer 0, V of tile j in buffer 1; scores of tile j in sb.
       {
         const int2 e2 = entry(j + 2);
-        if (j + 2 < cnt) issue_k(std::integral_constant<int, 1>{}, e2.x);
-        if (j + 1 < cnt) issue_v(std::integral_constant<int, 0>{}, e_nxt.x);
-        stage(std::integral_constant<int, 0>{}, std::integral_constant<int, 1>{}, sb0, sb1, sa0, sa1, cls_of(e_cur));
+        if (j + 2 < cnt) issue_k(I1{}, e2.x);
+        if (j + 1 < cnt) issue_v(I0{}, e_nxt.x);
+        stage(I0{}, I1{}, sb0, sb1, sa0, sa1, cls_of(e_cur));
         wait_vmem();
         __syncthreads();
         e_cur = e_nxt;
@@ -673,11 +764,13 @@ __global__ __launch_bounds__(kF32Threads, 1) void fwd_f32_kernel(KParams p) {
   if (valid) store_out<C::DT>(p, it, row, hi, m_run, l_tot, oacc);
 }
 
-// Per key tile: position bounds and count of valid rows.  For bf16 inputs also
-// the key positions padded per tile slot and V transposed into the workspace
+// Per key tile: position bounds {min pos, max pos, widest gap lo, gap hi}; for
+// bf16 inputs also the key positions padded per tile slot (kInvalidKey in the
+// padding of a shard's last tile), which the kernel copies into LDS with each
+// tile for its per-element masks.  VT: also V transposed into the workspace
 // ([b][kv head][d][tile * BN + key], zero in the padding of a shard's last
-// tile) so the kernel above can read V^T rows.
-template <bool BF16, int D>
+// tile), which the wide launch reads as V^T tiles.
+template <bool BF16, int D, bool VT>
 __global__ __launch_bounds__(256) void prep_kernel(const int* __restrict__ k_pos, const char* __restrict__ v,
                                                    long long v_sb, long long v_sh, long long v_ss, int Hkv,
                                                    int R, int tpr, int4* __restrict__ bounds,
@@ -698,7 +791,7 @@ __global__ __launch_bounds__(256) void prep_kernel(const int* __restrict__ k_pos
     if (tid == 0) bounds[tile] = int4{mn, mx, gp.x, gp.y};
     if (BF16 && tid < BN) kpos_pad[tile * BN + tid] = ok ? kp : kInvalidKey;
   }
-  if constexpr (BF16) {
+  if constexpr (VT) {
     __shared__ __bf16 s[BN][D + 8];
     const int b = blockIdx.y / Hkv, kvh = blockIdx.y % Hkv;
     const char* vb = v + ((long long)b * v_sb + (long long)kvh * v_sh) * 2;
@@ -728,13 +821,27 @@ hipError_t launch_t(const FwdArgs& a, hipStream_t stream) {
   int4* bounds = reinterpret_cast<int4*>(ws + w.bounds_off);
   int* kpos_pad = reinterpret_cast<int*>(ws + w.kpos_off);
   __bf16* vt = reinterpret_cast<__bf16*>(ws + w.vt_off);
+  // Launch shape of the bf16 kernel (the same result bits either way):
+  //  - dense causal rings of >= 65536 keys (every row sees many keys): 8
+  //    waves share each tile copy (one workgroup per CU), and V is read from
+  //    a transposed copy (one 16-byte LDS read per V^T operand instead of two
+  //    transposing reads; 2% faster at 131072 keys, prep pass included);
+  //  - shorter rings and document masks (rows see fewer keys): two 4-wave
+  //    workgroups per CU, whose barriers stay apart, reading V itself (no
+  //    prep pass: 8-10% faster on the packed-document workloads).
+  const bool wide = BF16 && a.q_lo == nullptr && fwd_wide_keys(a.in_dtype, a.sk);
   const int ntiles = a.cp * a.tiles_per_rank;
   if (ntiles > 0) {
-    dim3 grid(ntiles, BF16 ? a.b * a.hkv : 1);
-    hipLaunchKernelGGL((prep_kernel<BF16, D>), grid, dim3(256), 0, stream, a.k_pos,
-                       static_cast<const char*>(a.v), (long long)a.v_str[0], (long long)a.v_str[1],
-                       (long long)a.v_str[2], a.hkv, a.rows_per_rank, a.tiles_per_rank, bounds, kpos_pad, vt,
-                       (long long)w.vt_row);
+    const dim3 grid(ntiles, wide ? a.b * a.hkv : 1);
+    const long long vs[3] = {a.v_str[0], a.v_str[1], a.v_str[2]};
+    if (wide)
+      hipLaunchKernelGGL((prep_kernel<BF16, D, true>), grid, dim3(256), 0, stream, a.k_pos,
+                         static_cast<const char*>(a.v), vs[0], vs[1], vs[2], a.hkv, a.rows_per_rank,
+                         a.tiles_per_rank, bounds, kpos_pad, vt, (long long)w.vt_row);
+    else
+      hipLaunchKernelGGL((prep_kernel<BF16, D, false>), grid, dim3(256), 0, stream, a.k_pos,
+                         static_cast<const char*>(a.v), vs[0], vs[1], vs[2], a.hkv, a.rows_per_rank,
+                         a.tiles_per_rank, bounds, kpos_pad, vt, (long long)w.vt_row);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -754,7 +861,7 @@ hipError_t launch_t(const FwdArgs& a, hipStream_t stream) {
   p.k_sb = a.k_str[0];
   p.k_sh = a.k_str[1];
   p.k_ss = a.k_str[2];
-  if constexpr (BF16) {
+  if (wide) {  // V^T copy: [b][hkv][d][vt_row]
     p.v = reinterpret_cast<const char*>(vt);
     p.v_ss = w.vt_row;
     p.v_sh = (long long)D * w.vt_row;
@@ -781,20 +888,13 @@ hipError_t launch_t(const FwdArgs& a, hipStream_t stream) {
   p.merge_acc = a.merge_acc;
   p.c2 = a.scale_log2;
   if constexpr (BF16) {
-    // Wave count of the bf16 kernel (results are the same bits either way):
-    // 8 waves share each K/V tile copy, the better choice when every row sees
-    // many keys (dense causal rings of >= 65536 keys, 1% faster at 131072);
-    // two 4-wave workgroups per CU keep their barriers apart, better for
-    // shorter rings (1.5% at 32768 keys) and for document masks, whose rows
-    // see few keys (4-10%).
-    const bool wide = a.q_lo == nullptr && a.sk >= 65536;
     const int nw = wide ? 8 : 4;
     p.n_qtiles = (a.sq + nw * kRowsPerWave - 1) / (nw * kRowsPerWave);
     const long long nblk = (long long)p.n_qtiles * a.hq * a.b;
     if (wide)
-      hipLaunchKernelGGL((fwd_bf16_kernel<D, 8>), dim3((unsigned)nblk), dim3(8 * 64), 0, stream, p);
+      hipLaunchKernelGGL((fwd_bf16_kernel<D, 8, true>), dim3((unsigned)nblk), dim3(8 * 64), 0, stream, p);
     else
-      hipLaunchKernelGGL((fwd_bf16_kernel<D, 4>), dim3((unsigned)nblk), dim3(4 * 64), 0, stream, p);
+      hipLaunchKernelGGL((fwd_bf16_kernel<D, 4, false>), dim3((unsigned)nblk), dim3(4 * 64), 0, stream, p);
   } else {
     p.n_qtiles = (a.sq + kF32BlockM - 1) / kF32BlockM;
     const long long nblk = (long long)p.n_qtiles * a.hq * a.b;

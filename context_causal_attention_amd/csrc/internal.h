@@ -22,6 +22,12 @@ constexpr int kTileKeysF32 = 32;
 
 inline int tile_keys(int32_t dtype) { return dtype == CP_BF16 ? kTileKeysBf16 : kTileKeysF32; }
 
+// bf16 rings of at least this many keys may take the forward's wide launch,
+// which reads a transposed copy of V kept in the workspace (when the call has
+// no document masks); shorter ones read V in place.
+constexpr int64_t kFwdWideKeys = 65536;
+inline bool fwd_wide_keys(int32_t dtype, int64_t sk) { return dtype == CP_BF16 && sk >= kFwdWideKeys; }
+
 // Everything the forward launch needs, resolved and validated on the host.
 struct FwdArgs {
   const void* q;
@@ -47,11 +53,11 @@ struct FwdArgs {
 };
 
 struct FwdWorkspace {
-  size_t bounds_off;   // int4 per key tile: {min pos, max pos, valid rows, 0}
+  size_t bounds_off;   // int4 per key tile: {min pos, max pos, widest gap lo, gap hi}
   size_t kpos_off;     // int32 per key slot of every tile, padding slots = INT32_MAX (bf16 inputs only)
-  size_t vt_off;       // bf16 V^T [b][hkv][d][cp * tiles_per_rank * tile_keys] (bf16 inputs only)
+  size_t vt_off;       // bf16 V^T [b][hkv][d][vt_row] (wide bf16 rings only, see fwd_wide_keys)
   size_t total;
-  int64_t vt_row;      // elements per V^T row
+  int64_t vt_row;      // elements per V^T row: every key slot of the padded tiles
 };
 
 FwdWorkspace fwd_workspace_layout(int32_t b, int32_t hkv, int32_t d, int64_t sk, int32_t cp,

@@ -1,0 +1,174 @@
+// Throughput probes of the gfx950 units the attention kernels lean on, for the
+// measurement harness only (libcpattn_probe.so; not part of the C ABI of
+// libcpattn.so).  Each probe runs one workgroup of 8 wave64s per CU (two waves
+// per SIMD, as the attention kernels run) over a fixed number of iterations of
+// independent work, so the time measures issue and execution rates, not
+// latency:
+//   kind 0  MFMA only: v_mfma_f32_32x32x16_bf16 on 4 independent accumulators
+//           per wave (32768 flop each);
+//   kind 1  exp only: v_exp_f32 on 8 independent chains per lane;
+//   kind 2  FMA only: v_fma_f32 on 8 independent chains per lane;
+//   kind 3  the forward's inner mix in every wave: per MFMA, 2 FMA, 2 exp,
+//           1 bf16 pack and 2 adds (the exponentials of two scores);
+//   kind 4  the same work split by wave: waves 0-3 (one per SIMD) issue only
+//           the MFMAs, waves 4-7 only the vector part, so a SIMD's matrix
+//           work and vector work come from different waves;
+//   kind 5  MFMA only, one accumulator chain per wave (each MFMA depends on
+//           the previous one);
+//   kinds 6, 7, 8  as 3, 4 and 0 with the MFMA accumulators held in the
+//           accumulation registers (AGPRs) instead of VGPRs (the MFMAs are
+//           written as inline assembly with an AGPR operand; the results are
+//           read only after the loop, behind enough wait states).
+// Results are written to out so that no work is dropped.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
+typedef __bf16 bf16x2 __attribute__((__vector_size__(2 * sizeof(__bf16))));
+typedef float f32x16 __attribute__((__vector_size__(16 * sizeof(float))));
+typedef float f32x2 __attribute__((__vector_size__(2 * sizeof(float))));
+
+__device__ __forceinline__ bf16x8 seed_operand(int salt) {
+  bf16x8 v;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] = (__bf16)(0.001f * (float)((threadIdx.x * 7 + i * 3 + salt) & 15));
+  return v;
+}
+
+// acc += A B with acc in AGPRs.
+__device__ __forceinline__ void mfma_agpr(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+
+__device__ __forceinline__ float fold(const f32x16& a) {
+  float s = 0.f;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) s += a[r];
+  return s;
+}
+
+template <int KIND>
+__global__ __launch_bounds__(512, 1) void probe_kernel(float* out, int iters) {
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const bf16x8 a = seed_operand(1), b = seed_operand(2);
+  float result = 0.f;
+  if constexpr (KIND == 8) {
+    f32x16 acc[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[c][r] = 0.f;
+    for (int i = 0; i < iters; ++i)
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) mfma_agpr(acc[c], a, b);
+    asm volatile("s_nop 15\n\ts_nop 15\n\ts_nop 15" ::: "memory");
+#pragma unroll
+    for (int c = 0; c < 4; ++c) result += fold(acc[c]);
+  } else if constexpr (KIND == 0 || KIND == 5) {
+    constexpr int NC = KIND == 0 ? 4 : 1;
+    f32x16 acc[NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[c][r] = 0.f;
+    for (int i = 0; i < iters; ++i)
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int c = 0; c < NC; ++c) acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[c], 0, 0, 0);
+#pragma unroll
+    for (int c = 0; c < NC; ++c) result += fold(acc[c]);
+  } else if constexpr (KIND == 1 || KIND == 2) {
+    float x[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) x[c] = 0.01f * (float)(c + (threadIdx.x & 7));
+    for (int i = 0; i < iters; ++i)
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          // exp2(-x) maps [0, 1] into [0.5, 1]: one v_exp_f32 (negated source) a step
+          if constexpr (KIND == 1) x[c] = __builtin_amdgcn_exp2f(-x[c]);
+          else x[c] = __builtin_fmaf(x[c], 0.999f, -0.0001f);
+        }
+#pragma unroll
+    for (int c = 0; c < 8; ++c) result += x[c];
+  } else {
+    // per step: one MFMA and the vector work of two scores (kind 3: both in
+    // every wave; kind 4: the MFMAs in waves 0-3, the vector work in 4-7)
+    f32x16 acc[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[c][r] = 0.f;
+    float s[16], lsum = 0.f;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) s[j] = -0.01f * (float)((threadIdx.x + j) & 31);
+    auto vec = [&](int m) {
+      const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * m], 0.18f, -0.5f));
+      const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * m + 1], 0.18f, -0.5f));
+      const bf16x2 pk = __builtin_convertvector((f32x2){e0, e1}, bf16x2);
+      lsum += e0 + e1;
+      // The pair's bf16 bits read as fp32 are about e1 (its high half), so the
+      // pack feeds the next step and stays live; 2^(0.18 x - 0.5) keeps every
+      // value in (0.7, 0.9).
+      s[2 * m] = __builtin_bit_cast(float, pk);
+      s[2 * m + 1] = e1;
+    };
+    constexpr bool AG = KIND >= 6;
+    auto mm = [&](int m) {
+      if constexpr (AG) mfma_agpr(acc[m & 3], a, b);
+      else acc[m & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[m & 3], 0, 0, 0);
+    };
+    if (KIND == 3 || KIND == 6) {
+      for (int i = 0; i < iters; ++i)
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+          mm(m);
+          vec(m);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+    } else if (wave < 4) {
+      for (int i = 0; i < iters; ++i)
+#pragma unroll
+        for (int m = 0; m < 8; ++m) mm(m);
+    } else {
+      for (int i = 0; i < iters; ++i)
+#pragma unroll
+        for (int m = 0; m < 8; ++m) vec(m);
+    }
+    if constexpr (AG) asm volatile("s_nop 15\n\ts_nop 15\n\ts_nop 15" ::: "memory");
+#pragma unroll
+    for (int c = 0; c < 4; ++c) result += fold(acc[c]);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) result += s[j];
+    result += lsum;
+  }
+  out[blockIdx.x * blockDim.x + threadIdx.x] = result;
+}
+
+}  // namespace
+
+// Runs probe `kind` on `blocks` workgroups of 512 threads with `iters`
+// iterations; out (device) holds blocks * 512 floats.  Returns a hipError_t.
+extern "C" int cp_probe_run(int kind, int blocks, int iters, float* out, hipStream_t stream) {
+  const dim3 g(blocks), t(512);
+  switch (kind) {
+    case 0: hipLaunchKernelGGL(probe_kernel<0>, g, t, 0, stream, out, iters); break;
+    case 1: hipLaunchKernelGGL(probe_kernel<1>, g, t, 0, stream, out, iters); break;
+    case 2: hipLaunchKernelGGL(probe_kernel<2>, g, t, 0, stream, out, iters); break;
+    case 3: hipLaunchKernelGGL(probe_kernel<3>, g, t, 0, stream, out, iters); break;
+    case 4: hipLaunchKernelGGL(probe_kernel<4>, g, t, 0, stream, out, iters); break;
+    case 5: hipLaunchKernelGGL(probe_kernel<5>, g, t, 0, stream, out, iters); break;
+    case 6: hipLaunchKernelGGL(probe_kernel<6>, g, t, 0, stream, out, iters); break;
+    case 7: hipLaunchKernelGGL(probe_kernel<7>, g, t, 0, stream, out, iters); break;
+    case 8: hipLaunchKernelGGL(probe_kernel<8>, g, t, 0, stream, out, iters); break;
+    default: return (int)hipErrorInvalidValue;
+  }
+  return (int)hipGetLastError();
+}

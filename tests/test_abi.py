@@ -250,17 +250,24 @@ def test_ring_fwd_rejects_bad_args():
 
 
 def test_ring_fwd_rejects_keys_beyond_one_buffer_descriptor():
-    # 16777200 keys of d = 128 (row stride d, cp = 8): K takes 4294963200
-    # bytes, inside one buffer descriptor's reach, but the V^T copy over the
-    # padded tiles (8 x 32768 tiles of 64 keys) takes 2^32 bytes.
-    s = _shape(sk=16777200, hkv=1, hq=1)
-    assert _ring(s, cp=8) == cpa.CP_EINVAL
-    assert "V^T" in cpa.cp_last_error()
-    # A row stride that stretches 2^22 keys of K beyond 4 GiB.
+    # The bf16 kernel reads one (batch, kv head) of K and of V through 32-bit
+    # buffer offsets.  A row stride that stretches 2^22 keys of K beyond 4 GiB:
     s = _shape(sk=1 << 22, hkv=1, hq=1)
     s.k_str[2] = 1024
     assert _ring(s, cp=8) == cpa.CP_EINVAL
     assert "4 GiB" in cpa.cp_last_error()
+    # The same for V alone (K rows of d elements stay inside the reach).
+    s = _shape(sk=1 << 22, hkv=1, hq=1)
+    s.v_str[2] = 1024
+    assert _ring(s, cp=8) == cpa.CP_EINVAL
+    assert "4 GiB" in cpa.cp_last_error()
+    # 16777200 keys of d = 128 (row stride d, cp = 8): K and V take 4294963200
+    # bytes each, inside the reach, but the transposed V copy of the wide
+    # launch (rings of >= 65536 keys) over the padded tiles (8 x 32768 tiles
+    # of 64 keys) takes 2^32 bytes.
+    s = _shape(sk=16777200, hkv=1, hq=1)
+    assert _ring(s, cp=8) == cpa.CP_EINVAL
+    assert "V^T" in cpa.cp_last_error()
 
 
 def _stepwise(s, cp=2, rank=0, ws=FAKE, ws_bytes=1 << 40, stage=None, stage_bytes=0, o=FAKE):
@@ -332,11 +339,16 @@ def test_a2a_validation():
 
 
 def test_workspace_query():
+    # 131072 keys: the wide launch's V^T copy (8 heads x 128 x 131072 x 2 B),
+    # then per 64-key tile its bounds (16 B) and 64 padded key positions
     s = _shape(sk=131072, sq=16384, hq=32, hkv=8)
     n = cpa.lib().cp_attn_ring_fwd_workspace(ctypes.byref(s), 8)
-    # bf16 V^T copy (8 heads x 128 x 131072 x 2 B) plus the tile bounds table
-    assert n >= 8 * 128 * 131072 * 2
-    assert n < 8 * 128 * 131072 * 2 + (1 << 20)
+    tiles = 131072 // 64
+    assert n == tiles * 16 + tiles * 64 * 4 + 8 * 128 * 131072 * 2
+    # 32768 keys read V in place: only the tables
+    s = _shape(sk=32768, sq=4096, hq=32, hkv=8)
+    tiles = 32768 // 64
+    assert cpa.lib().cp_attn_ring_fwd_workspace(ctypes.byref(s), 8) == tiles * 16 + tiles * 64 * 4
     assert cpa.lib().cp_attn_ring_fwd_workspace(ctypes.byref(_shape(d=96)), 8) == 0
 
 
