@@ -25,7 +25,7 @@ __all__ = [
     "CP_OK", "CP_EINVAL", "CP_ESHAPE", "CP_EDTYPE", "CP_EWORKSPACE", "CP_EHIP",
     "CP_F32", "CP_BF16", "CP_STREAM", "CP_PER_DOC", "CP_WHOLE_DOC", "CpShape", "CpError", "LIB_PATH",
     "lib", "cp_version", "cp_last_error", "cp_shard_zigzag", "cp_unshard_zigzag",
-    "cp_varlen_index", "cp_ring_source", "cp_pairs", "cp_attn_ring_fwd_workspace",
+    "cp_varlen_index", "cp_ring_source", "cp_pairs", "cp_attn_ring_fwd_workspace", "cp_attn_ring_fwd_noalloc",
     "cp_attn_partial_fwd", "cp_attn_merge", "cp_attn_ring_fwd", "RingFwdPlan", "cp_attn_ring_fwd_stepwise",
     "RingFwdStepwisePlan", "cp_a2a_pack", "cp_a2a_pack_inverse", "cp_a2a_unpack", "cp_a2a_unpack_inverse",
     "cp_attn_bwd_workspace", "cp_attn_bwd_delta", "cp_attn_partial_bwd", "cp_attn_ring_bwd", "RingBwdPlan",
@@ -82,6 +82,8 @@ def lib() -> ctypes.CDLL:
         L.cp_attn_merge.argtypes = [c_int64, c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]
         L.cp_attn_ring_fwd.argtypes = [POINTER(CpShape), c_int32, c_int32] + [c_void_p] * 6 + \
             [c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]
+        L.cp_attn_ring_fwd_noalloc.argtypes = [POINTER(CpShape), c_int32, c_int32] + [c_void_p] * 6 + \
+            [c_void_p, c_void_p, c_void_p]
         L.cp_attn_ring_fwd_stepwise_workspace.argtypes = [POINTER(CpShape), c_int32]
         L.cp_attn_ring_fwd_stepwise_workspace.restype = c_size_t
         L.cp_attn_ring_stage_bytes.argtypes = [POINTER(CpShape), c_int32]
@@ -298,6 +300,23 @@ def cp_attn_ring_fwd(q_loc, k_all, v_all, cp, rank, q_pos, q_lo, k_pos_all, scal
     """A virtual rank's whole ring with every K/V shard resident: final (O, LSE)."""
     return RingFwdPlan(q_loc, k_all, v_all, cp, rank, q_pos, q_lo, k_pos_all, scale, out_dtype, out, lse,
                        workspace).run()
+
+
+def cp_attn_ring_fwd_noalloc(q_loc, k_all, v_all, cp, rank, q_pos, q_lo, k_pos_all, out, lse, scale=None,
+                             q_pos_dev=None, q_lo_dev=None, k_pos_dev=None):
+    """cp_attn_ring_fwd without a workspace (the library's static per-device
+    scratch holds the tile tables).  out and lse are caller-provided; positions
+    may be given already on the device (q_pos_dev, ...) so that the call itself
+    allocates nothing."""
+    dev = q_loc.device
+    shape = _shape(q_loc, k_all, v_all, _strides(out), scale, out.dtype)
+    qp = q_pos_dev if q_pos_dev is not None else _dev_i32(q_pos, dev)
+    ql = q_lo_dev if q_lo_dev is not None else (None if q_lo is None else _dev_i32(q_lo, dev))
+    kp = k_pos_dev if k_pos_dev is not None else _dev_i32(k_pos_all, dev)
+    _check(lib().cp_attn_ring_fwd_noalloc(ctypes.byref(shape), cp, rank, q_loc.data_ptr(), k_all.data_ptr(),
+                                          v_all.data_ptr(), qp.data_ptr(), None if ql is None else ql.data_ptr(),
+                                          kp.data_ptr(), out.data_ptr(), lse.data_ptr(), _stream(dev)))
+    return out, lse
 
 
 class RingFwdStepwisePlan:

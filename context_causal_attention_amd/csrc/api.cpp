@@ -183,7 +183,7 @@ namespace {
 // Validates one forward launch and fills its kernel arguments; launches nothing.
 int prep_fwd(const cp_shape* s, int32_t cp, int32_t rank, const void* q, const void* k, const void* v,
              const int32_t* q_pos, const int32_t* q_lo, const int32_t* k_pos, void* o, int32_t o_dtype,
-             float* lse, void* ws, size_t ws_bytes, FwdArgs* out) {
+             float* lse, void* ws, size_t ws_bytes, FwdArgs* out, bool v_in_place = false) {
   if (int rc = check_ptrs16({{q, "q"}, {o, "o"}, {lse, "lse"}})) return rc;
   if (!q_pos) return fail(CP_EINVAL, "q_pos is null");
   if (s->sk > 0) {
@@ -207,11 +207,13 @@ int prep_fwd(const cp_shape* s, int32_t cp, int32_t rank, const void* q, const v
     return fail(CP_EINVAL, "a shard of %lld key rows has more than 65535 key tiles", (long long)(s->sk / cp));
   const FwdWorkspace w = fwd_workspace_layout(s->b, s->hkv, s->d, s->sk, cp, s->in_dtype);
   // So does the wide launch's V^T copy: d rows over every key slot of the padded tiles.
-  if (fwd_wide_keys(s->in_dtype, s->sk) && (double)s->d * (double)w.vt_row * 2.0 >= 4294967040.0)
+  if (!v_in_place && fwd_wide_keys(s->in_dtype, s->sk) && (double)s->d * (double)w.vt_row * 2.0 >= 4294967040.0)
     return fail(CP_EINVAL, "%lld key rows exceed the 4 GiB reach of one buffer descriptor for V^T", (long long)s->sk);
-  if (!ws) return fail(CP_EWORKSPACE, "workspace is null (%zu bytes needed)", w.total);
+  // Reading V in place, the launch uses the tables only (the workspace up to its V^T part).
+  const size_t need = (v_in_place && fwd_wide_keys(s->in_dtype, s->sk)) ? w.vt_off : w.total;
+  if (!ws) return fail(CP_EWORKSPACE, "workspace is null (%zu bytes needed)", need);
   if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0) return fail(CP_EWORKSPACE, "workspace is not 256-byte aligned");
-  if (ws_bytes < w.total) return fail(CP_EWORKSPACE, "workspace too small: %zu < %zu bytes", ws_bytes, w.total);
+  if (ws_bytes < need) return fail(CP_EWORKSPACE, "workspace too small: %zu < %zu bytes", ws_bytes, need);
   FwdArgs a = base_args(s);
   a.q = q;
   a.k = k;
@@ -228,6 +230,7 @@ int prep_fwd(const cp_shape* s, int32_t cp, int32_t rank, const void* q, const v
   a.tiles_per_rank = (a.rows_per_rank + tk - 1) / tk;
   a.out_dtype = o_dtype;
   a.ws = ws;
+  a.v_in_place = v_in_place ? 1 : 0;
   *out = a;
   return CP_OK;
 }
@@ -264,6 +267,34 @@ extern "C" int cp_attn_ring_fwd(const cp_shape* s, int32_t cp, int32_t rank, con
                 2 * (long long)cp);
   return run_fwd(s, cp, rank, q_loc, k_all, v_all, q_pos, q_lo, k_pos_all, o, s->out_dtype, lse, ws,
                  ws_bytes, stream);
+}
+
+extern "C" int cp_attn_ring_fwd_noalloc(const cp_shape* s, int32_t cp, int32_t rank, const void* q_loc,
+                                        const void* k_all, const void* v_all, const int32_t* q_pos,
+                                        const int32_t* q_lo, const int32_t* k_pos_all, void* o, float* lse,
+                                        hipStream_t stream) {
+  clear_error();
+  if (int rc = check_shape(s)) return rc;
+  if (cp < 1) return fail(CP_EINVAL, "cp must be >= 1 (got %d)", cp);
+  if (rank < 0 || rank >= cp) return fail(CP_EINVAL, "rank %d outside [0, %d)", rank, cp);
+  if (s->sk % (2 * (int64_t)cp) != 0)
+    return fail(CP_ESHAPE, "key rows %lld are not a multiple of 2*cp = %lld", (long long)s->sk,
+                2 * (long long)cp);
+  if (s->sq == 0) return CP_OK;
+  // The tables of the launch that reads V in place: the workspace without its
+  // V^T part.
+  const FwdWorkspace w = fwd_workspace_layout(s->b, s->hkv, s->d, s->sk, cp, s->in_dtype);
+  const size_t need = fwd_wide_keys(s->in_dtype, s->sk) ? w.vt_off : w.total;
+  if (need > kNoAllocScratchBytes)
+    return fail(CP_EINVAL, "%lld key rows need %zu bytes of tile tables, beyond the %zu-byte static scratch of the "
+                "allocation-free forward", (long long)s->sk, need, kNoAllocScratchBytes);
+  void* scratch = nullptr;
+  if (int rc = hip_status(fwd_noalloc_scratch(&scratch), "static scratch address")) return rc;
+  FwdArgs a;
+  if (int rc = prep_fwd(s, cp, rank, q_loc, k_all, v_all, q_pos, q_lo, k_pos_all, o, s->out_dtype, lse, scratch,
+                        kNoAllocScratchBytes, &a, /*v_in_place=*/true))
+    return rc;
+  return hip_status(launch_fwd(a, stream), "forward launch");
 }
 
 extern "C" int cp_attn_merge(int64_t rows, int32_t d, float* o_acc, float* lse_acc, const float* o_p,

@@ -41,6 +41,7 @@
 #include <hip/hip_runtime.h>
 
 #include <climits>
+#include <mutex>
 #include <type_traits>
 
 #include "device_common.h"
@@ -830,11 +831,12 @@ hipError_t launch_t(const FwdArgs& a, hipStream_t stream) {
   //    workgroups per CU, whose barriers stay apart, reading V itself (no
   //    prep pass: 8-10% faster on the packed-document workloads).
   const bool wide = BF16 && a.q_lo == nullptr && fwd_wide_keys(a.in_dtype, a.sk);
+  const bool use_vt = wide && !a.v_in_place;
   const int ntiles = a.cp * a.tiles_per_rank;
   if (ntiles > 0) {
-    const dim3 grid(ntiles, wide ? a.b * a.hkv : 1);
+    const dim3 grid(ntiles, use_vt ? a.b * a.hkv : 1);
     const long long vs[3] = {a.v_str[0], a.v_str[1], a.v_str[2]};
-    if (wide)
+    if (use_vt)
       hipLaunchKernelGGL((prep_kernel<BF16, D, true>), grid, dim3(256), 0, stream, a.k_pos,
                          static_cast<const char*>(a.v), vs[0], vs[1], vs[2], a.hkv, a.rows_per_rank,
                          a.tiles_per_rank, bounds, kpos_pad, vt, (long long)w.vt_row);
@@ -861,7 +863,7 @@ hipError_t launch_t(const FwdArgs& a, hipStream_t stream) {
   p.k_sb = a.k_str[0];
   p.k_sh = a.k_str[1];
   p.k_ss = a.k_str[2];
-  if (wide) {  // V^T copy: [b][hkv][d][vt_row]
+  if (use_vt) {  // V^T copy: [b][hkv][d][vt_row]
     p.v = reinterpret_cast<const char*>(vt);
     p.v_ss = w.vt_row;
     p.v_sh = (long long)D * w.vt_row;
@@ -891,8 +893,10 @@ hipError_t launch_t(const FwdArgs& a, hipStream_t stream) {
     const int nw = wide ? 8 : 4;
     p.n_qtiles = (a.sq + nw * kRowsPerWave - 1) / (nw * kRowsPerWave);
     const long long nblk = (long long)p.n_qtiles * a.hq * a.b;
-    if (wide)
+    if (use_vt)
       hipLaunchKernelGGL((fwd_bf16_kernel<D, 8, true>), dim3((unsigned)nblk), dim3(8 * 64), 0, stream, p);
+    else if (wide)
+      hipLaunchKernelGGL((fwd_bf16_kernel<D, 8, false>), dim3((unsigned)nblk), dim3(8 * 64), 0, stream, p);
     else
       hipLaunchKernelGGL((fwd_bf16_kernel<D, 4, false>), dim3((unsigned)nblk), dim3(4 * 64), 0, stream, p);
   } else {
@@ -903,7 +907,31 @@ hipError_t launch_t(const FwdArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// Tile tables of the allocation-free forward (see fwd_noalloc_scratch).  In
+// host code `scratch` names a host-side stand-in, not the device array: only
+// the address hipGetSymbolAddress returns for the current device is ever used.
+__device__ __attribute__((aligned(256))) char scratch[kNoAllocScratchBytes];
+
 }  // namespace fwdk
+
+hipError_t fwd_noalloc_scratch(void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(fwdk::scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
+}
 
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream) {
   using namespace fwdk;

@@ -50,6 +50,7 @@ struct FwdArgs {
   int32_t out_dtype;       // dtype of o (CP_F32 for partial outputs)
   void* ws;                // workspace (layout: see fwd_workspace_layout)
   int32_t merge_acc;       // 1: merge the result into (o, lse) instead of writing it
+  int32_t v_in_place;      // 1: never read the transposed copy of V (the workspace holds only the tables)
 };
 
 struct FwdWorkspace {
@@ -62,6 +63,14 @@ struct FwdWorkspace {
 
 FwdWorkspace fwd_workspace_layout(int32_t b, int32_t hkv, int32_t d, int64_t sk, int32_t cp,
                                   int32_t in_dtype);
+
+// The allocation-free forward keeps its tile tables (bounds and padded key
+// positions, the workspace without the V^T copy) in a static device array of
+// this many bytes, one per device (attn_fwd.hip).
+constexpr size_t kNoAllocScratchBytes = (size_t)4 << 20;
+// This device's address of that array (resolved once per device with
+// hipGetSymbolAddress); no allocation.
+hipError_t fwd_noalloc_scratch(void** ptr);
 
 // Everything the backward launches need, resolved and validated on the host.
 struct BwdArgs {

@@ -21,11 +21,14 @@
  *     effects and launches nothing.
  *   - Ownership: the caller owns every buffer.  The library never allocates
  *     device memory; scratch space is a caller-provided workspace whose size a
- *     *_workspace query returns.  Pointers marked (device) must be device
- *     memory on the current HIP device; (host) ones are ordinary host memory.
+ *     *_workspace query returns (cp_attn_ring_fwd_noalloc alone uses a static
+ *     device array of its own instead).  Pointers marked (device) must be
+ *     device memory on the current HIP device; (host) ones are ordinary host
+ *     memory.
  *   - Streams: device work is enqueued asynchronously on the caller's stream,
  *     with no implicit synchronisation; a device fault surfaces at the caller's
- *     next synchronisation.  Calls are re-entrant and keep no state.
+ *     next synchronisation.  Calls are re-entrant and keep no state (apart
+ *     from that array's per-device address).
  *   - Layout: tensors are [B, H, rows, D] with the D dimension contiguous
  *     ("[batch, num_heads, seq_len // context_parallel_size, head_dim]" in the
  *     guide's pseudocode); element strides for B, H and rows are passed, so row
@@ -191,6 +194,25 @@ int cp_attn_ring_fwd(const cp_shape* s, int32_t cp, int32_t rank, const void* q_
                      const void* k_all, const void* v_all, const int32_t* q_pos,
                      const int32_t* q_lo, const int32_t* k_pos_all, void* o, float* lse,
                      void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* The whole ring of cp_attn_ring_fwd for callers that cannot allocate device
+ * memory or hand a workspace in: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc.  Arguments as for cp_attn_ring_fwd,
+ * without the workspace.  The per-tile tables the kernels need (key position
+ * bounds and padded key positions, 272 bytes per 64-key tile for bf16, 16 per
+ * 32-key tile for fp32) live in one static device array of 4 MiB per device,
+ * held until the process ends; its address is resolved on the first call on
+ * each device.  Rings whose tables exceed it (about 15000 bf16 key tiles,
+ * 985 000 keys) are rejected with CP_EINVAL.  V is always read in place (no
+ * transposed copy), so a long dense ring runs somewhat slower than through
+ * cp_attn_ring_fwd; the results are the same bits.  Nothing is allocated and
+ * every table entry is rewritten by each call.  Calls on one device share the
+ * array: calls that overlap on one device (different streams, or host threads
+ * without ordering) race and give wrong results. */
+int cp_attn_ring_fwd_noalloc(const cp_shape* s, int32_t cp, int32_t rank, const void* q_loc,
+                             const void* k_all, const void* v_all, const int32_t* q_pos,
+                             const int32_t* q_lo, const int32_t* k_pos_all, void* o, float* lse,
+                             hipStream_t stream);
 
 /* ---------------------------------------------------------------- stepwise ring
  * The ring forward computed the way a ring of separate steps computes it

@@ -27,6 +27,10 @@ hipError_t launch_a2a(int32_t, int32_t, int64_t, int32_t, int32_t, const void*, 
 hipError_t launch_merge(int64_t, int32_t, float*, float*, const float*, const float*, hipStream_t) {
   return hipSuccess;
 }
+hipError_t fwd_noalloc_scratch(void** p) {
+  *p = reinterpret_cast<void*>(0x200000);  // 256-byte aligned, never dereferenced
+  return hipSuccess;
+}
 }  // namespace cpattn
 
 static int g_events = 0;
@@ -90,6 +94,16 @@ int main() {
     cp_shape s8 = shape(256, 4096, 128, in);
     CHECK(cp_attn_ring_fwd_stepwise(&s8, 8, 3, F, F, F, FI, nullptr, FI, FF, FF, WS, BIG, WS, BIG, nullptr,
                                      nullptr) == CP_OK);
+    // the allocation-free ring: valid up to its 4 MiB of tables, rejected past them
+    CHECK(cp_attn_ring_fwd_noalloc(&s, 2, 1, F, F, F, FI, FI, FI, F, FF, nullptr) == CP_OK);
+    cp_shape wide = shape(256, 131072, 128, in);
+    CHECK(cp_attn_ring_fwd_noalloc(&wide, 8, 7, F, F, F, FI, nullptr, FI, F, FF, nullptr) == CP_OK);
+    // bf16: 2^21 keys take 32768 tiles x 272 bytes; fp32: 2^24 keys, 524288 tiles x 16 bytes
+    cp_shape huge = shape(256, int64_t(1) << (in == CP_BF16 ? 21 : 24), 128, in);
+    CHECK(cp_attn_ring_fwd_noalloc(&huge, 8, 0, F, F, F, FI, nullptr, FI, F, FF, nullptr) == CP_EINVAL);
+    CHECK(cp_attn_ring_fwd_noalloc(&s, 3, 0, F, F, F, FI, nullptr, FI, F, FF, nullptr) == CP_ESHAPE);
+    CHECK(cp_attn_ring_fwd_noalloc(&s, 2, 2, F, F, F, FI, nullptr, FI, F, FF, nullptr) == CP_EINVAL);
+    CHECK(cp_attn_ring_fwd_noalloc(&s, 2, 0, nullptr, F, F, FI, nullptr, FI, F, FF, nullptr) == CP_EINVAL);
   }
   CHECK(stub_live_events() == 0);  // every event the calls created was destroyed
   {
