@@ -318,42 +318,54 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(KParams p) {
   auto kbuf = [&](auto bc) -> char* { if constexpr (decltype(bc)::value) return sK1; else return sK0; };
   auto vbuf = [&](auto bc) -> char* { if constexpr (decltype(bc)::value) return sV1; else return sV0; };
   auto pbuf = [&](auto bc) -> int* { if constexpr (decltype(bc)::value) return sP1; else return sP0; };
-  // List entry .x: src | i << 8 for key tile i of rank src's shard (tile id
-  // src * tpr + i); .y: class of wave w in bits 2w, 2w+1.
-  auto rows_of = [&](int e, int& r0, int& nval) {
+  // A list entry, as this wave sees it: src | i << 8 for key tile i of rank
+  // src's shard (tile id src * tpr + i), and the wave's class of the tile in
+  // bits 24-25.
+  auto rows_of = [&](unsigned e, int& r0, int& nval) {
     const int src = e & 0xFF, i = (e >> 8) & 0xFFFF;
     r0 = src * p.R + i * C::BN;
     nval = min(C::BN, p.R - i * C::BN);
   };
-  // Copies this wave's share of K of list entry e into buffer bc.  Each tile
-  // gets a descriptor whose record count ends at the shard's last valid row, so
-  // rows past it read as zero.
-  auto issue_k = [&](auto bc, int e) {
+  auto tile_of = [&](unsigned e) { return (int)(e & 0xFF) * p.tpr + (int)((e >> 8) & 0xFFFF); };
+  // Copy source of a tile's K (or V) rows: a descriptor whose record count
+  // ends at the shard's last valid row, so rows past it read as zero, and a
+  // byte offset.  A copy that is not needed (ok false) gets a descriptor of
+  // no records: it writes zeros into the free buffer.
+  struct Src {
+    __amdgpu_buffer_rsrc_t rs;
+    int soff;
+  };
+  auto k_src = [&](unsigned e, bool ok) {
     int r0, nval;
     rows_of(e, r0, nval);
-    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(kbase + (long long)r0 * k_row_bytes), 0, (int)(nval * k_row_bytes), kBufferFlags);
-#pragma unroll
-    for (int j = 0; j < BPW; ++j) copy_lds16(rs, voffK[j], 0, lds_addr(kbuf(bc) + (wave + NW * j) * 1024));
+    return Src{__builtin_amdgcn_make_buffer_rsrc((void*)(kbase + (long long)r0 * k_row_bytes), 0,
+                                                 ok ? (int)(nval * k_row_bytes) : 0, kBufferFlags),
+               0};
   };
-  // Copies this wave's share of V (or V^T: the tile's 64 key columns, zero in
-  // the padding of a shard's last tile) of entry e into buffer bc, and (wave
-  // 0) the tile's key positions, padding slots kInvalidKey.
-  auto issue_v = [&](auto bc, int e) {
-    const int tile = (e & 0xFF) * p.tpr + ((e >> 8) & 0xFFFF);
+  // V, or V^T (the tile's 64 key columns, zero in the padding of a shard's
+  // last tile).
+  auto v_src = [&](unsigned e, bool ok) {
     if constexpr (VT) {
-#pragma unroll
-      for (int j = 0; j < BPW; ++j)
-        copy_lds16(rsVT, voffV[j], tile * C::BN * 2, lds_addr(vbuf(bc) + (wave + NW * j) * 1024));
+      return Src{ok ? rsVT : __builtin_amdgcn_make_buffer_rsrc((void*)vbase, 0, 0, kBufferFlags),
+                 tile_of(e) * C::BN * 2};
     } else {
       int r0, nval;
       rows_of(e, r0, nval);
-      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-          (void*)(vbase + (long long)r0 * v_row_bytes), 0, (int)(nval * v_row_bytes), kBufferFlags);
-#pragma unroll
-      for (int j = 0; j < BPW; ++j) copy_lds16(rs, voffV[j], 0, lds_addr(vbuf(bc) + (wave + NW * j) * 1024));
+      return Src{__builtin_amdgcn_make_buffer_rsrc((void*)(vbase + (long long)r0 * v_row_bytes), 0,
+                                                   ok ? (int)(nval * v_row_bytes) : 0, kBufferFlags),
+                 0};
     }
-    if (wave == 0) copy_lds4(rsP, tile * C::BN * 4 + lane * 4, lds_addr(pbuf(bc)));
+  };
+  // This wave's share of a K or V tile copy: blocks wave, wave + NW, ...
+  auto copy_k = [&](auto bc, const Src& sr, int j) {
+    copy_lds16(sr.rs, voffK[j], sr.soff, lds_addr(kbuf(bc) + (wave + NW * j) * 1024));
+  };
+  auto copy_v = [&](auto bc, const Src& sr, int j) {
+    copy_lds16(sr.rs, voffV[j], sr.soff, lds_addr(vbuf(bc) + (wave + NW * j) * 1024));
+  };
+  // The key positions of tile e (wave 0; padding slots kInvalidKey).
+  auto copy_pos = [&](auto bc, unsigned e) {
+    if (wave == 0) copy_lds4(rsP, tile_of(e) * C::BN * 4 + lane * 4, lds_addr(pbuf(bc)));
   };
 
   // ---- online softmax state ------------------------------------------------
@@ -407,7 +419,15 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(KParams p) {
   // One tile: its scores (c0, c1) are masked (key positions in buffer vbc),
   // exponentiated into pb while the next tile's scores are computed into (n0,
   // n1) from K buffer kbc, then multiplied into O with V from buffer vbc.
-  auto stage = [&](auto kbc, auto vbc, f32x16& c0, f32x16& c1, f32x16& n0, f32x16& n1, int cls_cur) {
+  // dk, dv: sources of the copies this tile's stage issues, K of the tile
+  // after next into the K buffer other than kbc and V of the next tile into
+  // the V buffer other than vbc, spread over the score chunks: issued
+  // together, the copies of all waves queue at the vector memory unit and
+  // stall the waves behind them.
+  auto stage = [&](auto kbc, auto vbc, f32x16& c0, f32x16& c1, f32x16& n0, f32x16& n1, int cls_cur, const Src& dk,
+                   const Src& dv) {
+    using KO = std::integral_constant<int, 1 - decltype(kbc)::value>;
+    using VO = std::integral_constant<int, 1 - decltype(vbc)::value>;
     const int* sP = pbuf(vbc);
     // Register r of sub-tile sub holds key 32*sub + 16*(r/8) + 8*hi + r%8.
     if (cls_cur == kPartial) {
@@ -454,6 +474,13 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(KParams p) {
       for (int m = 0; m < PF; ++m) ops[m] = kop(m);
 #pragma unroll
       for (int m = 0; m < NM; ++m) {
+        constexpr int NC = 2 * BPW;                      // copy instructions per tile
+        constexpr int STEP = NM / NC > 1 ? NM / NC : 1;  // chunks between them
+        if (m % STEP == 0 && m / STEP < NC) {
+          const int i = m / STEP;
+          if (i < BPW) copy_k(KO{}, dk, i);
+          else copy_v(VO{}, dv, i - BPW);
+        }
         if (m + PF < NM) ops[m + PF] = kop(m + PF);
         if (m & 1) n1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ops[m], qreg[m >> 1], n1, 0, 0, 0);
         else n0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ops[m], qreg[m >> 1], n0, 0, 0, 0);
@@ -531,33 +558,46 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(KParams p) {
 
   // ---- walk the ring: list the needed key tiles, then stream them ---------
   // Iteration j reads K of tile j+1 and V of tile j while tile j+2's K and
-  // tile j+1's V are copied in; buffers alternate, so the loop is unrolled by
-  // two with static buffer and register roles.  Each copy has the iteration
-  // to land: every wave waits for its own copies at the end of the iteration,
-  // before the barrier after which any wave reads them.
+  // tile j+1's V (and key positions) are copied in; buffers alternate, so the
+  // loop is unrolled by two with static buffer and register roles.  Each copy
+  // has the iteration to land: every wave waits for its own copies at the end
+  // of the iteration, before the barrier after which any wave reads them.
   f32x16 sa0, sa1, sb0, sb1;
   const int total = p.cp * p.tpr;
   const int csh = 2 * wave;
-  auto cls_of = [&](int2 e) { return (int)(((unsigned)e.y >> csh) & 3); };
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
   for (int u0 = 0; u0 < total; u0 += kListCap) {
     const int cnt = build_key_list<C::BN, NW>(p.bounds, p.tpr, p.R, p.rank, p.cp, u0, min(total, u0 + kListCap), tid,
                                                   wave, lane, sWb, sList, sCnt);
     if (cnt == 0) continue;
-    // Entry of list slot j (x: tile, y: classes), read as scalars.
-    auto entry = [&](int j) {
-      int2 e = {0, 0};
-      if (j < cnt) {
-        e.x = __builtin_amdgcn_readfirstlane(sList[j].x);
-        e.y = __builtin_amdgcn_readfirstlane(sList[j].y);
+    // Lane l of vl holds list slot lbase + l as this wave sees it (0 past the
+    // end): an iteration takes its entry with v_readlane, not an LDS round trip.
+    int lbase = 0;
+    unsigned vl = 0;
+    auto fill = [&](int b) {
+      lbase = b;
+      unsigned v = 0;
+      if (b + lane < cnt) {
+        const int2 e = sList[b + lane];
+        v = (unsigned)e.x | ((((unsigned)e.y >> csh) & 3u) << 24);
       }
-      return e;
+      vl = v;
     };
-    int2 e_cur = entry(0), e_nxt = entry(1);
-    issue_k(I0{}, e_cur.x);
-    issue_v(I0{}, e_cur.x);
-    if (cnt > 1) issue_k(I1{}, e_nxt.x);
+    auto slot = [&](int j) { return (unsigned)__builtin_amdgcn_readlane((int)vl, j - lbase); };
+    auto cls_of = [](unsigned e) { return (int)(e >> 24); };
+    fill(0);
+    unsigned e_cur = slot(0), e_nxt = slot(1);
+    copy_pos(I0{}, e_cur);
+    {
+      const Src k0 = k_src(e_cur, true), v0 = v_src(e_cur, true), k1 = k_src(e_nxt, cnt > 1);
+#pragma unroll
+      for (int j = 0; j < BPW; ++j) {
+        copy_k(I0{}, k0, j);
+        copy_v(I0{}, v0, j);
+        copy_k(I1{}, k1, j);
+      }
+    }
     wait_vmem();
     __syncthreads();
     if (cls_of(e_cur) != kSkip) scores(I0{}, sa0, sa1);
@@ -565,10 +605,10 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(KParams p) {
     for (int j = 0;;) {
       // K of tile j+1 in buffer 1, V of tile j in buffer 0; scores of tile j in sa.
       {
-        const int2 e2 = entry(j + 2);
-        if (j + 2 < cnt) issue_k(I0{}, e2.x);
-        if (j + 1 < cnt) issue_v(I1{}, e_nxt.x);
-        stage(I1{}, I0{}, sa0, sa1, sb0, sb1, cls_of(e_cur));
+        if (j + 2 - lbase >= 64) fill(j + 2);
+        const unsigned e2 = slot(j + 2);
+        copy_pos(I1{}, e_nxt);
+        stage(I1{}, I0{}, sa0, sa1, sb0, sb1, cls_of(e_cur), k_src(e2, j + 2 < cnt), v_src(e_nxt, j + 1 < cnt));
         wait_vmem();
         __syncthreads();
         e_cur = e_nxt;
@@ -577,10 +617,10 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(KParams p) {
       if (++j >= cnt) break;
       // K of tile j+1 in buffer 0, V of tile j in buffer 1; scores of tile j in sb.
       {
-        const int2 e2 = entry(j + 2);
-        if (j + 2 < cnt) issue_k(I1{}, e2.x);
-        if (j + 1 < cnt) issue_v(I0{}, e_nxt.x);
-        stage(I0{}, I1{}, sb0, sb1, sa0, sa1, cls_of(e_cur));
+        if (j + 2 - lbase >= 64) fill(j + 2);
+        const unsigned e2 = slot(j + 2);
+        copy_pos(I0{}, e_nxt);
+        stage(I0{}, I1{}, sb0, sb1, sa0, sa1, cls_of(e_cur), k_src(e2, j + 2 < cnt), v_src(e_nxt, j + 1 < cnt));
         wait_vmem();
         __syncthreads();
         e_cur = e_nxt;
