@@ -206,8 +206,10 @@ def probe_bench(args):
     (one 8-wave workgroup per CU, two waves per SIMD), from the probe kernels
     of libcpattn_probe.so: sustained bf16 MFMA rate, exp and FMA issue rates,
     and the forward's MFMA + exponential mix with the two kinds of work in the
-    same waves or in different waves of each SIMD.  Cycles are counted at the
-    sclk sampled during each probe."""
+    same waves or in different waves of each SIMD.  The clock each probe ran
+    at is its workgroups' shader clock cycles (s_memtime readings at the start
+    and end of each workgroup, median over workgroups) over the kernel's
+    duration; cycles per unit are counted at that clock."""
     import ctypes
     import numpy as np
     import torch
@@ -215,30 +217,34 @@ def probe_bench(args):
     if not os.path.exists(cpb.PROBE_LIB):
         raise RuntimeError(f"{cpb.PROBE_LIB} is not built; run __graft_entry__.build() first")
     L = ctypes.CDLL(cpb.PROBE_LIB)
-    L.cp_probe_run.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    L.cp_probe_run.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                               ctypes.c_void_p]
     blocks = 256
     out = torch.empty(blocks * 512, device="cuda:0")
+    clk = torch.zeros(2 * blocks, dtype=torch.int64, device="cuda:0")
     stream = torch.cuda.current_stream().cuda_stream
     # iterations per launch, sized for ~20-60 ms per launch
     iters = {0: 20000, 5: 20000, 8: 20000, 1: 100000, 2: 100000, 3: 40000, 4: 40000, 6: 40000, 7: 40000}
     res = {}
     for kind, (name, what) in PROBES.items():
         def launch():
-            rc = L.cp_probe_run(kind, blocks, iters[kind], ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(stream))
+            rc = L.cp_probe_run(kind, blocks, iters[kind], ctypes.c_void_p(out.data_ptr()),
+                                ctypes.c_void_p(clk.data_ptr()), ctypes.c_void_p(stream))
             if rc != 0:
                 raise RuntimeError(f"probe {name}: hip error {rc}")
         launch()
         torch.cuda.synchronize()
-        times = []
-        with ClockSampler(0.01) as clk:
-            for _ in range(max(3, args.steps)):
-                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                a.record(); launch(); b.record()
-                b.synchronize()
-                times.append(a.elapsed_time(b) / 1e3)
+        times, mhzs = [], []
+        for _ in range(max(3, args.steps)):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(); launch(); b.record()
+            b.synchronize()
+            dt = a.elapsed_time(b) / 1e3
+            c = clk.view(blocks, 2).cpu().numpy()
+            times.append(dt)
+            mhzs.append(float(np.median(c[:, 1] - c[:, 0])) / dt / 1e6)
         t = float(np.median(times))
-        cs = clk.summary()
-        mhz = cs["sclk_mhz"]["median"] if cs.get("sclk_mhz") else None
+        mhz = round(float(np.median(mhzs)), 1)
         it = iters[kind]
         per_simd = {}
         if kind in (0, 5, 8):

@@ -19,7 +19,10 @@
 //           accumulation registers (AGPRs) instead of VGPRs (the MFMAs are
 //           written as inline assembly with an AGPR operand; the results are
 //           read only after the loop, behind enough wait states).
-// Results are written to out so that no work is dropped.
+// Results are written to out so that no work is dropped.  Wave 0 of every
+// workgroup also records the shader clock counter (s_memtime) before and after
+// the work, so the host can tell the clock the probe ran at: cycles over the
+// kernel's duration.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -51,8 +54,9 @@ __device__ __forceinline__ float fold(const f32x16& a) {
 }
 
 template <int KIND>
-__global__ __launch_bounds__(512, 1) void probe_kernel(float* out, int iters) {
+__global__ __launch_bounds__(512, 1) void probe_kernel(float* out, unsigned long long* clk, int iters) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const unsigned long long t0 = __builtin_amdgcn_s_memtime();
   const bf16x8 a = seed_operand(1), b = seed_operand(2);
   float result = 0.f;
   if constexpr (KIND == 8) {
@@ -150,24 +154,31 @@ __global__ __launch_bounds__(512, 1) void probe_kernel(float* out, int iters) {
     result += lsum;
   }
   out[blockIdx.x * blockDim.x + threadIdx.x] = result;
+  if (threadIdx.x == 0) {
+    const unsigned long long t1 = __builtin_amdgcn_s_memtime();
+    clk[2 * blockIdx.x] = t0;
+    clk[2 * blockIdx.x + 1] = t1;
+  }
 }
 
 }  // namespace
 
 // Runs probe `kind` on `blocks` workgroups of 512 threads with `iters`
-// iterations; out (device) holds blocks * 512 floats.  Returns a hipError_t.
-extern "C" int cp_probe_run(int kind, int blocks, int iters, float* out, hipStream_t stream) {
+// iterations; out (device) holds blocks * 512 floats, clk (device) 2 * blocks
+// clock readings (start and end of each workgroup).  Returns a hipError_t.
+extern "C" int cp_probe_run(int kind, int blocks, int iters, float* out, unsigned long long* clk,
+                            hipStream_t stream) {
   const dim3 g(blocks), t(512);
   switch (kind) {
-    case 0: hipLaunchKernelGGL(probe_kernel<0>, g, t, 0, stream, out, iters); break;
-    case 1: hipLaunchKernelGGL(probe_kernel<1>, g, t, 0, stream, out, iters); break;
-    case 2: hipLaunchKernelGGL(probe_kernel<2>, g, t, 0, stream, out, iters); break;
-    case 3: hipLaunchKernelGGL(probe_kernel<3>, g, t, 0, stream, out, iters); break;
-    case 4: hipLaunchKernelGGL(probe_kernel<4>, g, t, 0, stream, out, iters); break;
-    case 5: hipLaunchKernelGGL(probe_kernel<5>, g, t, 0, stream, out, iters); break;
-    case 6: hipLaunchKernelGGL(probe_kernel<6>, g, t, 0, stream, out, iters); break;
-    case 7: hipLaunchKernelGGL(probe_kernel<7>, g, t, 0, stream, out, iters); break;
-    case 8: hipLaunchKernelGGL(probe_kernel<8>, g, t, 0, stream, out, iters); break;
+    case 0: hipLaunchKernelGGL(probe_kernel<0>, g, t, 0, stream, out, clk, iters); break;
+    case 1: hipLaunchKernelGGL(probe_kernel<1>, g, t, 0, stream, out, clk, iters); break;
+    case 2: hipLaunchKernelGGL(probe_kernel<2>, g, t, 0, stream, out, clk, iters); break;
+    case 3: hipLaunchKernelGGL(probe_kernel<3>, g, t, 0, stream, out, clk, iters); break;
+    case 4: hipLaunchKernelGGL(probe_kernel<4>, g, t, 0, stream, out, clk, iters); break;
+    case 5: hipLaunchKernelGGL(probe_kernel<5>, g, t, 0, stream, out, clk, iters); break;
+    case 6: hipLaunchKernelGGL(probe_kernel<6>, g, t, 0, stream, out, clk, iters); break;
+    case 7: hipLaunchKernelGGL(probe_kernel<7>, g, t, 0, stream, out, clk, iters); break;
+    case 8: hipLaunchKernelGGL(probe_kernel<8>, g, t, 0, stream, out, clk, iters); break;
     default: return (int)hipErrorInvalidValue;
   }
   return (int)hipGetLastError();
