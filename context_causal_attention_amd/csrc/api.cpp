@@ -120,7 +120,7 @@ int fail(int code, const char* fmt, ...) {
 
 void clear_error() { g_last_error.clear(); }
 
-FwdWorkspace fwd_workspace_layout(int32_t b, int32_t hkv, int32_t d, int64_t sk, int32_t cp,
+FwdWorkspace fwd_workspace_layout(int32_t b, int32_t hkv, int32_t d, int64_t sq, int64_t sk, int32_t cp,
                                   int32_t in_dtype) {
   FwdWorkspace w{};
   const int tk = tile_keys(in_dtype);
@@ -131,6 +131,8 @@ FwdWorkspace fwd_workspace_layout(int32_t b, int32_t hkv, int32_t d, int64_t sk,
   size_t off = align_up((size_t)ntiles * 16, 256);
   w.kpos_off = off;
   if (in_dtype == CP_BF16) off += align_up((size_t)ntiles * tk * 4, 256);
+  w.order_off = off;
+  if (in_dtype == CP_BF16) off += align_up((size_t)2 * ((sq + kOrderRows - 1) / kOrderRows) * 4, 256);
   w.vt_off = off;
   w.vt_row = ntiles * tk;
   if (fwd_wide_keys(in_dtype, sk)) off += align_up((size_t)b * hkv * d * (size_t)w.vt_row * 2, 256);
@@ -175,7 +177,7 @@ extern "C" int cp_version(void) { return 200; }
 
 extern "C" size_t cp_attn_ring_fwd_workspace(const cp_shape* s, int32_t cp) {
   if (check_shape(s) != CP_OK || cp < 1) return 0;
-  return fwd_workspace_layout(s->b, s->hkv, s->d, s->sk, cp, s->in_dtype).total;
+  return fwd_workspace_layout(s->b, s->hkv, s->d, s->sq, s->sk, cp, s->in_dtype).total;
 }
 
 namespace {
@@ -205,7 +207,7 @@ int prep_fwd(const cp_shape* s, int32_t cp, int32_t rank, const void* q, const v
   if (cp > 255) return fail(CP_EINVAL, "cp must be <= 255 (got %d)", cp);
   if ((s->sk / cp + tile_keys(s->in_dtype) - 1) / tile_keys(s->in_dtype) > 65535)
     return fail(CP_EINVAL, "a shard of %lld key rows has more than 65535 key tiles", (long long)(s->sk / cp));
-  const FwdWorkspace w = fwd_workspace_layout(s->b, s->hkv, s->d, s->sk, cp, s->in_dtype);
+  const FwdWorkspace w = fwd_workspace_layout(s->b, s->hkv, s->d, s->sq, s->sk, cp, s->in_dtype);
   // So does the wide launch's V^T copy: d rows over every key slot of the padded tiles.
   if (!v_in_place && fwd_wide_keys(s->in_dtype, s->sk) && (double)s->d * (double)w.vt_row * 2.0 >= 4294967040.0)
     return fail(CP_EINVAL, "%lld key rows exceed the 4 GiB reach of one buffer descriptor for V^T", (long long)s->sk);
@@ -283,7 +285,7 @@ extern "C" int cp_attn_ring_fwd_noalloc(const cp_shape* s, int32_t cp, int32_t r
   if (s->sq == 0) return CP_OK;
   // The tables of the launch that reads V in place: the workspace without its
   // V^T part.
-  const FwdWorkspace w = fwd_workspace_layout(s->b, s->hkv, s->d, s->sk, cp, s->in_dtype);
+  const FwdWorkspace w = fwd_workspace_layout(s->b, s->hkv, s->d, s->sq, s->sk, cp, s->in_dtype);
   const size_t need = fwd_wide_keys(s->in_dtype, s->sk) ? w.vt_off : w.total;
   if (need > kNoAllocScratchBytes)
     return fail(CP_EINVAL, "%lld key rows need %zu bytes of tile tables, beyond the %zu-byte static scratch of the "
@@ -325,7 +327,7 @@ StepwiseLayout stepwise_layout(const cp_shape* s, int32_t cp) {
     off += align_up(bytes, 256);
     return at;
   };
-  w.kern_bytes = fwd_workspace_layout(s->b, s->hkv, s->d, s->sk / cp, 1, s->in_dtype).total;
+  w.kern_bytes = fwd_workspace_layout(s->b, s->hkv, s->d, s->sq, s->sk / cp, 1, s->in_dtype).total;
   w.kern_off = take(w.kern_bytes);
   w.total = off;
   return w;

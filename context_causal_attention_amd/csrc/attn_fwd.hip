@@ -69,6 +69,7 @@ struct KParams {
   const int* k_pos;
   const int* kpos_pad;      // bf16: key positions per tile slot, padding = kInvalidKey
   const int4* bounds;       // per key tile {min pos, max pos, gap lo, gap hi}
+  const int* order;         // may be null: query tiles in dispatch order (heaviest first)
   char* o;
   float* lse;
   long long q_sb, q_sh, q_ss;
@@ -84,7 +85,8 @@ struct KParams {
 // XCDs; each XCD gets a contiguous range of logical ids so that the query heads
 // sharing one K/V head (and the same key tiles) run on the same L2.  Within a
 // range, query tiles run from the last (most keys under a causal mask) to the
-// first.
+// first, or in the order of p.order (document masks: the tiles that list the
+// most key tiles first, so the longest workgroups do not start last).
 struct Item {
   int b, h, kvh, qt;
 };
@@ -94,7 +96,7 @@ __device__ __forceinline__ Item map_block(const KParams& p) {
   const int hg = logical % g;
   int rest = logical / g;
   Item it;
-  it.qt = p.n_qtiles - 1 - rest % p.n_qtiles;
+  it.qt = p.order ? p.order[rest % p.n_qtiles] : p.n_qtiles - 1 - rest % p.n_qtiles;
   rest /= p.n_qtiles;
   it.kvh = rest % p.Hkv;
   it.b = rest / p.Hkv;
@@ -855,9 +857,83 @@ __global__ __launch_bounds__(256) void prep_kernel(const int* __restrict__ k_pos
   }
 }
 
+// Dispatch order of a document-masked bf16 launch.  order_cost_kernel: per
+// 128-row query tile (4 waves of 32 rows, as the launch deals them), the number
+// of ring key tiles the tile's workgroup lists, by the forward's own rule
+// (build_key_list).  order_sort_kernel: one workgroup sorts the tiles by that
+// count, most first, ties by tile index, with a bitonic sort in LDS, and
+// writes their indices to order.
+__global__ __launch_bounds__(256) void order_cost_kernel(const int* __restrict__ q_pos, const int* __restrict__ q_lo,
+                                                         const int4* __restrict__ bounds, int sq, int R, int tpr,
+                                                         int rank, int cp, int* __restrict__ cost) {
+  constexpr int NW = kOrderRows / kRowsPerWave;
+  __shared__ int sWb[NW][6];
+  __shared__ int sCnt[NW];
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int row = blockIdx.x * kOrderRows + wave * kRowsPerWave + (lane & 31);
+  const bool valid = row < sq;
+  wave_row_bounds(wave, lane, valid, valid ? q_pos[row] : -1, valid ? q_lo[row] : INT_MAX, sWb);
+  __syncthreads();
+  const int total = cp * tpr;
+  int cnt = 0;
+  for (int u = tid; u < total; u += NW * 64) {
+    const int t = u / tpr;
+    const int i = u - t * tpr;
+    int src = rank - t;
+    if (src < 0) src += cp;
+    const int4 bd = bounds[src * tpr + i];
+    bool act = false;
+#pragma unroll
+    for (int w = 0; w < NW; ++w)
+      act |= bd.x <= sWb[w][1] && bd.y >= sWb[w][2] && !(bd.z < sWb[w][2] && sWb[w][1] < bd.w) &&
+             !(sWb[w][4] < bd.x && bd.y < sWb[w][5]);
+    cnt += act ? 1 : 0;
+  }
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) cnt += __shfl_xor(cnt, o);
+  if (lane == 0) sCnt[wave] = cnt;
+  __syncthreads();
+  if (tid == 0) {
+    int tot = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) tot += sCnt[w];
+    cost[blockIdx.x] = tot;
+  }
+}
+
+__global__ __launch_bounds__(1024) void order_sort_kernel(const int* __restrict__ cost, int n, int* __restrict__ order) {
+  __shared__ unsigned long long key[kOrderMaxTiles];
+  int m = 1;
+  while (m < n) m <<= 1;
+  // key: count in the high word, ~index in the low word (distinct, so the
+  // descending sort is total); padding 0 sorts last.
+  for (int i = threadIdx.x; i < m; i += blockDim.x)
+    key[i] = i < n ? ((unsigned long long)(unsigned)cost[i] << 32) | (0xFFFFFFFFu - (unsigned)i) : 0ull;
+  __syncthreads();
+  for (int k = 2; k <= m; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      for (int i = threadIdx.x; i < m; i += blockDim.x) {
+        const int l = i ^ j;
+        if (l > i) {
+          const unsigned long long a = key[i], b = key[l];
+          const bool desc = (i & k) == 0;  // this block sorts descending
+          if (desc ? a < b : a > b) {
+            key[i] = b;
+            key[l] = a;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+  for (int i = threadIdx.x; i < n; i += blockDim.x) order[i] = (int)(0xFFFFFFFFu - (unsigned)key[i]);
+}
+
 template <bool BF16, int D>
 hipError_t launch_t(const FwdArgs& a, hipStream_t stream) {
-  const FwdWorkspace w = fwd_workspace_layout(a.b, a.hkv, a.d, a.sk, a.cp, a.in_dtype);
+  const FwdWorkspace w = fwd_workspace_layout(a.b, a.hkv, a.d, a.sq, a.sk, a.cp, a.in_dtype);
   char* ws = static_cast<char*>(a.ws);
   int4* bounds = reinterpret_cast<int4*>(ws + w.bounds_off);
   int* kpos_pad = reinterpret_cast<int*>(ws + w.kpos_off);
@@ -872,6 +948,12 @@ hipError_t launch_t(const FwdArgs& a, hipStream_t stream) {
   //    prep pass: 8-10% faster on the packed-document workloads).
   const bool wide = BF16 && a.q_lo == nullptr && fwd_wide_keys(a.in_dtype, a.sk);
   const bool use_vt = wide && !a.v_in_place;
+  // Document masks make the work per query tile uneven: those launches
+  // dispatch their query tiles heaviest first.
+  const int n_order = (int)((a.sq + kOrderRows - 1) / kOrderRows);
+  const bool ordered = BF16 && !wide && a.q_lo != nullptr && a.sk > 0 && n_order > 1 && n_order <= kOrderMaxTiles;
+  int* order_cost = reinterpret_cast<int*>(ws + w.order_off);
+  int* order = order_cost + n_order;
   const int ntiles = a.cp * a.tiles_per_rank;
   if (ntiles > 0) {
     const dim3 grid(ntiles, use_vt ? a.b * a.hkv : 1);
@@ -887,6 +969,13 @@ hipError_t launch_t(const FwdArgs& a, hipStream_t stream) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
+  if (ordered) {
+    hipLaunchKernelGGL(order_cost_kernel, dim3(n_order), dim3(256), 0, stream, a.q_pos, a.q_lo, bounds, (int)a.sq,
+                       a.rows_per_rank, a.tiles_per_rank, a.rank, a.cp, order_cost);
+    hipLaunchKernelGGL(order_sort_kernel, dim3(1), dim3(1024), 0, stream, order_cost, n_order, order);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   KParams p{};
   p.q = static_cast<const char*>(a.q);
   p.k = static_cast<const char*>(a.k);
@@ -895,6 +984,7 @@ hipError_t launch_t(const FwdArgs& a, hipStream_t stream) {
   p.k_pos = a.k_pos;
   p.kpos_pad = kpos_pad;
   p.bounds = bounds;
+  p.order = ordered ? order : nullptr;
   p.o = static_cast<char*>(a.o);
   p.lse = a.lse;
   p.q_sb = a.q_str[0];

@@ -56,13 +56,19 @@ struct FwdArgs {
 struct FwdWorkspace {
   size_t bounds_off;   // int4 per key tile: {min pos, max pos, widest gap lo, gap hi}
   size_t kpos_off;     // int32 per key slot of every tile, padding slots = INT32_MAX (bf16 inputs only)
+  size_t order_off;    // int32 per 128-row query tile: listed key tiles, then the dispatch order of
+                       // document-masked bf16 launches (bf16 inputs only)
   size_t vt_off;       // bf16 V^T [b][hkv][d][vt_row] (wide bf16 rings only, see fwd_wide_keys)
   size_t total;
   int64_t vt_row;      // elements per V^T row: every key slot of the padded tiles
 };
 
-FwdWorkspace fwd_workspace_layout(int32_t b, int32_t hkv, int32_t d, int64_t sk, int32_t cp,
+FwdWorkspace fwd_workspace_layout(int32_t b, int32_t hkv, int32_t d, int64_t sq, int64_t sk, int32_t cp,
                                   int32_t in_dtype);
+// Query tiles of the document-masked bf16 launch (4 waves of 32 rows), and
+// the most of them whose dispatch order is sorted (one workgroup sorts them).
+constexpr int kOrderRows = 128;
+constexpr int kOrderMaxTiles = 4096;
 
 // The allocation-free forward keeps its tile tables (bounds and padded key
 // positions, the workspace without the V^T copy) in a static device array of

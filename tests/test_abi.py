@@ -341,14 +341,15 @@ def test_a2a_validation():
 def test_workspace_query():
     # 131072 keys: the wide launch's V^T copy (8 heads x 128 x 131072 x 2 B),
     # then per 64-key tile its bounds (16 B) and 64 padded key positions
+    # and per 128-row query tile two ints (listed key tiles, dispatch order)
     s = _shape(sk=131072, sq=16384, hq=32, hkv=8)
     n = cpa.lib().cp_attn_ring_fwd_workspace(ctypes.byref(s), 8)
     tiles = 131072 // 64
-    assert n == tiles * 16 + tiles * 64 * 4 + 8 * 128 * 131072 * 2
+    assert n == tiles * 16 + tiles * 64 * 4 + 2 * 128 * 4 + 8 * 128 * 131072 * 2
     # 32768 keys read V in place: only the tables
     s = _shape(sk=32768, sq=4096, hq=32, hkv=8)
     tiles = 32768 // 64
-    assert cpa.lib().cp_attn_ring_fwd_workspace(ctypes.byref(s), 8) == tiles * 16 + tiles * 64 * 4
+    assert cpa.lib().cp_attn_ring_fwd_workspace(ctypes.byref(s), 8) == tiles * 16 + tiles * 64 * 4 + 256
     assert cpa.lib().cp_attn_ring_fwd_workspace(ctypes.byref(_shape(d=96)), 8) == 0
 
 
