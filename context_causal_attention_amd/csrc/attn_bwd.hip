@@ -830,7 +830,7 @@ __global__ __launch_bounds__(512, 1) void dq_kernel(BParams p) {
   const int total = p.cp * p.tpr;
   const int csh = 2 * wave;
   for (int u0 = 0; u0 < total; u0 += C::LIST) {
-    const int cnt = build_key_list<kKT, NW>(p.kbounds, p.tpr, p.R, p.rank, p.cp, u0, min(total, u0 + C::LIST), tid,
+    const int cnt = build_key_list<kKT, NW, C::LIST>(p.kbounds, p.tpr, p.R, p.rank, p.cp, u0, min(total, u0 + C::LIST), tid,
                                             wave, lane, sWb, sList, sCnt);
     if (cnt == 0) continue;
     auto ent = [&](int j) {

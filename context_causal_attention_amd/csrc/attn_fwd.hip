@@ -570,7 +570,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(KParams p) {
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
   for (int u0 = 0; u0 < total; u0 += kListCap) {
-    const int cnt = build_key_list<C::BN, NW>(p.bounds, p.tpr, p.R, p.rank, p.cp, u0, min(total, u0 + kListCap), tid,
+    const int cnt = build_key_list<C::BN, NW, kListCap>(p.bounds, p.tpr, p.R, p.rank, p.cp, u0, min(total, u0 + kListCap), tid,
                                                   wave, lane, sWb, sList, sCnt);
     if (cnt == 0) continue;
     // Lane l of vl holds list slot lbase + l as this wave sees it (0 past the
@@ -786,7 +786,7 @@ __global__ __launch_bounds__(kF32Threads, 1) void fwd_f32_kernel(KParams p) {
   const int csh = 2 * wave;
   auto entry_tile = [&](int2 e) { return (e.x & 0xFF) * p.tpr + ((e.x >> 8) & 0xFFFF); };
   for (int u0 = 0; u0 < total; u0 += kListCap) {
-    const int cnt = build_key_list<C::BN, kF32Waves>(p.bounds, p.tpr, p.R, p.rank, p.cp, u0, min(total, u0 + kListCap), tid,
+    const int cnt = build_key_list<C::BN, kF32Waves, kListCap>(p.bounds, p.tpr, p.R, p.rank, p.cp, u0, min(total, u0 + kListCap), tid,
                                                   wave, lane, sWb, sList, sCnt);
     if (cnt == 0) continue;
     stage_load(entry_tile(sList[0]));

@@ -162,57 +162,79 @@ __device__ __forceinline__ int xcd_logical_block() {
 }
 
 // Lists, in ring order, the key tiles of schedule slots [u0, u1) that some wave
-// of this workgroup needs.  Slot u is ring step u / tpr (rank (rank - step) mod
-// cp) and tile u % tpr of that rank's shard (R rows a shard).  Entry .x = src |
-// i << 8; .y = class(wave w) << 2w, from the tile bounds {min pos, max pos,
-// gap lo, gap hi} (no key of the tile lies strictly between gap lo and gap hi)
-// and each wave's row bounds sWb[w] (wave_row_bounds): skip when no key can
-// lie in [min q_lo, max q_pos] outside the rows' hole, full when every key
-// lies in [max q_lo, min q_pos] and the tile is whole.
-template <int BN, int NW>
+// of this workgroup needs (u1 - u0 <= CAP).  Slot u is ring step u / tpr (rank
+// (rank - step) mod cp) and tile u % tpr of that rank's shard (R rows a
+// shard).  Entry .x = src | i << 8; .y = class(wave w) << 2w, from the tile
+// bounds {min pos, max pos, gap lo, gap hi} (no key of the tile lies strictly
+// between gap lo and gap hi) and each wave's row bounds sWb[w]
+// (wave_row_bounds): skip when no key can lie in [min q_lo, max q_pos] outside
+// the rows' hole, full when every key lies in [max q_lo, min q_pos] and the
+// tile is whole.  Thread t classifies slots u0 + t*PER .. + PER-1 with all its
+// bound loads in flight at once, and one prefix sum over the workgroup places
+// the active entries: one load latency and two barriers per pass.
+template <int BN, int NW, int CAP>
 __device__ __forceinline__ int build_key_list(const int4* bounds, int tpr, int R, int rank, int cp, int u0, int u1,
                                               int tid, int wave, int lane, const int (*sWb)[6], int2* sList,
                                               int* sCnt) {
-  int cnt = 0;
-  for (int base = u0; base < u1; base += NW * 64) {
-    const int u = base + tid;
-    bool act = false;
-    int2 entry = {0, 0};
-    if (u < u1) {
-      const int t = u / tpr;
-      const int i = u - t * tpr;
-      int src = rank - t;
-      if (src < 0) src += cp;
-      const int4 bd = bounds[src * tpr + i];
-      const bool whole = R - i * BN >= BN;
-      entry.x = src | (i << 8);
-      unsigned cls_bits = 0;
+  constexpr int PER = CAP / (NW * 64);
+  static_assert(PER >= 1 && PER < 8 && CAP % (NW * 64) == 0, "slots per thread");
+  int4 bd[PER];
+  int tile_src[PER], tile_i[PER];
 #pragma unroll
-      for (int w = 0; w < NW; ++w) {
-        int cls = kSkip;
-        if (bd.x <= sWb[w][1] && bd.y >= sWb[w][2] && !(bd.z < sWb[w][2] && sWb[w][1] < bd.w) &&
-            !(sWb[w][4] < bd.x && bd.y < sWb[w][5]))
-          cls = (whole && bd.y <= sWb[w][0] && bd.x >= sWb[w][3]) ? kFull : kPartial;
-        cls_bits |= (unsigned)cls << (2 * w);
-        act |= cls != kSkip;
-      }
-      entry.y = (int)cls_bits;
-    }
-    const unsigned long long bal = __ballot(act);
-    const int before = __popcll(bal & ((1ull << lane) - 1ull));
-    if (lane == 0) sCnt[wave] = __popcll(bal);
-    __syncthreads();
-    int off = cnt, tot = 0;
+  for (int j = 0; j < PER; ++j) {
+    const int u = min(u0 + tid * PER + j, u1 - 1);
+    const int t = u / tpr;
+    tile_i[j] = u - t * tpr;
+    int src = rank - t;
+    if (src < 0) src += cp;
+    tile_src[j] = src;
+    bd[j] = bounds[src * tpr + tile_i[j]];
+  }
+  int2 ent[PER];
+  int c = 0;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const bool in = u0 + tid * PER + j < u1;
+    const bool whole = R - tile_i[j] * BN >= BN;
+    unsigned cls_bits = 0;
+    bool act = false;
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
-      off += w < wave ? sCnt[w] : 0;
-      tot += sCnt[w];
+      int cls = kSkip;
+      if (bd[j].x <= sWb[w][1] && bd[j].y >= sWb[w][2] && !(bd[j].z < sWb[w][2] && sWb[w][1] < bd[j].w) &&
+          !(sWb[w][4] < bd[j].x && bd[j].y < sWb[w][5]))
+        cls = (whole && bd[j].y <= sWb[w][0] && bd[j].x >= sWb[w][3]) ? kFull : kPartial;
+      cls_bits |= (unsigned)cls << (2 * w);
+      act |= cls != kSkip;
     }
-    if (act) sList[off + before] = entry;
-    cnt += tot;
-    __syncthreads();
+    act = act && in;
+    // .x stays below 2^24 (src < 256, tile < 65536): the sign bit marks an
+    // entry no wave needs
+    ent[j] = int2{tile_src[j] | (tile_i[j] << 8) | (act ? 0 : (int)0x80000000), (int)cls_bits};
+    c += act ? 1 : 0;
   }
-  return cnt;
+  // Exclusive prefix of c over the wave from the ballots of its bits (c < 8).
+  const unsigned long long lt = (1ull << lane) - 1ull;
+  int before = 0, wtot = 0;
+#pragma unroll
+  for (int b = 0; b < 3; ++b) {
+    const unsigned long long m = __ballot((c >> b) & 1);
+    before += __popcll(m & lt) << b;
+    wtot += __popcll(m) << b;
+  }
+  if (lane == 0) sCnt[wave] = wtot;
+  __syncthreads();
+  int off = before, tot = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    off += w < wave ? sCnt[w] : 0;
+    tot += sCnt[w];
+  }
+#pragma unroll
+  for (int j = 0; j < PER; ++j)
+    if (ent[j].x >= 0) sList[off++] = ent[j];
+  __syncthreads();
+  return tot;
 }
 
 }  // namespace dev
