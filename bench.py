@@ -201,6 +201,51 @@ PROBES = {
 }
 
 
+def dq_atomics_probe(L, args, np, torch):
+    """The dQ reduction traffic a single-pass backward would add on the
+    131072-token cp = 8 workload (rank 0): every (256-key dK/dV workgroup,
+    query head, 64-row query tile) pair with allowed keys adds a 64 x 128 fp32
+    block into dQ with float atomics, in the dK/dV kernel's grid and order
+    (cp_probe_dq_atomics)."""
+    import ctypes
+    import context_causal_attention_amd as cpa
+    S, cp, hkv, g, d = 131072, 8, 8, 4, 128
+    R = S // cp
+    qp = cpa.cp_shard_zigzag(S, cp, 0).astype(np.int32)
+    kp = cpa.cp_unshard_zigzag(S, cp).astype(np.int32)
+    # allowed (key block, query tile) pairs: a query at or after the block's first key
+    kmin = kp.reshape(-1, 256).min(1)
+    qmax = qp.reshape(-1, 64).max(1)
+    pairs = int((qmax[None, :] >= kmin[:, None]).sum()) * hkv * g
+    nbytes = pairs * 64 * d * 4
+    dev = torch.device("cuda:0")
+    qd, kd = torch.from_numpy(qp).to(dev), torch.from_numpy(kp).to(dev)
+    dq = torch.zeros(hkv * g * R * d, dtype=torch.float32, device=dev)
+    L.cp_probe_dq_atomics.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p] + [ctypes.c_int] * 5 + \
+        [ctypes.c_void_p]
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def launch():
+        rc = L.cp_probe_dq_atomics(ctypes.c_void_p(qd.data_ptr()), ctypes.c_void_p(kd.data_ptr()),
+                                   ctypes.c_void_p(dq.data_ptr()), R, R, cp, hkv, g, ctypes.c_void_p(stream))
+        if rc != 0:
+            raise RuntimeError(f"dq atomics probe: hip error {rc}")
+    launch()
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(max(3, args.steps)):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(); launch(); b.record()
+        b.synchronize()
+        times.append(a.elapsed_time(b))
+    ms = float(np.median(times))
+    r = {"what": "fp32 atomic adds of the dQ partials of a single-pass backward, 131072 tokens, cp = 8, rank 0, "
+                 "in the dK/dV grid and order", "ms": round(ms, 3), "block_pairs": pairs,
+         "atomic_GB": round(nbytes / 1e9, 2), "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1)}
+    print(f"[probe] dq_atomics: {r}", file=sys.stderr, flush=True)
+    return r
+
+
 def probe_bench(args):
     """Unit throughput of one MI355X under the attention kernels' occupancy
     (one 8-wave workgroup per CU, two waves per SIMD), from the probe kernels
@@ -266,6 +311,7 @@ def probe_bench(args):
             r["cycles_per_unit"] = round(t * mhz * 1e6 / unit, 2)
         res[name] = r
         print(f"[probe] {name}: {r}", file=sys.stderr, flush=True)
+    res["dq_atomics"] = dq_atomics_probe(L, args, np, torch)
     line = {"metric": "unit throughput probes (one 8-wave workgroup per CU)", "value": res["mfma"]["TFLOP/s"],
             "unit": "TFLOP/s (sustained bf16 MFMA)", "n_gpus": 1, "steps": max(3, args.steps), "warmup": 1,
             "higher_is_better": True, "dtype": "bf16", "data": "synthetic", "config": {"workload": "probe"},

@@ -25,6 +25,7 @@
 // kernel's duration.
 #include <hip/hip_runtime.h>
 
+#include <climits>
 #include <cstdint>
 
 namespace {
@@ -161,7 +162,64 @@ __global__ __launch_bounds__(512, 1) void probe_kernel(float* out, unsigned long
   }
 }
 
+// The dQ reduction traffic a single-pass backward would make: the dK/dV
+// kernel's grid (one workgroup per 256 keys of a kv head, dealt to the XCDs as
+// that kernel deals them) walks its query heads and 64-row query tiles in the
+// same order, and for every tile holding a query at or after its first key
+// (the causal rule of a dense ring) adds a 64 x 128 fp32 block into dQ with
+// global float atomics, as the workgroup's reduced partial would be added.
+__global__ __launch_bounds__(512, 1) void dq_atomics_kernel(const int* __restrict__ q_pos, const int* __restrict__ k_pos,
+                                                            float* __restrict__ dq, int sq, int R, int cp, int hkv,
+                                                            int g, float val) {
+  constexpr int KPW = 256, QT = 64, D = 128;
+  const int tg = (R + KPW - 1) / KPW;
+  const int nblk = gridDim.x, bid = blockIdx.x;
+  const int per_xcd = nblk / 8;
+  int logical = bid < per_xcd * 8 ? (bid % 8) * per_xcd + bid / 8 : bid;
+  const int grp = logical % (cp * tg);
+  const int kvh = (logical / (cp * tg)) % hkv;
+  const int src = grp / tg, ig = grp - src * tg;
+  const int key0 = src * R + ig * KPW;
+  const int nkeys = min(KPW, R - ig * KPW);
+  __shared__ int sMin[8];
+  // smallest key position of the workgroup
+  int kmin = INT_MAX;
+  for (int k = threadIdx.x; k < nkeys; k += 512) kmin = min(kmin, k_pos[key0 + k]);
+  for (int o = 1; o < 64; o <<= 1) kmin = min(kmin, __shfl_xor(kmin, o));
+  if ((threadIdx.x & 63) == 0) sMin[threadIdx.x >> 6] = kmin;
+  __syncthreads();
+  kmin = sMin[0];
+  for (int w = 1; w < 8; ++w) kmin = min(kmin, sMin[w]);
+  const int nqt = (sq + QT - 1) / QT;
+  for (int hg = 0; hg < g; ++hg) {
+    float* head = dq + (long long)(kvh * g + hg) * sq * D;
+    for (int t = 0; t < nqt; ++t) {
+      // largest query position of the tile (64 rows, one per lane of wave 0's
+      // view; every wave reads them, so no barrier is needed)
+      const int r = t * QT + (threadIdx.x & 63);
+      int qmax = r < sq ? q_pos[r] : INT_MIN;
+      for (int o = 1; o < 64; o <<= 1) qmax = max(qmax, __shfl_xor(qmax, o));
+      if (qmax < kmin) continue;
+      const int rows = min(QT, sq - t * QT);
+      float* blk = head + (long long)t * QT * D;
+      for (int e = threadIdx.x; e < rows * D; e += 512) atomicAdd(blk + e, val);
+    }
+  }
+}
+
 }  // namespace
+
+// Runs dq_atomics_kernel over the dK/dV grid of a dense causal ring (cp shards
+// of R keys, hkv kv heads of g query heads each, sq query rows of positions
+// q_pos, keys of positions k_pos, all device); dq (device) holds hkv * g * sq
+// * 128 floats.  Returns a hipError_t.
+extern "C" int cp_probe_dq_atomics(const int* q_pos, const int* k_pos, float* dq, int sq, int R, int cp, int hkv,
+                                   int g, hipStream_t stream) {
+  const int tg = (R + 255) / 256;
+  hipLaunchKernelGGL(dq_atomics_kernel, dim3((unsigned)(cp * tg * hkv)), dim3(512), 0, stream, q_pos, k_pos, dq,
+                     sq, R, cp, hkv, g, 1.0f / 1024);
+  return (int)hipGetLastError();
+}
 
 // Runs probe `kind` on `blocks` workgroups of 512 threads with `iters`
 // iterations; out (device) holds blocks * 512 floats, clk (device) 2 * blocks
