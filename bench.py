@@ -198,6 +198,7 @@ PROBES = {
     8: ("mfma_agpr", "as mfma, accumulators in AGPRs"),
     6: ("mix_same_wave_agpr", "as mix_same_wave, MFMA accumulators in AGPRs"),
     7: ("mix_split_waves_agpr", "as mix_split_waves, MFMA accumulators in AGPRs"),
+    9: ("mix_same_wave_2mfma", "as mix_same_wave with two MFMAs per step (the forward's ratio)"),
 }
 
 
@@ -269,7 +270,7 @@ def probe_bench(args):
     clk = torch.zeros(2 * blocks, dtype=torch.int64, device="cuda:0")
     stream = torch.cuda.current_stream().cuda_stream
     # iterations per launch, sized for ~20-60 ms per launch
-    iters = {0: 20000, 5: 20000, 8: 20000, 1: 100000, 2: 100000, 3: 40000, 4: 40000, 6: 40000, 7: 40000}
+    iters = {0: 20000, 5: 20000, 8: 20000, 1: 100000, 2: 100000, 3: 40000, 4: 40000, 6: 40000, 7: 40000, 9: 40000}
     res = {}
     for kind, (name, what) in PROBES.items():
         def launch():
@@ -301,6 +302,10 @@ def probe_bench(args):
         elif kind in (1, 2):
             unit = 2 * it * 32                                      # wave64 instructions per SIMD
             per_simd = {"instructions_per_simd": unit}
+        elif kind == 9:
+            unit = 2 * it * 8                                       # steps (two MFMAs each) per SIMD
+            flop = blocks * 8 * it * 8 * 2 * 32768
+            per_simd = {"mfma_steps_per_simd": unit, "TFLOP/s": round(flop / t / 1e12, 1)}
         else:
             same = kind in (3, 6)
             unit = 2 * it * 8 if same else it * 8                   # MFMA steps per SIMD

@@ -15,6 +15,8 @@
 //           work and vector work come from different waves;
 //   kind 5  MFMA only, one accumulator chain per wave (each MFMA depends on
 //           the previous one);
+//   kind 9  as kind 3 with two MFMAs per step (the forward's own ratio: per
+//           pair of scores, one score MFMA and one P V MFMA);
 //   kinds 6, 7, 8  as 3, 4 and 0 with the MFMA accumulators held in the
 //           accumulation registers (AGPRs) instead of VGPRs (the MFMAs are
 //           written as inline assembly with an AGPR operand; the results are
@@ -125,7 +127,7 @@ __global__ __launch_bounds__(512, 1) void probe_kernel(float* out, unsigned long
       s[2 * m] = __builtin_bit_cast(float, pk);
       s[2 * m + 1] = e1;
     };
-    constexpr bool AG = KIND >= 6;
+    constexpr bool AG = KIND >= 6 && KIND <= 8;
     auto mm = [&](int m) {
       if constexpr (AG) mfma_agpr(acc[m & 3], a, b);
       else acc[m & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[m & 3], 0, 0, 0);
@@ -135,6 +137,15 @@ __global__ __launch_bounds__(512, 1) void probe_kernel(float* out, unsigned long
 #pragma unroll
         for (int m = 0; m < 8; ++m) {
           mm(m);
+          vec(m);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+    } else if (KIND == 9) {
+      for (int i = 0; i < iters; ++i)
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+          mm(m);
+          mm(m + 1);
           vec(m);
           __builtin_amdgcn_sched_barrier(0);
         }
@@ -237,6 +248,7 @@ extern "C" int cp_probe_run(int kind, int blocks, int iters, float* out, unsigne
     case 6: hipLaunchKernelGGL(probe_kernel<6>, g, t, 0, stream, out, clk, iters); break;
     case 7: hipLaunchKernelGGL(probe_kernel<7>, g, t, 0, stream, out, clk, iters); break;
     case 8: hipLaunchKernelGGL(probe_kernel<8>, g, t, 0, stream, out, clk, iters); break;
+    case 9: hipLaunchKernelGGL(probe_kernel<9>, g, t, 0, stream, out, clk, iters); break;
     default: return (int)hipErrorInvalidValue;
   }
   return (int)hipGetLastError();
