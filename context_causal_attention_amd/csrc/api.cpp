@@ -543,6 +543,10 @@ extern "C" int cp_attn_bwd_delta(const cp_shape* s, const void* dout, const void
   if (!delta) return fail(CP_EINVAL, "delta is null");
   if (int rc = check_strides(s->o_str, s->out_dtype, "o")) return rc;
   if (s->o_str[2] < s->d || s->q_str[2] < s->d) return fail(CP_EINVAL, "dout/o row strides must be at least d");
+  // The kernel indexes rows in 32 bits; 2^31 rows of bf16 dO and O would
+  // already take over 500 GB at d = 64.
+  if ((int64_t)s->b * s->hq * s->sq >= (int64_t)1 << 31)
+    return fail(CP_EINVAL, "b x hq x sq = %lld rows reach 2^31", (long long)((int64_t)s->b * s->hq * s->sq));
   BwdArgs a{};
   for (int i = 0; i < 3; ++i) {
     a.q_str[i] = s->q_str[i];

@@ -122,29 +122,55 @@ __global__ __launch_bounds__(64) void query_prep_kernel(BParams p, const float* 
   dlt[(long long)bh * p.sq_pad + r0 + tid] = ok ? -delta[idx] : 0.f;
 }
 
-// delta_q = sum_d dO[q, d] * O[q, d]; one half-wave (32 lanes) per row.
+// delta_q = sum_d dO[q, d] * O[q, d] for rows q = (b*Hq + h)*sq + i (fewer
+// than 2^31 rows, so row arithmetic is 32-bit).  32 lanes share a row, D/32
+// consecutive elements a lane, so a half-wave reads a row's dO and O as one
+// contiguous segment each; the 8 half-waves of a block take 8 consecutive
+// rows a step, and kDeltaSteps steps with every load issued before the first
+// product keep that many rows of loads in flight per thread.
+constexpr int kDeltaSteps = 2;
+constexpr int kDeltaRowsPerBlock = 8 * kDeltaSteps;
 template <int D, typename OT>
 __global__ __launch_bounds__(256) void delta_kernel(const char* __restrict__ dout, long long do_sb, long long do_sh,
                                                     long long do_ss, const OT* __restrict__ o, long long o_sb,
                                                     long long o_sh, long long o_ss, float* __restrict__ delta, int Hq,
                                                     int sq, long long rows) {
-  const long long r = ((long long)blockIdx.x * 256 + threadIdx.x) / 32;
+  constexpr int PER = D / 32;  // elements per lane
+  typedef __bf16 bfv __attribute__((__vector_size__(PER * sizeof(__bf16))));
+  typedef OT ov_t __attribute__((__vector_size__(PER * sizeof(OT))));
   const int lane = threadIdx.x & 31;
-  float acc = 0.f;
-  if (r < rows) {
-    const long long bh = r / sq;
-    const int i = (int)(r - bh * sq);
-    const int b = (int)(bh / Hq), h = (int)(bh % Hq);
-    constexpr int PER = D / 32;  // elements per lane
-    const __bf16* dp = reinterpret_cast<const __bf16*>(dout) + (long long)b * do_sb + (long long)h * do_sh +
-                       (long long)i * do_ss + lane * PER;
-    const OT* op = o + (long long)b * o_sb + (long long)h * o_sh + (long long)i * o_ss + lane * PER;
+  const unsigned r0 = blockIdx.x * (unsigned)kDeltaRowsPerBlock + (threadIdx.x >> 5);
+  bfv dv[kDeltaSteps];
+  ov_t ov[kDeltaSteps];
 #pragma unroll
-    for (int e = 0; e < PER; ++e) acc += (float)dp[e] * (float)op[e];
+  for (int u = 0; u < kDeltaSteps; ++u) {
+    const unsigned r = r0 + 8u * u;
+    if (r < rows) {
+      const unsigned bh = r / (unsigned)sq, i = r - bh * (unsigned)sq;
+      const unsigned b = bh / (unsigned)Hq, h = bh - b * (unsigned)Hq;
+      const __bf16* dp = reinterpret_cast<const __bf16*>(dout) + (long long)b * do_sb + (long long)h * do_sh +
+                         (long long)i * do_ss + lane * PER;
+      const OT* op = o + (long long)b * o_sb + (long long)h * o_sh + (long long)i * o_ss + lane * PER;
+      dv[u] = *reinterpret_cast<const bfv*>(dp);
+      ov[u] = *reinterpret_cast<const ov_t*>(op);
+    } else {
+#pragma unroll
+      for (int e = 0; e < PER; ++e) {
+        dv[u][e] = (__bf16)0.f;
+        ov[u][e] = (OT)0.f;
+      }
+    }
   }
 #pragma unroll
-  for (int off = 16; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 32);
-  if (r < rows && lane == 0) delta[r] = acc;
+  for (int u = 0; u < kDeltaSteps; ++u) {
+    float acc = 0.f;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) acc += (float)dv[u][e] * (float)ov[u][e];
+#pragma unroll
+    for (int off = 16; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 32);
+    const unsigned r = r0 + 8u * u;
+    if (r < rows && lane == 0) delta[r] = acc;
+  }
 }
 
 // ============================================================================
@@ -955,7 +981,7 @@ namespace {
 template <int D, typename OT>
 hipError_t launch_delta_t(const BwdArgs& a, hipStream_t stream) {
   const long long rows = (long long)a.b * a.hq * a.sq;
-  const long long nblk = (rows * 32 + 255) / 256;
+  const long long nblk = (rows + bwdk::kDeltaRowsPerBlock - 1) / bwdk::kDeltaRowsPerBlock;
   hipLaunchKernelGGL((bwdk::delta_kernel<D, OT>), dim3((unsigned)nblk), dim3(256), 0, stream,
                      static_cast<const char*>(a.dout), (long long)a.q_str[0], (long long)a.q_str[1],
                      (long long)a.q_str[2], static_cast<const OT*>(a.o), (long long)a.o_str[0], (long long)a.o_str[1],

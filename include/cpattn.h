@@ -303,7 +303,7 @@ size_t cp_attn_bwd_workspace(const cp_shape* s, int32_t cp);
 /* delta_i = sum_d dO[i,d] O[i,d] for the sq rows of every (batch, query head).
  * dout (device bf16, strides q_str) [b,hq,sq,d]; o (device, out_dtype, strides
  * o_str) the final merged output of the forward; writes delta (device fp32,
- * contiguous [b,hq,sq]). */
+ * contiguous [b,hq,sq]).  b x hq x sq must stay below 2^31 rows (CP_EINVAL). */
 int cp_attn_bwd_delta(const cp_shape* s, const void* dout, const void* o, float* delta,
                       hipStream_t stream);
 

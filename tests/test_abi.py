@@ -435,6 +435,10 @@ def test_bwd_delta_and_partial_validation():
     assert L.cp_attn_bwd_delta(ctypes.byref(s), 0, FAKE, FAKE, None) == cpa.CP_EINVAL
     assert L.cp_attn_bwd_delta(ctypes.byref(s), FAKE, FAKE, 0, None) == cpa.CP_EINVAL
     assert L.cp_attn_bwd_delta(ctypes.byref(_shape(sq=0)), 0, 0, 0, None) == cpa.CP_OK
+    # 2^31 rows or more (the kernel's row index is 32-bit)
+    assert L.cp_attn_bwd_delta(ctypes.byref(_shape(b=4, hq=512, hkv=512, sq=1 << 20)), FAKE, FAKE, FAKE,
+                               None) == cpa.CP_EINVAL
+    assert "2^31" in cpa.cp_last_error()
     s5 = _shape(hq=5, hkv=2)
     assert L.cp_attn_partial_bwd(ctypes.byref(s5), *([FAKE] * 6), FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE,
                                  1 << 30, None) == cpa.CP_EINVAL
