@@ -29,9 +29,11 @@ per-token cost of attention the Accelerate context-parallel guide quotes
 backward's recomputed Q K^T (10*d*Hq, 14*d*Hq for forward plus backward) is
 reported beside it, and so is the rate of the MFMA work the kernels execute.
 The clocks sampled during the timed steps give the peak at the measured sclk.
+With the backward, ``delta_alone`` times cp_attn_bwd_delta on the first rank's
+(dO, O) after the timed steps, launched back to back, with its HBM rate.
 
-Prints one JSON line.  ``--gpus N`` with N > 1 exits: this build runs on one
-GPU and every figure is that GPU's.
+Prints one JSON line.  ``--gpus N`` with N > 1 exits: the bench measures one
+GPU's share of the ring and every figure is that GPU's.
 """
 from __future__ import annotations
 
@@ -470,6 +472,27 @@ def main():
     rooflines = {ps: roof(ps) for ps in passes}
     dominant = max(passes, key=lambda ps: rooflines[ps]["launch_ms"])
 
+    # delta alone, after the timed steps: launches back to back on the first
+    # rank's (dO, O), so no other kernel's dirty cache lines drain during it
+    # (inside a step it follows the forward's output writes and the zeroing of
+    # dQ).
+    delta_alone = None
+    if bwd:
+        r0 = ranks[0]
+        o_r, (do_r, dl_r) = fplans[r0].out, deltas[r0]
+        dev_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(20)]
+        torch.cuda.synchronize()
+        for a, b in dev_ev:
+            a.record(stream)
+            cpa.cp_attn_bwd_delta(do_r, o_r, dl_r)
+            b.record(stream)
+        torch.cuda.synchronize()
+        ts = sorted(a.elapsed_time(b) for a, b in dev_ev)
+        dbytes = do_r.numel() * do_r.element_size() + o_r.numel() * o_r.element_size() + dl_r.numel() * 4
+        med = ts[len(ts) // 2]
+        delta_alone = {"launches": len(ts), "median_us": round(med * 1e3, 2), "bytes": dbytes,
+                       "GB/s": round(dbytes / (med * 1e-3) / 1e9, 1), "peak_GB/s": PEAK_HBM_GBS}
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w, full, idx[ranks[0]], allp, cu, args.cpu_seconds, ranks[0], bwd)
@@ -516,6 +539,7 @@ def main():
         "passes": per_pass,
         "roofline": rooflines[dominant],
         "roofline_by_pass": rooflines,
+        **({"delta_alone": delta_alone} if delta_alone else {}),
         "cpu_baseline": cpu,
     }
     if balance is not None:
