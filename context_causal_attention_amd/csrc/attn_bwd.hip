@@ -127,8 +127,11 @@ __global__ __launch_bounds__(64) void query_prep_kernel(BParams p, const float* 
 // consecutive elements a lane, so a half-wave reads a row's dO and O as one
 // contiguous segment each; the 8 half-waves of a block take 8 consecutive
 // rows a step, and kDeltaSteps steps with every load issued before the first
-// product keep that many rows of loads in flight per thread.
-constexpr int kDeltaSteps = 2;
+// product keep that many rows of loads in flight per thread.  One step: two
+// or four, though up to 19% faster when the kernel runs alone, were 11%
+// slower inside the backward step, where it follows the forward's output
+// writes and the zeroing of dQ.
+constexpr int kDeltaSteps = 1;
 constexpr int kDeltaRowsPerBlock = 8 * kDeltaSteps;
 template <int D, typename OT>
 __global__ __launch_bounds__(256) void delta_kernel(const char* __restrict__ dout, long long do_sb, long long do_sh,
