@@ -201,6 +201,9 @@ PROBES = {
     6: ("mix_same_wave_agpr", "as mix_same_wave, MFMA accumulators in AGPRs"),
     7: ("mix_split_waves_agpr", "as mix_split_waves, MFMA accumulators in AGPRs"),
     9: ("mix_same_wave_2mfma", "as mix_same_wave with two MFMAs per step (the forward's ratio)"),
+    10: ("mfma_lds", "as mfma with each MFMA's A operand read from LDS (1 KB a wave, four steps ahead)"),
+    11: ("mix_same_wave_lds", "as mix_same_wave with the MFMA operand read from LDS (the forward's score phase)"),
+    12: ("mix_same_wave_2mfma_lds", "as mix_same_wave_2mfma with both MFMA operands read from LDS"),
 }
 
 
@@ -272,7 +275,8 @@ def probe_bench(args):
     clk = torch.zeros(2 * blocks, dtype=torch.int64, device="cuda:0")
     stream = torch.cuda.current_stream().cuda_stream
     # iterations per launch, sized for ~20-60 ms per launch
-    iters = {0: 20000, 5: 20000, 8: 20000, 1: 100000, 2: 100000, 3: 40000, 4: 40000, 6: 40000, 7: 40000, 9: 40000}
+    iters = {0: 20000, 5: 20000, 8: 20000, 1: 100000, 2: 100000, 3: 40000, 4: 40000, 6: 40000, 7: 40000, 9: 40000,
+             10: 40000, 11: 40000, 12: 40000}
     res = {}
     for kind, (name, what) in PROBES.items():
         def launch():
@@ -304,6 +308,12 @@ def probe_bench(args):
         elif kind in (1, 2):
             unit = 2 * it * 32                                      # wave64 instructions per SIMD
             per_simd = {"instructions_per_simd": unit}
+        elif kind >= 10:
+            per_it = 16 if kind == 12 else 8                         # MFMAs per wave per iteration
+            unit = 2 * it * per_it                                  # MFMAs per SIMD
+            flop = blocks * 8 * it * per_it * 32768
+            per_simd = {"mfma_per_simd": unit, "TFLOP/s": round(flop / t / 1e12, 1),
+                        "pct_of_2516.6": round(100 * flop / t / 1e12 / PEAK_BF16_TFLOPS, 1)}
         elif kind == 9:
             unit = 2 * it * 8                                       # steps (two MFMAs each) per SIMD
             flop = blocks * 8 * it * 8 * 2 * 32768

@@ -20,7 +20,11 @@
 //   kinds 6, 7, 8  as 3, 4 and 0 with the MFMA accumulators held in the
 //           accumulation registers (AGPRs) instead of VGPRs (the MFMAs are
 //           written as inline assembly with an AGPR operand; the results are
-//           read only after the loop, behind enough wait states).
+//           read only after the loop, behind enough wait states);
+//   kinds 10, 11, 12  as 0, 3 and 9 (8 steps an iteration) with each MFMA's
+//           A operand read from LDS (one 16-byte read per lane, 1 KB per wave,
+//           four steps ahead), as the attention kernels read their K and V
+//           tiles.
 // Results are written to out so that no work is dropped.  Wave 0 of every
 // workgroup also records the shader clock counter (s_memtime) before and after
 // the work, so the host can tell the clock the probe ran at: cycles over the
@@ -132,7 +136,32 @@ __global__ __launch_bounds__(512, 1) void probe_kernel(float* out, unsigned long
       if constexpr (AG) mfma_agpr(acc[m & 3], a, b);
       else acc[m & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[m & 3], 0, 0, 0);
     };
-    if (KIND == 3 || KIND == 6) {
+    if constexpr (KIND >= 10) {
+      __shared__ bf16x8 lbuf[2048];
+      for (int j = threadIdx.x; j < 2048; j += 512) lbuf[j] = seed_operand(j & 15);
+      __syncthreads();
+      const int lane = threadIdx.x & 63;
+      constexpr int NR = KIND == 12 ? 2 : 1;  // MFMAs (and LDS reads) per step
+      constexpr int PF = 4;                   // steps read ahead
+      // read r: 1 KB block r % 32 of the buffer, lane l its 16 bytes l
+      auto ld = [&](int r) { return lbuf[((r & 31) << 6) + lane]; };
+      bf16x8 op[8][NR];  // step m's operands in op[m % 8]
+#pragma unroll
+      for (int q = 0; q < PF; ++q)
+#pragma unroll
+        for (int n = 0; n < NR; ++n) op[q][n] = ld(q * NR + n);
+      for (int i = 0; i < iters; ++i)
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+#pragma unroll
+          for (int n = 0; n < NR; ++n) op[(m + PF) & 7][n] = ld((i * 8 + m + PF) * NR + n);
+#pragma unroll
+          for (int n = 0; n < NR; ++n)
+            acc[(m * NR + n) & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[m & 7][n], b, acc[(m * NR + n) & 3], 0, 0, 0);
+          if constexpr (KIND != 10) vec(m);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+    } else if (KIND == 3 || KIND == 6) {
       for (int i = 0; i < iters; ++i)
 #pragma unroll
         for (int m = 0; m < 8; ++m) {
@@ -249,6 +278,9 @@ extern "C" int cp_probe_run(int kind, int blocks, int iters, float* out, unsigne
     case 7: hipLaunchKernelGGL(probe_kernel<7>, g, t, 0, stream, out, clk, iters); break;
     case 8: hipLaunchKernelGGL(probe_kernel<8>, g, t, 0, stream, out, clk, iters); break;
     case 9: hipLaunchKernelGGL(probe_kernel<9>, g, t, 0, stream, out, clk, iters); break;
+    case 10: hipLaunchKernelGGL(probe_kernel<10>, g, t, 0, stream, out, clk, iters); break;
+    case 11: hipLaunchKernelGGL(probe_kernel<11>, g, t, 0, stream, out, clk, iters); break;
+    case 12: hipLaunchKernelGGL(probe_kernel<12>, g, t, 0, stream, out, clk, iters); break;
     default: return (int)hipErrorInvalidValue;
   }
   return (int)hipGetLastError();
