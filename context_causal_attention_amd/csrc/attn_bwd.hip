@@ -566,12 +566,24 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(BParams p) {
   for (int u0 = 0; u0 < total; u0 += C::LIST) {
     const int cnt = build(u0, min(total, u0 + C::LIST));
     if (cnt == 0) continue;
+    // Lane l of (lx, ly) holds list slot lb + l (0 past the end): a tile
+    // takes its entries with v_readlane, not an LDS read per tile; the lane
+    // vectors are refilled from LDS once per 63 tiles.
+    int lb = 0, lx = 0, ly = 0;
+    auto fill = [&](int b0) {
+      lb = b0;
+      int2 e = {0, 0};
+      if (b0 + lane < cnt) e = sList[b0 + lane];
+      lx = e.x;
+      ly = e.y;
+    };
     auto ent = [&](int j) {
       int2 e;
-      e.x = __builtin_amdgcn_readfirstlane(sList[j].x);
-      e.y = __builtin_amdgcn_readfirstlane(sList[j].y);
+      e.x = __builtin_amdgcn_readlane(lx, j - lb);
+      e.y = __builtin_amdgcn_readlane(ly, j - lb);
       return e;
     };
+    fill(0);
     const std::integral_constant<int, 0> b0{};
     const std::integral_constant<int, 1> b1{};
     issue(b0, ent(0).x);
@@ -579,6 +591,7 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(BParams p) {
     __syncthreads();
     // Tile j from buffer B while tile j+1 is copied into the other buffer.
     auto tile = [&](auto bc, int j) {
+      if (j + 1 - lb >= 64) fill(j);
       if (j + 1 < cnt) issue(std::integral_constant<int, 1 - decltype(bc)::value>{}, ent(j + 1).x);
       const int cls = (int)(((unsigned)ent(j).y >> csh) & 3);
       if (cls != kSkip) {
@@ -862,12 +875,24 @@ __global__ __launch_bounds__(512, 1) void dq_kernel(BParams p) {
     const int cnt = build_key_list<kKT, NW, C::LIST>(p.kbounds, p.tpr, p.R, p.rank, p.cp, u0, min(total, u0 + C::LIST), tid,
                                             wave, lane, sWb, sList, sCnt);
     if (cnt == 0) continue;
+    // Lane l of (lx, ly) holds list slot lb + l (0 past the end): a tile
+    // takes its entries with v_readlane, not an LDS read per tile; the lane
+    // vectors are refilled from LDS once per 63 tiles.
+    int lb = 0, lx = 0, ly = 0;
+    auto fill = [&](int b0) {
+      lb = b0;
+      int2 e = {0, 0};
+      if (b0 + lane < cnt) e = sList[b0 + lane];
+      lx = e.x;
+      ly = e.y;
+    };
     auto ent = [&](int j) {
       int2 e;
-      e.x = __builtin_amdgcn_readfirstlane(sList[j].x);
-      e.y = __builtin_amdgcn_readfirstlane(sList[j].y);
+      e.x = __builtin_amdgcn_readlane(lx, j - lb);
+      e.y = __builtin_amdgcn_readlane(ly, j - lb);
       return e;
     };
+    fill(0);
     const std::integral_constant<int, 0> b0{};
     const std::integral_constant<int, 1> b1{};
     issue(b0, ent(0).x);
@@ -875,6 +900,7 @@ __global__ __launch_bounds__(512, 1) void dq_kernel(BParams p) {
     __syncthreads();
     // Tile j from buffer B while tile j+1 is copied into the other buffer.
     auto tile = [&](auto bc, int j) {
+      if (j + 1 - lb >= 64) fill(j);
       if (j + 1 < cnt) issue(std::integral_constant<int, 1 - decltype(bc)::value>{}, ent(j + 1).x);
       const int cls = (int)(((unsigned)ent(j).y >> csh) & 3);
       if (cls != kSkip) {
