@@ -24,7 +24,10 @@
 //   kinds 10, 11, 12  as 0, 3 and 9 (8 steps an iteration) with each MFMA's
 //           A operand read from LDS (one 16-byte read per lane, 1 KB per wave,
 //           four steps ahead), as the attention kernels read their K and V
-//           tiles.
+//           tiles;
+//   kind 13  as 11 with each exponential replaced by an FMA (same instruction
+//           count), to tell the exponential's own cost from the rest of the
+//           mix.
 // Results are written to out so that no work is dropped.  Wave 0 of every
 // workgroup also records the shader clock counter (s_memtime) before and after
 // the work, so the host can tell the clock the probe ran at: cycles over the
@@ -120,9 +123,13 @@ __global__ __launch_bounds__(512, 1) void probe_kernel(float* out, unsigned long
     float s[16], lsum = 0.f;
 #pragma unroll
     for (int j = 0; j < 16; ++j) s[j] = -0.01f * (float)((threadIdx.x + j) & 31);
+    auto ex = [](float x) {
+      if constexpr (KIND == 13) return __builtin_fmaf(x, 0.25f, 0.8f);  // in (0.7, 0.9) as exp2 gives
+      else return __builtin_amdgcn_exp2f(x);
+    };
     auto vec = [&](int m) {
-      const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * m], 0.18f, -0.5f));
-      const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * m + 1], 0.18f, -0.5f));
+      const float e0 = ex(__builtin_fmaf(s[2 * m], 0.18f, -0.5f));
+      const float e1 = ex(__builtin_fmaf(s[2 * m + 1], 0.18f, -0.5f));
       const bf16x2 pk = __builtin_convertvector((f32x2){e0, e1}, bf16x2);
       lsum += e0 + e1;
       // The pair's bf16 bits read as fp32 are about e1 (its high half), so the
@@ -281,6 +288,7 @@ extern "C" int cp_probe_run(int kind, int blocks, int iters, float* out, unsigne
     case 10: hipLaunchKernelGGL(probe_kernel<10>, g, t, 0, stream, out, clk, iters); break;
     case 11: hipLaunchKernelGGL(probe_kernel<11>, g, t, 0, stream, out, clk, iters); break;
     case 12: hipLaunchKernelGGL(probe_kernel<12>, g, t, 0, stream, out, clk, iters); break;
+    case 13: hipLaunchKernelGGL(probe_kernel<13>, g, t, 0, stream, out, clk, iters); break;
     default: return (int)hipErrorInvalidValue;
   }
   return (int)hipGetLastError();
