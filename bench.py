@@ -205,6 +205,7 @@ PROBES = {
     11: ("mix_same_wave_lds", "as mix_same_wave with the MFMA operand read from LDS (the forward's score phase)"),
     12: ("mix_same_wave_2mfma_lds", "as mix_same_wave_2mfma with both MFMA operands read from LDS"),
     13: ("mix_same_wave_lds_noexp", "as mix_same_wave_lds with each exponential replaced by an FMA"),
+    14: ("mix_same_wave_lds_2step", "as mix_same_wave_lds with two steps between scheduling barriers"),
 }
 
 
@@ -277,7 +278,7 @@ def probe_bench(args):
     stream = torch.cuda.current_stream().cuda_stream
     # iterations per launch, sized for ~20-60 ms per launch
     iters = {0: 20000, 5: 20000, 8: 20000, 1: 100000, 2: 100000, 3: 40000, 4: 40000, 6: 40000, 7: 40000, 9: 40000,
-             10: 40000, 11: 40000, 12: 40000, 13: 40000}
+             10: 40000, 11: 40000, 12: 40000, 13: 40000, 14: 40000}
     res = {}
     for kind, (name, what) in PROBES.items():
         def launch():

@@ -27,7 +27,9 @@
 //           tiles;
 //   kind 13  as 11 with each exponential replaced by an FMA (same instruction
 //           count), to tell the exponential's own cost from the rest of the
-//           mix.
+//           mix;
+//   kind 14  as 11 with the work grouped two steps to a fence (two MFMAs and
+//           the vector work of four scores between scheduling barriers).
 // Results are written to out so that no work is dropped.  Wave 0 of every
 // workgroup also records the shader clock counter (s_memtime) before and after
 // the work, so the host can tell the clock the probe ran at: cycles over the
@@ -149,6 +151,7 @@ __global__ __launch_bounds__(512, 1) void probe_kernel(float* out, unsigned long
       __syncthreads();
       const int lane = threadIdx.x & 63;
       constexpr int NR = KIND == 12 ? 2 : 1;  // MFMAs (and LDS reads) per step
+      constexpr int FENCE = KIND == 14 ? 2 : 1;  // steps between scheduling barriers
       constexpr int PF = 4;                   // steps read ahead
       // read r: 1 KB block r % 32 of the buffer, lane l its 16 bytes l
       auto ld = [&](int r) { return lbuf[((r & 31) << 6) + lane]; };
@@ -166,7 +169,7 @@ __global__ __launch_bounds__(512, 1) void probe_kernel(float* out, unsigned long
           for (int n = 0; n < NR; ++n)
             acc[(m * NR + n) & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[m & 7][n], b, acc[(m * NR + n) & 3], 0, 0, 0);
           if constexpr (KIND != 10) vec(m);
-          __builtin_amdgcn_sched_barrier(0);
+          if (m % FENCE == FENCE - 1) __builtin_amdgcn_sched_barrier(0);
         }
     } else if (KIND == 3 || KIND == 6) {
       for (int i = 0; i < iters; ++i)
@@ -289,6 +292,7 @@ extern "C" int cp_probe_run(int kind, int blocks, int iters, float* out, unsigne
     case 11: hipLaunchKernelGGL(probe_kernel<11>, g, t, 0, stream, out, clk, iters); break;
     case 12: hipLaunchKernelGGL(probe_kernel<12>, g, t, 0, stream, out, clk, iters); break;
     case 13: hipLaunchKernelGGL(probe_kernel<13>, g, t, 0, stream, out, clk, iters); break;
+    case 14: hipLaunchKernelGGL(probe_kernel<14>, g, t, 0, stream, out, clk, iters); break;
     default: return (int)hipErrorInvalidValue;
   }
   return (int)hipGetLastError();
