@@ -454,7 +454,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(KParams p) {
     const float nm = -m_run;
     {
       // 16 chunks, fenced from each other: chunk m reads the K operand of MFMA
-      // m+4, issues MFMA m of the next tile's scores (sub-tile m%2, d-slice
+      // m+PF, issues MFMA m of the next tile's scores (sub-tile m%2, d-slice
       // m/2), and exponentiates scores 2m, 2m+1 of this tile.
       const char* sK = kbuf(kbc);
 #pragma unroll
@@ -470,7 +470,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(KParams p) {
       // the gaps.
       __builtin_amdgcn_s_setprio(1);
       constexpr int NM = 2 * C::QREG;  // MFMAs per tile
-      constexpr int PF = 4;            // operand reads in flight
+      constexpr int PF = 3;            // operand reads in flight
       bf16x8 ops[NM];
 #pragma unroll
       for (int m = 0; m < PF; ++m) ops[m] = kop(m);
@@ -537,7 +537,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(KParams p) {
     // LDS latency on every pair).
     const char* sV = vbuf(vbc);
     constexpr int NMV = 4 * C::DT;  // P V MFMAs per tile
-    constexpr int PFV = 4;
+    constexpr int PFV = 3;
     auto vop = [&](int m) {
       const int kg = m / C::DT, t = m % C::DT;
       if constexpr (VT) {
