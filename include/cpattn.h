@@ -198,9 +198,10 @@ int cp_attn_ring_fwd(const cp_shape* s, int32_t cp, int32_t rank, const void* q_
 /* The whole ring of cp_attn_ring_fwd for callers that cannot allocate device
  * memory or hand a workspace in: code under HIP graph capture, tight serving
  * loops, harnesses that forbid hipMalloc.  Arguments as for cp_attn_ring_fwd,
- * without the workspace.  The per-tile tables the kernels need (key position
- * bounds and padded key positions, 272 bytes per 64-key tile for bf16, 16 per
- * 32-key tile for fp32) live in one static device array of 4 MiB per device,
+ * without the workspace.  The tables the kernels need (key position bounds and
+ * padded key positions, 272 bytes per 64-key tile for bf16, 16 per 32-key
+ * tile for fp32; for bf16 also the dispatch order of the query tiles, 8 bytes
+ * per 128 query rows) live in one static device array of 4 MiB per device,
  * held until the process ends; its address is resolved on the first call on
  * each device.  Rings whose tables exceed it (about 15000 bf16 key tiles,
  * 985 000 keys) are rejected with CP_EINVAL.  V is always read in place (no
