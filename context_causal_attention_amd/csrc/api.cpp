@@ -133,6 +133,8 @@ FwdWorkspace fwd_workspace_layout(int32_t b, int32_t hkv, int32_t d, int64_t sq,
   if (in_dtype == CP_BF16) off += align_up((size_t)ntiles * tk * 4, 256);
   w.order_off = off;
   if (in_dtype == CP_BF16) off += align_up((size_t)2 * ((sq + kOrderRows - 1) / kOrderRows) * 4, 256);
+  w.list_off = off;
+  if (fwd_pre_lists(in_dtype, sq, sk, cp)) off += align_up((size_t)((sq + kOrderRows - 1) / kOrderRows) * ntiles * 4, 256);
   w.vt_off = off;
   w.vt_row = ntiles * tk;
   if (fwd_wide_keys(in_dtype, sk)) off += align_up((size_t)b * hkv * d * (size_t)w.vt_row * 2, 256);
@@ -212,7 +214,9 @@ int prep_fwd(const cp_shape* s, int32_t cp, int32_t rank, const void* q, const v
   if (!v_in_place && fwd_wide_keys(s->in_dtype, s->sk) && (double)s->d * (double)w.vt_row * 2.0 >= 4294967040.0)
     return fail(CP_EINVAL, "%lld key rows exceed the 4 GiB reach of one buffer descriptor for V^T", (long long)s->sk);
   // Reading V in place, the launch uses the tables only (the workspace up to its V^T part).
-  const size_t need = (v_in_place && fwd_wide_keys(s->in_dtype, s->sk)) ? w.vt_off : w.total;
+  // Reading V in place needs only the tables; the key lists are then used
+  // when they fit as well.
+  const size_t need = v_in_place ? w.list_off : w.total;
   if (!ws) return fail(CP_EWORKSPACE, "workspace is null (%zu bytes needed)", need);
   if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0) return fail(CP_EWORKSPACE, "workspace is not 256-byte aligned");
   if (ws_bytes < need) return fail(CP_EWORKSPACE, "workspace too small: %zu < %zu bytes", ws_bytes, need);
@@ -233,6 +237,7 @@ int prep_fwd(const cp_shape* s, int32_t cp, int32_t rank, const void* q, const v
   a.out_dtype = o_dtype;
   a.ws = ws;
   a.v_in_place = v_in_place ? 1 : 0;
+  a.pre_lists = fwd_pre_lists(s->in_dtype, s->sq, s->sk, cp) && ws_bytes >= w.vt_off ? 1 : 0;
   *out = a;
   return CP_OK;
 }
@@ -284,9 +289,9 @@ extern "C" int cp_attn_ring_fwd_noalloc(const cp_shape* s, int32_t cp, int32_t r
                 2 * (long long)cp);
   if (s->sq == 0) return CP_OK;
   // The tables of the launch that reads V in place: the workspace without its
-  // V^T part.
+  // V^T part and without the per-query-tile key lists (used when they fit).
   const FwdWorkspace w = fwd_workspace_layout(s->b, s->hkv, s->d, s->sq, s->sk, cp, s->in_dtype);
-  const size_t need = fwd_wide_keys(s->in_dtype, s->sk) ? w.vt_off : w.total;
+  const size_t need = w.list_off;
   if (need > kNoAllocScratchBytes)
     return fail(CP_EINVAL, "%lld key rows need %zu bytes of tile tables, beyond the %zu-byte static scratch of the "
                 "allocation-free forward", (long long)s->sk, need, kNoAllocScratchBytes);

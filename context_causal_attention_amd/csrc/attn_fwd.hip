@@ -58,6 +58,7 @@ constexpr int kF32Waves = 8;
 constexpr int kF32Threads = kF32Waves * 64;
 constexpr int kF32BlockM = kF32Waves * kRowsPerWave;
 constexpr int kListCap = 1024;          // active key tiles listed per pass
+static_assert(kPreListMaxTiles <= kListCap, "a precomputed list is one pass");
 constexpr float kRescaleLog2 = 8.0f;    // keep a stale running max while scores stay within 2^8 of it
 
 struct KParams {
@@ -70,6 +71,8 @@ struct KParams {
   const int* kpos_pad;      // bf16: key positions per tile slot, padding = kInvalidKey
   const int4* bounds;       // per key tile {min pos, max pos, gap lo, gap hi}
   const int* order;         // may be null: query tiles in dispatch order (heaviest first)
+  const unsigned* lists;    // may be null (4-wave launches only): per query tile, its listed key tiles
+  const int* lcnt;          // with lists: their counts
   char* o;
   float* lse;
   long long q_sb, q_sh, q_ss;
@@ -214,7 +217,7 @@ __device__ __forceinline__ unsigned lds_addr(const void* p) {
 // prep kernel writes into the workspace ([d][keys] tiles, one 16-byte LDS read
 // per V^T operand); otherwise from V itself, row-major tiles read transposed
 // by ds_read_b64_tr_b16 (two 8-byte reads per operand, no copy of V).
-template <int D, int NW, bool VT>
+template <int D, int NW, bool VT, bool PRE = false>
 __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(KParams p) {
   // The body uses device-only buffer-descriptor types; the host pass only needs
   // the launch stub.
@@ -241,20 +244,49 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(KParams p) {
   const int row = it.qt * (NW * kRowsPerWave) + wave * kRowsPerWave + l32;
   const bool valid = row < p.sq;
 
+  // Precomputed list: its first 64 entries are loaded before the queries, so
+  // that the first copies need not wait for the query loads.
+  int pre_cnt = 0;
+  unsigned pre_g0 = 0;
+  if constexpr (PRE) {
+    pre_cnt = p.lcnt[it.qt];
+    // Unconditional (clamped into this tile's list) so that the wait for it
+    // need not cover the loads issued after it.
+    const int ntot = p.cp * p.tpr;
+    pre_g0 = p.lists[(size_t)it.qt * ntot + min(lane, ntot - 1)];
+    __builtin_amdgcn_sched_barrier(0);
+  }
   // ---- query operand (B of S^T = K Q^T) in registers ----------------------
   bf16x8 qreg[C::QREG];
-  {
+  int qp, ql;
+  if constexpr (PRE) {
+    // Loads without branches or selects, so that the wait for the list
+    // entries above covers only them: lanes of rows past the end compute on a
+    // copy of the last row, every lane's row is its own, and only valid rows
+    // are stored.
+    const int rc = min(row, p.sq - 1);
+    const char* qrow = p.q + ((long long)it.b * p.q_sb + (long long)it.h * p.q_sh + (long long)rc * p.q_ss) * 2;
+#pragma unroll
+    for (int kk = 0; kk < C::QREG; ++kk)
+      qreg[kk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qrow + (16 * kk + 8 * hi) * 2));
+    qp = p.q_pos[rc];
+    ql = p.q_lo[rc];
+  } else {
     const char* qrow = p.q + ((long long)it.b * p.q_sb + (long long)it.h * p.q_sh + (long long)row * p.q_ss) * 2;
 #pragma unroll
     for (int kk = 0; kk < C::QREG; ++kk) {
       const u32x4 raw = valid ? *reinterpret_cast<const u32x4*>(qrow + (16 * kk + 8 * hi) * 2) : u32x4{0, 0, 0, 0};
       qreg[kk] = __builtin_bit_cast(bf16x8, raw);
     }
+    qp = valid ? p.q_pos[row] : -1;
+    ql = valid ? (p.q_lo ? p.q_lo[row] : 0) : INT_MAX;
   }
-  const int qp = valid ? p.q_pos[row] : -1;
-  const int ql = valid ? (p.q_lo ? p.q_lo[row] : 0) : INT_MAX;
-  wave_row_bounds(wave, lane, valid, qp, ql, sWb);
-  __syncthreads();
+  static_assert(!PRE || NW == 4, "precomputed lists: 4-wave launches");
+  constexpr bool pre = PRE;
+  if (!pre) {
+    wave_row_bounds(wave, lane, valid, qp, ql, sWb);
+    __syncthreads();
+  }
 
   // ---- per-lane constant addresses ------------------------------------------
   // Copies: each wave fills blocks wave, wave + NW, ... of every K and V tile;
@@ -570,8 +602,10 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(KParams p) {
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
   for (int u0 = 0; u0 < total; u0 += kListCap) {
-    const int cnt = build_key_list<C::BN, NW, kListCap>(p.bounds, p.tpr, p.R, p.rank, p.cp, u0, min(total, u0 + kListCap), tid,
-                                                  wave, lane, sWb, sList, sCnt);
+    const int cnt = pre ? pre_cnt
+                        : build_key_list<C::BN, NW, kListCap>(p.bounds, p.tpr, p.R, p.rank, p.cp, u0,
+                                                              min(total, u0 + kListCap), tid, wave, lane, sWb,
+                                                              sList, sCnt);
     if (cnt == 0) continue;
     // Lane l of vl holds list slot lbase + l as this wave sees it (0 past the
     // end): an iteration takes its entry with v_readlane, not an LDS round trip.
@@ -581,14 +615,24 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(KParams p) {
       lbase = b;
       unsigned v = 0;
       if (b + lane < cnt) {
-        const int2 e = sList[b + lane];
-        v = (unsigned)e.x | ((((unsigned)e.y >> csh) & 3u) << 24);
+        if constexpr (PRE) {
+          const unsigned g = p.lists[(size_t)it.qt * total + b + lane];
+          v = (g & 0xFFFFFFu) | (((g >> (24 + csh)) & 3u) << 24);
+        } else {
+          const int2 e = sList[b + lane];
+          v = (unsigned)e.x | ((((unsigned)e.y >> csh) & 3u) << 24);
+        }
       }
       vl = v;
     };
     auto slot = [&](int j) { return (unsigned)__builtin_amdgcn_readlane((int)vl, j - lbase); };
     auto cls_of = [](unsigned e) { return (int)(e >> 24); };
-    fill(0);
+    if constexpr (PRE) {
+      lbase = 0;
+      vl = lane < cnt ? (pre_g0 & 0xFFFFFFu) | (((pre_g0 >> (24 + csh)) & 3u) << 24) : 0u;
+    } else {
+      fill(0);
+    }
     unsigned e_cur = slot(0), e_nxt = slot(1);
     copy_pos(I0{}, e_cur);
     {
@@ -860,15 +904,19 @@ __global__ __launch_bounds__(256) void prep_kernel(const int* __restrict__ k_pos
 // Dispatch order of a document-masked bf16 launch.  order_cost_kernel: per
 // 128-row query tile (4 waves of 32 rows, as the launch deals them), the number
 // of ring key tiles the tile's workgroup lists, by the forward's own rule
-// (build_key_list).  order_sort_kernel: one workgroup sorts the tiles by that
-// count, most first, ties by tile index, with a bitonic sort in LDS, and
-// writes their indices to order.
+// (build_key_list); with lists, also the list itself (entry .x | .y << 24),
+// which the 4-wave kernel then reads instead of building it in every
+// workgroup.  order_sort_kernel: one workgroup sorts the tiles by that count,
+// most first, ties by tile index, with a bitonic sort in LDS, and writes their
+// indices to order.
 __global__ __launch_bounds__(256) void order_cost_kernel(const int* __restrict__ q_pos, const int* __restrict__ q_lo,
                                                          const int4* __restrict__ bounds, int sq, int R, int tpr,
-                                                         int rank, int cp, int* __restrict__ cost) {
+                                                         int rank, int cp, int* __restrict__ cost,
+                                                         unsigned* __restrict__ lists) {
   constexpr int NW = kOrderRows / kRowsPerWave;
   __shared__ int sWb[NW][6];
   __shared__ int sCnt[NW];
+  __shared__ int2 sList[kPreListMaxTiles];
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
@@ -877,6 +925,14 @@ __global__ __launch_bounds__(256) void order_cost_kernel(const int* __restrict__
   wave_row_bounds(wave, lane, valid, valid ? q_pos[row] : -1, valid ? q_lo[row] : INT_MAX, sWb);
   __syncthreads();
   const int total = cp * tpr;
+  if (lists) {
+    const int n = build_key_list<kTileKeysBf16, NW, kPreListMaxTiles>(bounds, tpr, R, rank, cp, 0, total, tid, wave,
+                                                                     lane, sWb, sList, sCnt);
+    unsigned* out = lists + (size_t)blockIdx.x * total;
+    for (int i = tid; i < n; i += NW * 64) out[i] = (unsigned)sList[i].x | ((unsigned)sList[i].y << 24);
+    if (tid == 0) cost[blockIdx.x] = n;
+    return;
+  }
   int cnt = 0;
   for (int u = tid; u < total; u += NW * 64) {
     const int t = u / tpr;
@@ -955,6 +1011,11 @@ hipError_t launch_t(const FwdArgs& a, hipStream_t stream) {
   int* order_cost = reinterpret_cast<int*>(ws + w.order_off);
   int* order = order_cost + n_order;
   const int ntiles = a.cp * a.tiles_per_rank;
+  // Those of at most kPreListMaxTiles key tiles list each query tile's key
+  // tiles once, here, for all heads (the same lists every workgroup of the
+  // tile would build).
+  const bool pre = ordered && a.pre_lists && ntiles <= kPreListMaxTiles;
+  unsigned* lists = reinterpret_cast<unsigned*>(ws + w.list_off);
   if (ntiles > 0) {
     const dim3 grid(ntiles, use_vt ? a.b * a.hkv : 1);
     const long long vs[3] = {a.v_str[0], a.v_str[1], a.v_str[2]};
@@ -971,7 +1032,7 @@ hipError_t launch_t(const FwdArgs& a, hipStream_t stream) {
   }
   if (ordered) {
     hipLaunchKernelGGL(order_cost_kernel, dim3(n_order), dim3(256), 0, stream, a.q_pos, a.q_lo, bounds, (int)a.sq,
-                       a.rows_per_rank, a.tiles_per_rank, a.rank, a.cp, order_cost);
+                       a.rows_per_rank, a.tiles_per_rank, a.rank, a.cp, order_cost, pre ? lists : nullptr);
     hipLaunchKernelGGL(order_sort_kernel, dim3(1), dim3(1024), 0, stream, order_cost, n_order, order);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -985,6 +1046,8 @@ hipError_t launch_t(const FwdArgs& a, hipStream_t stream) {
   p.kpos_pad = kpos_pad;
   p.bounds = bounds;
   p.order = ordered ? order : nullptr;
+  p.lists = pre ? lists : nullptr;
+  p.lcnt = order_cost;
   p.o = static_cast<char*>(a.o);
   p.lse = a.lse;
   p.q_sb = a.q_str[0];
@@ -1027,6 +1090,8 @@ hipError_t launch_t(const FwdArgs& a, hipStream_t stream) {
       hipLaunchKernelGGL((fwd_bf16_kernel<D, 8, true>), dim3((unsigned)nblk), dim3(8 * 64), 0, stream, p);
     else if (wide)
       hipLaunchKernelGGL((fwd_bf16_kernel<D, 8, false>), dim3((unsigned)nblk), dim3(8 * 64), 0, stream, p);
+    else if (pre)
+      hipLaunchKernelGGL((fwd_bf16_kernel<D, 4, false, true>), dim3((unsigned)nblk), dim3(4 * 64), 0, stream, p);
     else
       hipLaunchKernelGGL((fwd_bf16_kernel<D, 4, false>), dim3((unsigned)nblk), dim3(4 * 64), 0, stream, p);
   } else {

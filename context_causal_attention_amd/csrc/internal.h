@@ -51,6 +51,7 @@ struct FwdArgs {
   void* ws;                // workspace (layout: see fwd_workspace_layout)
   int32_t merge_acc;       // 1: merge the result into (o, lse) instead of writing it
   int32_t v_in_place;      // 1: never read the transposed copy of V (the workspace holds only the tables)
+  int32_t pre_lists;       // 1: the workspace holds the per-query-tile key lists (list_off)
 };
 
 struct FwdWorkspace {
@@ -58,6 +59,8 @@ struct FwdWorkspace {
   size_t kpos_off;     // int32 per key slot of every tile, padding slots = INT32_MAX (bf16 inputs only)
   size_t order_off;    // int32 per 128-row query tile: listed key tiles, then the dispatch order of
                        // document-masked bf16 launches (bf16 inputs only)
+  size_t list_off;     // u32 per (128-row query tile, ring key tile): the key tiles each query tile of a
+                       // document-masked bf16 launch lists (fwd_pre_lists shapes only; up to vt_off)
   size_t vt_off;       // bf16 V^T [b][hkv][d][vt_row] (wide bf16 rings only, see fwd_wide_keys)
   size_t total;
   int64_t vt_row;      // elements per V^T row: every key slot of the padded tiles
@@ -69,6 +72,15 @@ FwdWorkspace fwd_workspace_layout(int32_t b, int32_t hkv, int32_t d, int64_t sq,
 // the most of them whose dispatch order is sorted (one workgroup sorts them).
 constexpr int kOrderRows = 128;
 constexpr int kOrderMaxTiles = 4096;
+// Document-masked bf16 launches of at most this many ring key tiles list each
+// query tile's key tiles once, in the ordering pass, for all heads.
+constexpr int kPreListMaxTiles = 1024;
+inline bool fwd_pre_lists(int32_t in_dtype, int64_t sq, int64_t sk, int32_t cp) {
+  if (in_dtype != CP_BF16 || cp < 1 || sk <= 0) return false;
+  const int64_t n_order = (sq + kOrderRows - 1) / kOrderRows;
+  const int64_t ntiles = (sk / cp + kTileKeysBf16 - 1) / kTileKeysBf16 * cp;
+  return n_order > 1 && n_order <= kOrderMaxTiles && ntiles <= kPreListMaxTiles;
+}
 
 // The allocation-free forward keeps its tile tables (bounds and padded key
 // positions, the workspace without the V^T copy) in a static device array of

@@ -155,7 +155,12 @@ int64_t cp_pairs(const int32_t* q_pos, const int32_t* q_lo, int64_t nq,
 /* ---------------------------------------------------------------- device calls */
 
 /* Workspace bytes needed by cp_attn_partial_fwd (cp = 1) and cp_attn_ring_fwd
- * (cp = ring size).  Returns 0 for an invalid descriptor. */
+ * (cp = ring size).  Returns 0 for an invalid descriptor.  It holds per key
+ * tile its position bounds and padded key positions; for bf16 inputs, per
+ * 128-row query tile its dispatch rank, and for rings of at most 1024 key
+ * tiles (65536 keys) also the key tiles a document-masked query tile lists,
+ * 4 bytes per query tile and key tile, computed once for every head; for dense
+ * bf16 rings of 65536 keys or more, a transposed copy of V. */
 size_t cp_attn_ring_fwd_workspace(const cp_shape* s, int32_t cp);
 
 /* One ring step, the guide's attn(Q_i, K_j, V_j): every query row attends to
@@ -204,7 +209,10 @@ int cp_attn_ring_fwd(const cp_shape* s, int32_t cp, int32_t rank, const void* q_
  * per 128 query rows) live in one static device array of 4 MiB per device,
  * held until the process ends; its address is resolved on the first call on
  * each device.  Rings whose tables exceed it (about 15000 bf16 key tiles,
- * 985 000 keys) are rejected with CP_EINVAL.  V is always read in place (no
+ * 985 000 keys) are rejected with CP_EINVAL.  The per-query-tile key lists of
+ * document-masked rings (see cp_attn_ring_fwd_workspace) are kept there too
+ * when they fit beside the tables; otherwise each workgroup lists its key
+ * tiles itself, with the same result bits.  V is always read in place (no
  * transposed copy), so a long dense ring runs somewhat slower than through
  * cp_attn_ring_fwd; the results are the same bits.  Nothing is allocated and
  * every table entry is rewritten by each call.  Calls on one device share the

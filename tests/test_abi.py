@@ -346,9 +346,13 @@ def test_workspace_query():
     n = cpa.lib().cp_attn_ring_fwd_workspace(ctypes.byref(s), 8)
     tiles = 131072 // 64
     assert n == tiles * 16 + tiles * 64 * 4 + 2 * 128 * 4 + 8 * 128 * 131072 * 2
-    # 32768 keys read V in place: only the tables
+    # 32768 keys read V in place: the tables, then per 128-row query tile one
+    # int per ring key tile (the key tiles a document-masked launch lists)
     s = _shape(sk=32768, sq=4096, hq=32, hkv=8)
     tiles = 32768 // 64
+    assert cpa.lib().cp_attn_ring_fwd_workspace(ctypes.byref(s), 8) == tiles * 16 + tiles * 64 * 4 + 256 + 32 * tiles * 4
+    # one query tile: no dispatch order, hence no lists
+    s = _shape(sk=32768, sq=128, hq=32, hkv=8)
     assert cpa.lib().cp_attn_ring_fwd_workspace(ctypes.byref(s), 8) == tiles * 16 + tiles * 64 * 4 + 256
     assert cpa.lib().cp_attn_ring_fwd_workspace(ctypes.byref(_shape(d=96)), 8) == 0
 

@@ -135,6 +135,23 @@ def test_ring_varlen_documents(mode):
         assert_close(o, lse, *R.oracle(), "bf16", f"varlen rank {rank}")
 
 
+def test_ring_varlen_one_query_tile():
+    """Packed documents with 128 rows a rank (one query tile, so no dispatch
+    order and no key lists precomputed for it: the workgroup lists its key
+    tiles itself, masks included): every rank, every row, against the oracle."""
+    cp = 4
+    L = si.doc_lengths(total=512, mean=60, sigma=1.0, lo=4, hi=400, seed=17)
+    cu = si.cu_seqlens_from_lengths(L)
+    S = int(cu[-1])
+    full = si.make_qkv(1, 4, 2, S, 128, "bf16", seed=18)
+    for rank in range(cp):
+        announce(f"varlen one query tile rank {rank} ({len(L)} docs)")
+        R = Rank(1, 4, 2, S, 128, cp, rank, "bf16", full=full, cu=cu)
+        assert len(R.pos) == 128
+        o, lse = R.ring_fwd()
+        assert_close(o, lse, *R.oracle(), "bf16", f"varlen one tile rank {rank}")
+
+
 def test_llama8b_s32k_cp8_all_ranks_sampled():
     """32q/8kv heads, d=128, S=32768, cp=8: every rank's full ring, checked on
     sampled rows (first/last rows of both chunks plus random rows)."""

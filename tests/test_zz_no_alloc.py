@@ -48,6 +48,29 @@ def test_noalloc_matches_workspace_entry_two_calls():
     assert_close(o2, l2, *small.oracle(), "bf16", "noalloc packed documents")
 
 
+def test_noalloc_without_key_lists():
+    """Rows whose per-query-tile key lists do not fit the static scratch (1024
+    query tiles x 1024 key tiles x 4 bytes beside the tables): the
+    allocation-free call then lets each workgroup list its key tiles, the
+    workspace entry reads the precomputed lists; the two agree bit for bit and
+    with the oracle on sampled rows."""
+    announce("noalloc ring fwd without key lists: 65536 packed tokens, cp=1, every row twice")
+    cu = si.cu_seqlens_from_lengths(si.doc_lengths(total=65536, mean=1500, sigma=1.0, lo=16, hi=16384, seed=44))
+    R = Rank(1, 2, 1, 65536, 64, 1, 0, "bf16", seed=45, cu=cu, mode=cpa.CP_STREAM)
+    # 131072 query rows: the rank's rows twice (1024 query tiles of 128 rows)
+    R.pos, R.lo = np.concatenate([R.pos, R.pos]), np.concatenate([R.lo, R.lo])
+    R.q_loc = torch.cat([R.q_loc, R.q_loc], dim=2).contiguous()
+    o1, l1 = _noalloc(R)
+    r1, rl1 = R.ring_fwd()
+    torch.cuda.synchronize()
+    assert torch.equal(o1, r1) and torch.equal(l1, rl1)
+    rng = np.random.default_rng(5)
+    n = len(R.pos)
+    idx = np.unique(np.concatenate([[0, n // 2 - 1, n // 2, n - 1], rng.integers(0, n, 24)]))
+    O_ref, L_ref = R.oracle(idx)
+    assert_close(o1[:, :, idx], l1[:, :, idx], O_ref, L_ref, "bf16", "noalloc without key lists")
+
+
 def test_noalloc_fp32_and_size_limit():
     announce("noalloc ring fwd: fp32, 1024 tokens, cp=2")
     w = si.WORKLOADS["c0_f32_s1024_cp2"]
