@@ -608,24 +608,28 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(BParams p) {
   }
 
   // ---- accumulate into dK, dV (this lane's key; d = 32t + 8*(r/4) + 4*hi + r%4)
+  // One array at a time, each read whole before it is written: dK and dV may
+  // alias as far as the compiler knows, so a load of one after a store to the
+  // other waits for that store's round trip; read in pairs, the update made
+  // one round trip per 16-byte pair.
   if (kvalid) {
-    float* dkr = p.dk + (((long long)b * p.Hkv + kvh) * p.sk + krow) * D;
-    float* dvr = p.dv + (((long long)b * p.Hkv + kvh) * p.sk + krow) * D;
+    auto acc = [&](float* r, const f32x16* a, float sc) {
+      f32x4 x[C::DT][4];
 #pragma unroll
-    for (int t = 0; t < C::DT; ++t)
+      for (int t = 0; t < C::DT; ++t)
 #pragma unroll
-      for (int rg = 0; rg < 4; ++rg) {
-        const int dd = 32 * t + 8 * rg + 4 * hi;
-        f32x4 k4 = *reinterpret_cast<f32x4*>(dkr + dd);
-        f32x4 v4 = *reinterpret_cast<f32x4*>(dvr + dd);
+        for (int rg = 0; rg < 4; ++rg) x[t][rg] = *reinterpret_cast<const f32x4*>(r + 32 * t + 8 * rg + 4 * hi);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          k4[e] += p.scale * dka[t][4 * rg + e];
-          v4[e] += dva[t][4 * rg + e];
+      for (int t = 0; t < C::DT; ++t)
+#pragma unroll
+        for (int rg = 0; rg < 4; ++rg) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) x[t][rg][e] += sc * a[t][4 * rg + e];
+          *reinterpret_cast<f32x4*>(r + 32 * t + 8 * rg + 4 * hi) = x[t][rg];
         }
-        *reinterpret_cast<f32x4*>(dkr + dd) = k4;
-        *reinterpret_cast<f32x4*>(dvr + dd) = v4;
-      }
+    };
+    acc(p.dk + (((long long)b * p.Hkv + kvh) * p.sk + krow) * D, dka, p.scale);
+    acc(p.dv + (((long long)b * p.Hkv + kvh) * p.sk + krow) * D, dva, 1.f);
   }
 #endif
 }
