@@ -165,6 +165,10 @@ BwdWorkspace bwd_workspace_layout(int32_t b, int32_t hq, int32_t hkv, int32_t d,
   w.qspan_off = take((size_t)w.sq_pad * 4);
   w.nl2_off = take((size_t)b * hq * (size_t)w.sq_pad * 4);
   w.dlt_off = take((size_t)b * hq * (size_t)w.sq_pad * 4);
+  w.kvcost_off = off;
+  if (bwd_kv_order(sk, cp)) take((size_t)2 * bwd_kv_groups(sk, cp) * 4);
+  w.qcost_off = off;
+  if (bwd_q_order(sq)) take((size_t)2 * ((sq + 255) / 256) * 4);
   w.total = off < 256 ? 256 : off;
   return w;
 }

@@ -54,6 +54,8 @@ struct BParams {
   const int* qspan_pad;  // position - document start (padding 0)
   const float* nl2;      // [b][hq][sq_pad]: -LSE * log2(e), 0 in padding and where LSE = -inf
   const float* dlt;      // [b][hq][sq_pad]: -delta, 0 in padding
+  const int* kv_order;   // may be null: the dK/dV kernel's key groups in dispatch order (most work first)
+  const int* q_order;    // may be null: the dQ kernel's 256-row query tiles in dispatch order
   float* dq;             // fp32 [b, hq, sq, d] contiguous, accumulated
   float* dk;             // fp32 [b, hkv, sk, d] contiguous, accumulated
   float* dv;
@@ -198,6 +200,8 @@ __global__ __launch_bounds__(256) void delta_kernel(const char* __restrict__ dou
 // an immediate.
 constexpr int kColBytes = kQT * 16 + 64;  // a column of a 64-row tile
 constexpr int kKeysPerWg = 256;
+static_assert(kKeysPerWg == 256, "bwd_kv_groups counts 256-key groups");
+constexpr int kKvOrderDenseGroups = 256;  // dense rings of at most this many key groups are sorted too
 constexpr int kVColBytes = kKeysPerWg * 16 + 64;
 
 template <int D>
@@ -217,6 +221,78 @@ struct KvCfg {
   // pattern so that one lane offset serves all of them.
   static_assert(NW % (16 / RPB) == 0 && NBLK % (16 / RPB) == 0 && (2 * NBLK) % NW == 0, "DMA split");
 };
+
+// Bounds of one wave's 32 keys (lanes l and l + 32 hold the same key):
+// sKb[wave] = {min key pos, max key pos, all 32 keys valid, gap lo, gap hi},
+// the gap being the widest between consecutive key positions.
+__device__ __forceinline__ void kv_wave_bounds(bool kvalid, int kp, int wave, int lane, int (*sKb)[5]) {
+  const int a = wave_min(kvalid ? kp : INT_MAX);
+  const int c = wave_max(kvalid ? kp : INT_MIN);
+  const bool all_valid = __all(kvalid);
+  const int nk = __popcll(__ballot(kvalid) & 0xffffffffull);
+  const int2 gp = largest_gap(wave_sort<32>(kvalid ? kp : INT_MAX, lane), nk, lane);
+  if (lane == 0) {
+    sKb[wave][0] = a;
+    sKb[wave][1] = c;
+    sKb[wave][2] = all_valid ? 1 : 0;
+    sKb[wave][3] = gp.x;
+    sKb[wave][4] = gp.y;
+  }
+}
+
+// Class of 64-row query tile (bounds qb = {min pos, max pos, min lo, max lo},
+// hole qh) for wave w's keys: skip when no key of the wave can lie in [min lo,
+// max pos] of the tile (from the wave's key bounds and its largest gap between
+// consecutive key positions, and the tile's widest hole), full when every key
+// lies in [max lo, min pos] and the tile is whole.
+__device__ __forceinline__ int kv_class(const int (*sKb)[5], int w, const int4& qb, const int2& qh, bool tile_full) {
+  const int kmn = sKb[w][0], kmx = sKb[w][1];
+  if (kmn != INT_MAX && kmn <= qb.y && kmx >= qb.z && !(sKb[w][3] < qb.z && qb.y < sKb[w][4]) &&
+      !(qh.x < kmn && kmx < qh.y))
+    return (sKb[w][2] && tile_full && kmx <= qb.x && kmn >= qb.w) ? kFull : kPartial;
+  return kSkip;
+}
+
+// Dispatch cost of each 256-key group of the ring (8 waves of 32 keys, as the
+// dK/dV kernel deals them): the number of 64-row query tiles some wave of the
+// group needs (the same for every query head and kv head), by the kernel's
+// own rule.
+__global__ __launch_bounds__(512) void kv_cost_kernel(BParams p, int* __restrict__ cost) {
+  constexpr int NW = 8;
+  __shared__ int sKb[NW][5];
+  __shared__ int sCnt[NW];
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int tg = (p.R + kKeysPerWg - 1) / kKeysPerWg;
+  const int src = blockIdx.x / tg;
+  const int ig = blockIdx.x - src * tg;
+  const int key0 = src * p.R + ig * kKeysPerWg;
+  const int nkeys = min(kKeysPerWg, p.R - ig * kKeysPerWg);
+  const int kloc = wave * 32 + (lane & 31);
+  const bool kvalid = kloc < nkeys;
+  kv_wave_bounds(kvalid, kvalid ? p.k_pos[key0 + kloc] : kInvalidKey, wave, lane, sKb);
+  __syncthreads();
+  int cnt = 0;
+  for (int t = tid; t < p.nqt; t += NW * 64) {
+    const int4 qb = p.qbounds[t];
+    const int2 qh = p.qholes[t];
+    bool act = false;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) act |= kv_class(sKb, w, qb, qh, false) != kSkip;
+    cnt += act ? 1 : 0;
+  }
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) cnt += __shfl_xor(cnt, o);
+  if (lane == 0) sCnt[wave] = cnt;
+  __syncthreads();
+  if (tid == 0) {
+    int tot = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) tot += sCnt[w];
+    cost[blockIdx.x] = tot;
+  }
+}
 
 template <int D>
 __global__ __launch_bounds__(512, 1) void dkdv_kernel(BParams p) {
@@ -252,7 +328,8 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(BParams p) {
   // ---- work item: 256 keys of rank src's shard, for one (batch, kv head) ----
   const int tg = (p.R + kKeysPerWg - 1) / kKeysPerWg;
   int logical = xcd_logical_block();
-  const int grp = logical % (p.cp * tg);
+  const int gl = logical % (p.cp * tg);
+  const int grp = p.kv_order ? p.kv_order[gl] : gl;
   logical /= p.cp * tg;
   const int kvh = logical % p.Hkv;
   const int b = logical / p.Hkv;
@@ -291,21 +368,7 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(BParams p) {
       kreg[kk] = __builtin_bit_cast(bf16x8, kvalid ? *reinterpret_cast<const u32x4*>(kr + (16 * kk + 8 * hi) * 2)
                                                    : u32x4{0, 0, 0, 0});
   }
-  {
-    const int a = wave_min(kvalid ? kp : INT_MAX);
-    const int c = wave_max(kvalid ? kp : INT_MIN);
-    const bool all_valid = __all(kvalid);
-    // Lanes l and l + 32 hold the same key: sort the 32 keys over lanes 0..31.
-    const int nk = __popcll(__ballot(kvalid) & 0xffffffffull);
-    const int2 gp = largest_gap(wave_sort<32>(kvalid ? kp : INT_MAX, lane), nk, lane);
-    if (lane == 0) {
-      sKb[wave][0] = a;
-      sKb[wave][1] = c;
-      sKb[wave][2] = all_valid ? 1 : 0;
-      sKb[wave][3] = gp.x;
-      sKb[wave][4] = gp.y;
-    }
-  }
+  kv_wave_bounds(kvalid, kp, wave, lane, sKb);
   __syncthreads();  // the list builder reads every wave's key bounds
 
   // ---- per-lane constant offsets ----------------------------------------
@@ -388,11 +451,7 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(BParams p) {
         unsigned bits = 0;
 #pragma unroll
         for (int w = 0; w < NW; ++w) {
-          const int kmn = sKb[w][0], kmx = sKb[w][1];
-          int cls = kSkip;
-          if (kmn != INT_MAX && kmn <= qb.y && kmx >= qb.z && !(sKb[w][3] < qb.z && qb.y < sKb[w][4]) &&
-              !(qh.x < kmn && kmx < qh.y))
-            cls = (sKb[w][2] && tile_full && kmx <= qb.x && kmn >= qb.w) ? kFull : kPartial;
+          const int cls = kv_class(sKb, w, qb, qh, tile_full);
           bits |= (unsigned)cls << (2 * w);
           act |= cls != kSkip;
         }
@@ -688,7 +747,7 @@ __global__ __launch_bounds__(512, 1) void dq_kernel(BParams p) {
   int logical = xcd_logical_block();
   const int hg = logical % g;
   logical /= g;
-  const int qt = nqt - 1 - logical % nqt;
+  const int qt = p.q_order ? p.q_order[logical % nqt] : nqt - 1 - logical % nqt;
   logical /= nqt;
   const int kvh = logical % p.Hkv;
   const int b = logical / p.Hkv;
@@ -995,6 +1054,29 @@ hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
   if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
   if (ntiles == 0) return hipSuccess;
   const int tg = (a.rows_per_rank + kKeysPerWg - 1) / kKeysPerWg;
+  // Dispatch orders, most work first: the work per key group (and, under
+  // document masks, per query tile) is uneven and does not follow the index,
+  // so in index order the longest workgroups could start last.  Dense rings
+  // of many key groups are left in index order, which already puts the
+  // heaviest groups (the shards' early chunks) first: sorted, 131072 tokens
+  // ran 0.1-0.9% slower; 32768 tokens (128 groups) ran 2% faster.
+  if (bwd_kv_order(a.sk, a.cp) && (a.q_lo != nullptr || a.cp * tg <= kKvOrderDenseGroups)) {
+    int* cost = reinterpret_cast<int*>(ws + w.kvcost_off);
+    const int ng = a.cp * tg;
+    hipLaunchKernelGGL(kv_cost_kernel, dim3(ng), dim3(512), 0, stream, p, cost);
+    if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+    if (hipError_t e = launch_order_sort(cost, ng, cost + ng, stream); e != hipSuccess) return e;
+    p.kv_order = cost + ng;
+  }
+  if (a.q_lo != nullptr && bwd_q_order(a.sq)) {
+    int* cost = reinterpret_cast<int*>(ws + w.qcost_off);
+    const int n = (a.sq + 255) / 256;
+    if (hipError_t e = launch_dq_order(a.q_pos, a.q_lo, p.kbounds, a.sq, a.rows_per_rank, p.tpr, a.rank, a.cp, cost,
+                                       cost + n, stream);
+        e != hipSuccess)
+      return e;
+    p.q_order = cost + n;
+  }
   const long long nkv = (long long)a.cp * tg * a.hkv * a.b;
   hipLaunchKernelGGL((dkdv_kernel<D>), dim3((unsigned)nkv), dim3(512), 0, stream, p);
   if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;

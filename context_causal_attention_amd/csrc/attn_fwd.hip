@@ -909,23 +909,25 @@ __global__ __launch_bounds__(256) void prep_kernel(const int* __restrict__ k_pos
 // workgroup.  order_sort_kernel: one workgroup sorts the tiles by that count,
 // most first, ties by tile index, with a bitonic sort in LDS, and writes their
 // indices to order.
-__global__ __launch_bounds__(256) void order_cost_kernel(const int* __restrict__ q_pos, const int* __restrict__ q_lo,
-                                                         const int4* __restrict__ bounds, int sq, int R, int tpr,
-                                                         int rank, int cp, int* __restrict__ cost,
-                                                         unsigned* __restrict__ lists) {
-  constexpr int NW = kOrderRows / kRowsPerWave;
+// NW waves of 32 rows per query tile: 4 for the forward's launch, 8 for the
+// backward's dQ kernel (whose key tiles have the same size and bounds).
+template <int NW>
+__global__ __launch_bounds__(NW * 64) void order_cost_kernel(const int* __restrict__ q_pos, const int* __restrict__ q_lo,
+                                                             const int4* __restrict__ bounds, int sq, int R, int tpr,
+                                                             int rank, int cp, int* __restrict__ cost,
+                                                             unsigned* __restrict__ lists) {
   __shared__ int sWb[NW][6];
   __shared__ int sCnt[NW];
-  __shared__ int2 sList[kPreListMaxTiles];
+  __shared__ int2 sList[NW == 4 ? kPreListMaxTiles : 1];
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
-  const int row = blockIdx.x * kOrderRows + wave * kRowsPerWave + (lane & 31);
+  const int row = blockIdx.x * NW * kRowsPerWave + wave * kRowsPerWave + (lane & 31);
   const bool valid = row < sq;
   wave_row_bounds(wave, lane, valid, valid ? q_pos[row] : -1, valid ? q_lo[row] : INT_MAX, sWb);
   __syncthreads();
   const int total = cp * tpr;
-  if (lists) {
+  if constexpr (NW == 4) if (lists) {
     const int n = build_key_list<kTileKeysBf16, NW, kPreListMaxTiles>(bounds, tpr, R, rank, cp, 0, total, tid, wave,
                                                                      lane, sWb, sList, sCnt);
     unsigned* out = lists + (size_t)blockIdx.x * total;
@@ -1031,7 +1033,7 @@ hipError_t launch_t(const FwdArgs& a, hipStream_t stream) {
     if (e != hipSuccess) return e;
   }
   if (ordered) {
-    hipLaunchKernelGGL(order_cost_kernel, dim3(n_order), dim3(256), 0, stream, a.q_pos, a.q_lo, bounds, (int)a.sq,
+    hipLaunchKernelGGL(order_cost_kernel<4>, dim3(n_order), dim3(256), 0, stream, a.q_pos, a.q_lo, bounds, (int)a.sq,
                        a.rows_per_rank, a.tiles_per_rank, a.rank, a.cp, order_cost, pre ? lists : nullptr);
     hipLaunchKernelGGL(order_sort_kernel, dim3(1), dim3(1024), 0, stream, order_cost, n_order, order);
     hipError_t e = hipGetLastError();
@@ -1126,6 +1128,20 @@ hipError_t fwd_noalloc_scratch(void** ptr) {
   }
   *ptr = addr[dev];
   return hipSuccess;
+}
+
+hipError_t launch_order_sort(const int* cost, int n, int* order, hipStream_t stream) {
+  hipLaunchKernelGGL(fwdk::order_sort_kernel, dim3(1), dim3(1024), 0, stream, cost, n, order);
+  return hipGetLastError();
+}
+
+hipError_t launch_dq_order(const int* q_pos, const int* q_lo, const int4* kbounds, int sq, int R, int tpr, int rank,
+                           int cp, int* cost, int* order, hipStream_t stream) {
+  const int n = (sq + 255) / 256;
+  hipLaunchKernelGGL(fwdk::order_cost_kernel<8>, dim3(n), dim3(512), 0, stream, q_pos, q_lo, kbounds, sq, R, tpr,
+                     rank, cp, cost, nullptr);
+  if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+  return launch_order_sort(cost, n, order, stream);
 }
 
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream) {

@@ -128,10 +128,28 @@ struct BwdWorkspace {
   size_t qspan_off;    // int32 [sq_pad]: position - document start, padding = 0
   size_t nl2_off;      // fp32 [b][hq][sq_pad]: -LSE * log2(e)
   size_t dlt_off;      // fp32 [b][hq][sq_pad]: delta
+  size_t kvcost_off;   // int32 per 256-key group of the ring: query tiles listed, then the groups'
+                       // dispatch order (bwd_kv_order shapes only)
+  size_t qcost_off;    // int32 per 256-row query tile: key tiles listed, then the dQ kernel's dispatch
+                       // order under document masks (bwd_q_order shapes only)
   size_t total;
   int64_t kt_row;      // key slots: cp * ceil((sk / cp) / 64) * 64
   int64_t sq_pad;      // ceil(sq / 64) * 64
 };
+
+// Backward launches sort the dK/dV kernel's key groups (256 keys of a shard)
+// by listed query tiles, most first, when there are 2..kOrderMaxTiles of
+// them, and, under document masks, the dQ kernel's 256-row query tiles by
+// listed key tiles.
+inline int64_t bwd_kv_groups(int64_t sk, int32_t cp) { return cp < 1 ? 0 : (sk / cp + 255) / 256 * cp; }
+inline bool bwd_kv_order(int64_t sk, int32_t cp) {
+  const int64_t n = bwd_kv_groups(sk, cp);
+  return n > 1 && n <= kOrderMaxTiles;
+}
+inline bool bwd_q_order(int64_t sq) {
+  const int64_t n = (sq + 255) / 256;
+  return n > 1 && n <= kOrderMaxTiles;
+}
 
 BwdWorkspace bwd_workspace_layout(int32_t b, int32_t hq, int32_t hkv, int32_t d, int64_t sq, int64_t sk,
                                   int32_t cp);
@@ -150,6 +168,15 @@ inline unsigned stride_blocks(int64_t items) {
 hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_delta(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
+// Sorts n <= kOrderMaxTiles non-negative costs, most first (ties by index), into
+// the index list order (one workgroup; attn_fwd.hip).
+hipError_t launch_order_sort(const int* cost, int n, int* order, hipStream_t stream);
+// The dQ kernel's dispatch order under document masks: per 256-row query tile
+// (8 waves of 32 rows) the number of 64-key ring tiles it lists, by the
+// forward's rule over the backward's key-tile bounds, then sorted (q_lo must
+// not be null; (sq + 255) / 256 <= kOrderMaxTiles).
+hipError_t launch_dq_order(const int* q_pos, const int* q_lo, const int4* kbounds, int sq, int R, int tpr, int rank,
+                           int cp, int* cost, int* order, hipStream_t stream);
 // Head exchange layout kernels (a2a.hip).  unpack = 0: packed [g][H/g][rows][d]
 // against the sequence shard [rows, H, d] with row stride x_row_stride
 // (elements); unpack = 1: packed against [H/g][g*rows][d].  to_packed = 1
