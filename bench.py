@@ -466,8 +466,10 @@ def main():
         ms = float(np.mean(list(launch_ms[ps].values())))
         fl = sum(flops[ps].values()) / len(ranks)
         ach = fl / (ms * 1e-3) / 1e12
-        kern = {"fwd": "cp_attn_ring_fwd launch (prep_kernel: bounds and V^T; fwd_bf16_kernel)",
-                "bwd": "cp_attn_ring_bwd launch (key_prep_kernel, query_prep_kernel, dkdv_kernel, dq_kernel)"}[ps]
+        kern = {"fwd": "cp_attn_ring_fwd launch (prep_kernel: bounds, and V^T on dense rings of 65536 keys or more; "
+                       "under document masks order_cost_kernel and order_sort_kernel; fwd_bf16_kernel)",
+                "bwd": "cp_attn_ring_bwd launch (key_prep_kernel, query_prep_kernel; on short or document-masked rings "
+                       "the dispatch-order kernels; dkdv_kernel, dq_kernel)"}[ps]
         r = {"bound": "mfma", "achieved": round(ach, 3), "peak": peak, "unit": "TFLOP/s",
              "frac": round(ach / peak, 4), "traffic": stored_traffic(ps, w.name), "launch_ms": round(ms, 4)}
         if ps == "bwd":
