@@ -203,6 +203,46 @@ def test_ring_bwd_varlen(mode):
         _check_grads((dq, dk, dv), R.oracle_grads(), f"varlen mode {mode} rank {rank}")
 
 
+@pytest.mark.parametrize("rank", [0, 3])
+def test_ring_bwd_varlen_s64k_cp4_whole_doc_sampled(rank):
+    """The packed-document backward at the bench workload's size (65536 tokens,
+    42 lognormal documents, 32q/8kv heads, d=128, bf16, cp=4, whole-document
+    deal), with the dispatch orders the bench runs.  dQ: sampled rows, all
+    heads, against the oracle's gradient of those rows' loss terms.  dK, dV: a
+    document that lies whole on the rank is attended only by its own rows, so
+    the oracle restricted to them gives its keys' gradients exactly."""
+    w = si.WORKLOADS["varlen_s64k_cp4"]
+    cu = si.workload_cu_seqlens(w)
+    full = si.make_qkv(w.B, w.Hq, w.Hkv, w.S, w.d, "bf16", seed=w.seed, with_dout=True)
+    announce(f"ring bwd varlen 64k cp4 whole-doc rank {rank}")
+    R = Rank(w.B, w.Hq, w.Hkv, w.S, w.d, w.cp, rank, "bf16", cu=cu, mode=cpa.CP_WHOLE_DOC, full=full)
+    _, _, dq, dk, dv = R.ring_bwd()
+    torch.cuda.synchronize()
+    for t in (dq, dk, dv):
+        assert torch.isfinite(t).all()
+    q64, k64, v64, do64 = (t.double().numpy() for t in full)
+    n = len(R.pos)
+    rng = np.random.default_rng(7)
+    starts = np.flatnonzero(R.pos == R.lo)
+    idx = np.unique(np.concatenate([[0, n - 1], rng.choice(starts, 3, replace=False), rng.integers(0, n, 5)]))
+    rows = R.pos[idx]
+    dq_ref, _, _ = orc.attention_bwd(q64, k64, v64, do64[:, :, rows], R.scale, cu_seqlens=cu, rows=rows)
+    e = max_err(dq[:, :, idx], dq_ref)
+    assert e <= GTOL, f"dq on sampled rows: max-abs error {e:.3e}"
+    # a document of 300-1500 tokens whose every row is on this rank
+    mine = set(R.pos.tolist())
+    docs = [(int(a), int(b)) for a, b in zip(cu[:-1], cu[1:])
+            if 300 <= b - a <= 1500 and all(p in mine for p in range(int(a), int(b)))]
+    assert docs, "no whole document of 300-1500 tokens on this rank"
+    a, b = min(docs, key=lambda ab: ab[1] - ab[0])
+    doc = np.arange(a, b)
+    _, dk_ref, dv_ref = orc.attention_bwd(q64, k64, v64, do64[:, :, doc], R.scale, cu_seqlens=cu, rows=doc)
+    where = np.argsort(R.allp)[doc]  # the document's rows in k_all
+    for name, got, ref in (("dk", dk[:, :, where], dk_ref[:, :, doc]), ("dv", dv[:, :, where], dv_ref[:, :, doc])):
+        e = max_err(got, ref)
+        assert e <= GTOL, f"{name} of document [{a}, {b}): max-abs error {e:.3e}"
+
+
 def test_ring_bwd_shuffled_rows_and_keys():
     """The backward with a rank's rows and every shard's keys in random order
     (whole-document deal): per-tile key gaps, per-wave and per-tile row holes
