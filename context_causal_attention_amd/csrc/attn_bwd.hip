@@ -670,8 +670,57 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(BParams p) {
   // One array at a time, each read whole before it is written: dK and dV may
   // alias as far as the compiler knows, so a load of one after a store to the
   // other waits for that store's round trip; read in pairs, the update made
-  // one round trip per 16-byte pair.
-  if (kvalid) {
+  // one round trip per 16-byte pair.  At d = 128 the values are first
+  // regrouped through LDS so that the global accesses are whole rows.
+  if constexpr (D == 128) {
+    // Each 32-column slice of the wave's accumulators goes through the wave's
+    // own LDS slot (the V tile's space, read by no wave after the loop's last
+    // barrier), so that a global access covers 8 whole 128-byte rows instead
+    // of 32 quarter rows.  Lane l then owns key 8i + l/8 of the wave and
+    // columns 32t + 4(l%8) .. +3.
+    constexpr int STR = 144;  // bytes per staged row (128 + 16: no bank conflicts on the writes)
+    static_assert(NW * 32 * STR <= C::VTILE, "staging slots fit in the V tile's space");
+    wait_vmem();              // the V copy into that space has landed (no tile may have waited for it)
+    lds_char* slot = to_lds(sV) + wave * 32 * STR;
+    // The lane index recomputed here, so that nothing derived from it stays
+    // live across the tile loop (which uses every register).
+    const int ln = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+    const int kr = ln >> 3, c4 = 4 * (ln & 7), r32 = ln & 31, h32 = ln >> 5;
+    auto acc = [&](float* base, const f32x16* a, float sc) {
+      // Every address is one base pointer plus a constant, so the compiler
+      // can tell the 16 accesses of an array apart and issue the loads together.
+      float* rp = base + (long long)(key0 + wave * 32 + kr) * D + c4;
+      f32x4 x[C::DT][4];
+#pragma unroll
+      for (int t = 0; t < C::DT; ++t) {
+#pragma unroll
+        for (int rg = 0; rg < 4; ++rg) {
+          const f32x4 v = {a[t][4 * rg], a[t][4 * rg + 1], a[t][4 * rg + 2], a[t][4 * rg + 3]};
+          *reinterpret_cast<f32x4*>(slot + r32 * STR + (8 * rg + 4 * h32) * 4) = v;
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x[t][i] = *reinterpret_cast<const f32x4*>(slot + (8 * i + kr) * STR + c4 * 4);
+      }
+      f32x4 y[C::DT][4];
+#pragma unroll
+      for (int t = 0; t < C::DT; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          y[t][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+          if (wave * 32 + 8 * i + kr < nkeys) y[t][i] = *reinterpret_cast<const f32x4*>(rp + 8 * i * D + 32 * t);
+        }
+#pragma unroll
+      for (int t = 0; t < C::DT; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) y[t][i][e] += sc * x[t][i][e];
+          if (wave * 32 + 8 * i + kr < nkeys) *reinterpret_cast<f32x4*>(rp + 8 * i * D + 32 * t) = y[t][i];
+        }
+    };
+    acc(p.dk + ((long long)b * p.Hkv + kvh) * p.sk * D, dka, p.scale);
+    acc(p.dv + ((long long)b * p.Hkv + kvh) * p.sk * D, dva, 1.f);
+  } else if (kvalid) {
     auto acc = [&](float* r, const f32x16* a, float sc) {
       f32x4 x[C::DT][4];
 #pragma unroll
