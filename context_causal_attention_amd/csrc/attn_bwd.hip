@@ -1028,7 +1028,51 @@ __global__ __launch_bounds__(512, 1) void dq_kernel(BParams p) {
     }
   }
 
-  if (valid) {
+  // Accumulate into dQ.  At d = 128 the values are first regrouped through
+  // LDS (the K/V tiles' space, read by no wave after the loop's last barrier;
+  // three 4.5 KB slots per 16 KB tile), one 32-column slice at a time, so
+  // that lane l owns row 8i + l/8 of the wave and columns 32t + 4(l%8) .. +3,
+  // and each global access covers 8 whole 128-byte rows.
+  if constexpr (D == 128) {
+    constexpr int STR = 144;  // bytes per staged row (128 + 16: no bank conflicts on the writes)
+    static_assert(3 * 32 * STR <= C::TILE && NW <= 9, "three staging slots per tile buffer");
+    wait_vmem();
+    char* sb = wave < 3 ? sK0 : (wave < 6 ? sK1 : sV0);
+    lds_char* slot = to_lds(sb) + (wave % 3) * 32 * STR;
+    // The lane index recomputed here, so that nothing derived from it stays
+    // live across the tile loop.
+    const int ln = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+    const int kr = ln >> 3, c4 = 4 * (ln & 7), r32 = ln & 31, h32 = ln >> 5;
+    const int row0 = qt * NW * 32 + wave * 32;  // the wave's first row
+    float* rp = p.dq + (bh * p.sq + row0 + kr) * D + c4;
+    f32x4 x[C::DT][4];
+#pragma unroll
+    for (int t = 0; t < C::DT; ++t) {
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        const f32x4 v = {dqa[t][4 * rg], dqa[t][4 * rg + 1], dqa[t][4 * rg + 2], dqa[t][4 * rg + 3]};
+        *reinterpret_cast<f32x4*>(slot + r32 * STR + (8 * rg + 4 * h32) * 4) = v;
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) x[t][i] = *reinterpret_cast<const f32x4*>(slot + (8 * i + kr) * STR + c4 * 4);
+    }
+    f32x4 y[C::DT][4];
+#pragma unroll
+    for (int t = 0; t < C::DT; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        y[t][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (row0 + 8 * i + kr < p.sq) y[t][i] = *reinterpret_cast<const f32x4*>(rp + 8 * i * D + 32 * t);
+      }
+#pragma unroll
+    for (int t = 0; t < C::DT; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) y[t][i][e] += p.scale * x[t][i][e];
+        if (row0 + 8 * i + kr < p.sq) *reinterpret_cast<f32x4*>(rp + 8 * i * D + 32 * t) = y[t][i];
+      }
+  } else if (valid) {
     float* dqr = p.dq + (bh * p.sq + row) * D;
 #pragma unroll
     for (int t = 0; t < C::DT; ++t)
