@@ -159,6 +159,96 @@ __device__ __forceinline__ void store_out(const KParams& p, const Item& it, int 
     }
 }
 
+// store_out with the rows regrouped through LDS first (d = 128, bf16 kernel):
+// the wave's 32 rows x 32-column slice t go through the wave's own 4.5 KB
+// slot, after which lane l owns row 8i + l/8 of the wave and columns 32t +
+// 4(l%8) .. +3, so that every global access covers 8 whole rows of the slice
+// instead of 32 quarter rows.  The per-row factors move to those lanes by
+// shuffles; the arithmetic is store_out's.  Every lane of the wave takes part.
+template <int DT>
+__device__ __forceinline__ void store_out_rows(const KParams& p, const Item& it, int row0, int row, int hi, bool valid,
+                                               float m_run, float l_tot, const f32x16* oacc, lds_char* slot) {
+  // LDS pointer casts exist in the device pass only.
+#if defined(__HIP_DEVICE_COMPILE__)
+  constexpr int STR = 144;  // bytes per staged row (128 + 16: no bank conflicts on the writes)
+  const bool empty = !(l_tot > 0.f);
+  const float inv = empty ? 0.f : 1.f / l_tot;
+  const long long li = ((long long)it.b * p.Hq + it.h) * p.sq + row;
+  const float lse_new = empty ? -INFINITY : (m_run + log2f(l_tot)) * kLn2;
+  float w1 = 0.f, w2 = inv;
+  if (p.merge_acc) {
+    const float l1 = valid ? p.lse[li] : -INFINITY;
+    const float M = fmaxf(l1, lse_new);
+    float L = -INFINITY;
+    w2 = 0.f;
+    if (M != -INFINITY) {
+      L = M + logf(expf(l1 - M) + expf(lse_new - M));
+      w1 = expf(l1 - L);
+      w2 = expf(lse_new - L) * inv;
+    }
+    if (valid && hi == 0) p.lse[li] = L;
+  } else if (valid && hi == 0) {
+    p.lse[li] = lse_new;
+  }
+  const int ln = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+  const int kr = ln >> 3, c4 = 4 * (ln & 7), r32 = ln & 31, h32 = ln >> 5;
+  float rw1[4], rw2[4];
+  bool rok[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    rw1[i] = __shfl(w1, 8 * i + kr);
+    rw2[i] = __shfl(w2, 8 * i + kr);
+    rok[i] = row0 + 8 * i + kr < p.sq;
+  }
+  f32x4 x[DT][4];
+#pragma unroll
+  for (int t = 0; t < DT; ++t) {
+#pragma unroll
+    for (int rg = 0; rg < 4; ++rg) {
+      const f32x4 v = {oacc[t][4 * rg], oacc[t][4 * rg + 1], oacc[t][4 * rg + 2], oacc[t][4 * rg + 3]};
+      *reinterpret_cast<f32x4*>(slot + r32 * STR + (8 * rg + 4 * h32) * 4) = v;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[t][i] = *reinterpret_cast<const f32x4*>(slot + (8 * i + kr) * STR + c4 * 4);
+  }
+  const long long obase = (long long)it.b * p.o_sb + (long long)it.h * p.o_sh + (long long)(row0 + kr) * p.o_ss + c4;
+  if (p.merge_acc) {
+    f32x4* dst[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dst[i] = reinterpret_cast<f32x4*>(p.o + (obase + (long long)(8 * i) * p.o_ss) * 4);
+    f32x4 old[DT][4];
+#pragma unroll
+    for (int t = 0; t < DT; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) old[t][i] = rok[i] ? dst[i][8 * t] : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int t = 0; t < DT; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        f32x4 val;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) val[e] = rw1[i] * old[t][i][e] + rw2[i] * x[t][i][e];
+        if (rok[i]) dst[i][8 * t] = val;
+      }
+    return;
+  }
+#pragma unroll
+  for (int t = 0; t < DT; ++t)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (!rok[i]) continue;
+      const f32x4 val = {x[t][i][0] * rw2[i], x[t][i][1] * rw2[i], x[t][i][2] * rw2[i], x[t][i][3] * rw2[i]};
+      const long long at = obase + (long long)(8 * i) * p.o_ss + 32 * t;
+      if (p.out_bf16) {
+        __bf16 bv[4] = {(__bf16)val[0], (__bf16)val[1], (__bf16)val[2], (__bf16)val[3]};
+        *reinterpret_cast<u32x2*>(p.o + at * 2) = __builtin_bit_cast(u32x2, bv);
+      } else {
+        *reinterpret_cast<f32x4*>(p.o + at * 4) = val;
+      }
+    }
+#endif
+}
+
 // ============================================================================
 // bf16 kernel
 // ============================================================================
@@ -677,7 +767,17 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(KParams p) {
   }
 
   const float l_tot = l_run + __shfl_xor(l_run, 32);
-  if (valid) store_out<C::DT>(p, it, row, hi, m_run, l_tot, oacc);
+  if constexpr (D == 128) {
+    // The K/V tiles' space is read by no wave after the loop's last barrier:
+    // three 4.5 KB slots per 16 KB buffer.
+    static_assert(3 * 32 * 144 <= C::TILE && NW <= 9, "three output slots per tile buffer");
+    wait_vmem();
+    char* sb = wave < 3 ? sK0 : (wave < 6 ? sK1 : sV0);
+    store_out_rows<C::DT>(p, it, it.qt * (NW * kRowsPerWave) + wave * kRowsPerWave, row, hi, valid, m_run, l_tot,
+                          oacc, to_lds(sb) + (wave % 3) * 32 * 144);
+  } else if (valid) {
+    store_out<C::DT>(p, it, row, hi, m_run, l_tot, oacc);
+  }
 #endif
 }
 
