@@ -186,6 +186,81 @@ def test_ring_bwd_128k_cp8_sampled(rank):
             assert e <= GTOL, f"{name} of the last 128 keys, kv head {kvh}: max-abs error {e:.3e}"
 
 
+@pytest.mark.parametrize("rank", [0, 7])
+def test_ring_bwd_128k_cp8_every_key_of_sampled_rows(rank):
+    """dK and dV of every key of the 131072-token ring (cp=8, 32q/8kv heads,
+    d=128, bf16), in the launch configuration the bench times, elementwise
+    against the oracle.  dO is zero except on sampled rows of the rank.  The
+    gradients are linear in dO (delta = rowsum(dO.O) too), so dK and dV are
+    exactly those rows' contributions, which the oracle computes from those
+    rows alone; the other rows' dQ is exactly zero.
+
+    The bound per element follows the arithmetic of one pair (i, j): P and dS
+    reach the MFMAs as bf16 (relative error <= 2^-9 each), P carries the
+    kernel's LSE error, dS the error of the kernel's delta, and dP, delta the
+    fp32 error of their sums.  The pair errors, weighted by |dO|, |q| or |k|
+    and doubled, bound dV, dK and dQ: about 2^-8 of each gradient's own
+    magnitude, far below the 5e-2 acceptance bar."""
+    w = si.WORKLOADS["llama8b_s128k_cp8"]
+    q, k, v, do = si.make_qkv(w.B, w.Hq, w.Hkv, w.S, w.d, "bf16", seed=w.seed, with_dout=True)
+    announce(f"ring bwd 128k cp8 rank {rank}, every key, dO on sampled rows")
+    n = w.S // w.cp
+    c = n // 2
+    pos_r = orc.zigzag_positions(w.S, w.cp, rank)
+    rng = np.random.default_rng(11 + rank)
+    idx = np.unique(np.concatenate([[0, 1, c - 1, c, c + 1, n - 1], rng.integers(0, n, 10)]))
+    rows = pos_r[idx]
+    keep = torch.zeros(w.S, dtype=torch.bool)
+    keep[torch.from_numpy(rows.astype(np.int64))] = True
+    do = torch.where(keep[None, None, :, None], do, torch.zeros((), dtype=do.dtype))
+    R = Rank(w.B, w.Hq, w.Hkv, w.S, w.d, w.cp, rank, "bf16", full=(q, k, v, do))
+    o, lse = R.ring_fwd()
+    delta = cpa.cp_attn_bwd_delta(R.do_loc, o)
+    dq, dk, dv = cpa.cp_attn_ring_bwd(R.q_loc, R.k_all, R.v_all, R.do_loc, lse, delta, R.cp, R.rank, R.pos,
+                                      R.lo, R.allp, scale=R.scale)
+    torch.cuda.synchronize()
+    others = np.setdiff1d(np.arange(n), idx)
+    assert torch.count_nonzero(dq[:, :, torch.from_numpy(others)]) == 0, "dQ of rows with zero dO is not zero"
+
+    q64, k64, v64 = (t.double().numpy() for t in (q, k, v))
+    do_r = do[:, :, torch.from_numpy(rows.astype(np.int64))].double().numpy()
+    dq_ref, dk_ref, dv_ref = orc.attention_bwd(q64, k64, v64, do_r, R.scale, rows=rows)
+    O_ref, L_ref = orc.attention_fwd(q64, k64, v64, R.scale, rows=rows)
+    dl_ref = orc.bwd_delta(do_r, O_ref)
+    # The kernels' own LSE and delta errors at the sampled rows enter the bound.
+    dL = np.abs(_np(lse[:, :, idx]) - L_ref)
+    ddl = np.abs(_np(delta[:, :, idx]) - dl_ref)
+    assert dL.max() <= 1e-3, f"LSE at the sampled rows: {dL.max():.3e}"
+
+    # Per-element bounds, from the pair errors (fp64, sampled rows only).
+    g = w.Hq // w.Hkv
+    tol_dv = np.zeros_like(dv_ref)
+    tol_dk = np.zeros_like(dk_ref)
+    tol_dq = np.zeros_like(dq_ref)
+    keys = np.arange(w.S)
+    allowed = keys[None, :] <= rows[:, None]
+    for h in range(w.Hq):
+        kvh = h // g
+        s = R.scale * (q64[0, h, rows] @ k64[0, kvh].T)
+        P = np.where(allowed, np.exp(np.where(allowed, s, 0.0) - L_ref[0, h][:, None]), 0.0)
+        dP = do_r[0, h] @ v64[0, kvh].T
+        dsd = np.abs(dP - dl_ref[0, h][:, None])
+        eps = 2.0 ** -9 + 2.0 * dL[0, h][:, None] + 1e-5
+        pair = P * ((eps + 2.0 ** -9) * dsd + ddl[0, h][:, None] + 1e-5 * (np.abs(dP) + np.abs(dl_ref[0, h])[:, None]))
+        tol_dv[0, kvh] += 2.0 * ((eps * P).T @ np.abs(do_r[0, h]))
+        tol_dk[0, kvh] += 2.0 * R.scale * (pair.T @ np.abs(q64[0, h, rows]))
+        tol_dq[0, h] = 2.0 * R.scale * (pair @ np.abs(k64[0, kvh]))
+    where = np.argsort(R.allp)  # natural position -> row of k_all
+    for name, got, ref, tol in (("dv", _np(dv)[:, :, where], dv_ref, tol_dv + 1e-6),
+                                ("dk", _np(dk)[:, :, where], dk_ref, tol_dk + 1e-6),
+                                ("dq", _np(dq[:, :, idx]), dq_ref, tol_dq + 1e-6)):
+        err = np.abs(got - ref)
+        worst = np.unravel_index(np.argmax(err / tol), err.shape)
+        assert np.all(err <= tol), (f"{name}: error {err[worst]:.3e} above its bound {tol[worst]:.3e} at {worst} "
+                                    f"(reference {ref[worst]:.3e})")
+        assert err.max() <= GTOL
+
+
 @pytest.mark.parametrize("mode", [cpa.CP_STREAM, cpa.CP_PER_DOC, cpa.CP_WHOLE_DOC])
 def test_ring_bwd_varlen(mode):
     """Block-diagonal document masks: each rank's loss against the oracle with
