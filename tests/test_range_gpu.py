@@ -39,7 +39,7 @@ MARGINS_BF16 = (8.0, 20.0, 32.0, 45.0, 70.0)
 MARGINS_F32 = (6.0, 9.0, 12.0)
 # The backward's margins stay at 20 or below.  delta = dO . O takes the
 # forward's O, whose P entered the P V product rounded to bf16 (relative error
-# up to 2^-9), and dQ = scale * sum_j dS_ij k_j multiplies that error by the
+# up to 2^-8, bf16's unit roundoff), and dQ = scale * sum_j dS_ij k_j multiplies that error by the
 # planted key, whose size grows with the margin.  Emulating exactly that
 # rounding (bf16 P in O, bf16 dS) on the 8192-token inputs gives dQ errors of
 # 0.06-0.11 at margins up to 70, past the 5e-2 bar the method's own arithmetic
