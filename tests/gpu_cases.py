@@ -112,3 +112,34 @@ def assert_close(o, lse, O_ref, L_ref, dtype, what=""):
     assert np.isfinite(eo) and eo <= to, f"{what}: O max-abs error {eo:.3e} > {to}"
     assert np.isfinite(el) and el <= tl, f"{what}: LSE max-abs error {el:.3e} > {tl}"
     return eo, el
+
+
+def pair_error_bounds(q64, k64, v64, do_r, rows, scale, L_ref, dl_ref, dL, ddl, g, u=2.0 ** -8):
+    """Per-element error bounds of dV, dK (every key, natural order) and of the
+    rows' dQ, for gradients whose dO is zero outside ``rows``.
+
+    The arithmetic of one pair (i, j): P and dS reach the MFMAs as bf16
+    (relative error <= u, the unit roundoff of bf16's 8-bit significand; dS
+    may be formed from the rounded P), P carries the kernel's LSE error dL,
+    dS the error ddl of the kernel's delta, and dP, delta the fp32 error of
+    their sums.  The pair errors, weighted by |dO|, |q| or |k|, are doubled.
+    q64, k64, v64: [1, H, S, d] fp64; do_r: [1, Hq, len(rows), d]; L_ref,
+    dl_ref, dL, ddl: [1, Hq, len(rows)]; g: query heads per kv head."""
+    S = k64.shape[2]
+    Hq = q64.shape[1]
+    tol_dv = np.zeros((1, k64.shape[1], S, k64.shape[3]))
+    tol_dk = np.zeros_like(tol_dv)
+    tol_dq = np.zeros((1, Hq, len(rows), q64.shape[3]))
+    allowed = np.arange(S)[None, :] <= np.asarray(rows)[:, None]
+    for h in range(Hq):
+        kvh = h // g
+        s = scale * (q64[0, h, rows] @ k64[0, kvh].T)
+        P = np.where(allowed, np.exp(np.where(allowed, s, 0.0) - L_ref[0, h][:, None]), 0.0)
+        dP = do_r[0, h] @ v64[0, kvh].T
+        dsd = np.abs(dP - dl_ref[0, h][:, None])
+        eps = u + 2.0 * dL[0, h][:, None] + 1e-5  # P as the MFMAs see it
+        pair = P * ((eps + u) * dsd + ddl[0, h][:, None] + 1e-5 * (np.abs(dP) + np.abs(dl_ref[0, h])[:, None]))
+        tol_dv[0, kvh] += 2.0 * ((eps * P).T @ np.abs(do_r[0, h]))
+        tol_dk[0, kvh] += 2.0 * scale * (pair.T @ np.abs(q64[0, h, rows]))
+        tol_dq[0, h] = 2.0 * scale * (pair @ np.abs(k64[0, kvh]))
+    return tol_dv + 1e-6, tol_dk + 1e-6, tol_dq + 1e-6

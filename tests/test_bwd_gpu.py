@@ -10,7 +10,7 @@ import torch
 import oracle as orc
 import seeded_inputs as si
 import context_causal_attention_amd as cpa
-from gpu_cases import Rank, announce, max_err
+from gpu_cases import Rank, announce, max_err, pair_error_bounds
 
 pytestmark = pytest.mark.gpu
 
@@ -195,13 +195,11 @@ def test_ring_bwd_128k_cp8_every_key_of_sampled_rows(rank):
     exactly those rows' contributions, which the oracle computes from those
     rows alone; the other rows' dQ is exactly zero.
 
-    The bound per element follows the arithmetic of one pair (i, j): P and dS
-    reach the MFMAs as bf16 (relative error <= u = 2^-8 each, the unit
-    roundoff of an 8-bit significand; dS may be formed from the rounded P),
-    P carries the kernel's LSE error, dS the error of the kernel's delta, and
-    dP, delta the fp32 error of their sums.  The pair errors, weighted by
-    |dO|, |q| or |k| and doubled, bound dV, dK and dQ: about 2^-6 of each
-    gradient's own magnitude, far below the 5e-2 acceptance bar."""
+    The bound per element (gpu_cases.pair_error_bounds) follows the
+    arithmetic of one pair: bf16 P and dS, the kernel's LSE and delta errors,
+    fp32 sums; about 2^-6 of each gradient's own magnitude, far below the
+    5e-2 acceptance bar.  tests/test_bounds_cpu.py checks it against an
+    emulation of that arithmetic and a planted mistake."""
     w = si.WORKLOADS["llama8b_s128k_cp8"]
     q, k, v, do = si.make_qkv(w.B, w.Hq, w.Hkv, w.S, w.d, "bf16", seed=w.seed, with_dout=True)
     announce(f"ring bwd 128k cp8 rank {rank}, every key, dO on sampled rows")
@@ -234,28 +232,12 @@ def test_ring_bwd_128k_cp8_every_key_of_sampled_rows(rank):
     assert dL.max() <= 1e-3, f"LSE at the sampled rows: {dL.max():.3e}"
 
     # Per-element bounds, from the pair errors (fp64, sampled rows only).
-    g = w.Hq // w.Hkv
-    tol_dv = np.zeros_like(dv_ref)
-    tol_dk = np.zeros_like(dk_ref)
-    tol_dq = np.zeros_like(dq_ref)
-    keys = np.arange(w.S)
-    allowed = keys[None, :] <= rows[:, None]
-    for h in range(w.Hq):
-        kvh = h // g
-        s = R.scale * (q64[0, h, rows] @ k64[0, kvh].T)
-        P = np.where(allowed, np.exp(np.where(allowed, s, 0.0) - L_ref[0, h][:, None]), 0.0)
-        dP = do_r[0, h] @ v64[0, kvh].T
-        dsd = np.abs(dP - dl_ref[0, h][:, None])
-        u = 2.0 ** -8
-        eps = u + 2.0 * dL[0, h][:, None] + 1e-5  # P as the MFMAs see it
-        pair = P * ((eps + u) * dsd + ddl[0, h][:, None] + 1e-5 * (np.abs(dP) + np.abs(dl_ref[0, h])[:, None]))
-        tol_dv[0, kvh] += 2.0 * ((eps * P).T @ np.abs(do_r[0, h]))
-        tol_dk[0, kvh] += 2.0 * R.scale * (pair.T @ np.abs(q64[0, h, rows]))
-        tol_dq[0, h] = 2.0 * R.scale * (pair @ np.abs(k64[0, kvh]))
+    tol_dv, tol_dk, tol_dq = pair_error_bounds(q64, k64, v64, do_r, rows, R.scale, L_ref, dl_ref, dL, ddl,
+                                               w.Hq // w.Hkv)
     where = np.argsort(R.allp)  # natural position -> row of k_all
-    for name, got, ref, tol in (("dv", _np(dv)[:, :, where], dv_ref, tol_dv + 1e-6),
-                                ("dk", _np(dk)[:, :, where], dk_ref, tol_dk + 1e-6),
-                                ("dq", _np(dq[:, :, idx]), dq_ref, tol_dq + 1e-6)):
+    for name, got, ref, tol in (("dv", _np(dv)[:, :, where], dv_ref, tol_dv),
+                                ("dk", _np(dk)[:, :, where], dk_ref, tol_dk),
+                                ("dq", _np(dq[:, :, idx]), dq_ref, tol_dq)):
         err = np.abs(got - ref)
         worst = np.unravel_index(np.argmax(err / tol), err.shape)
         assert np.all(err <= tol), (f"{name}: error {err[worst]:.3e} above its bound {tol[worst]:.3e} at {worst} "
